@@ -1,0 +1,365 @@
+"""Plain fp64 CPU statement of the sparse MoE layer forward pass.
+
+TEST INFRASTRUCTURE ONLY: see the package docstring.  Written for a reader
+who checks it against the pages by eye; nothing here is blocked, fused or
+reordered beyond the pages' own per-expert grouping, and every function cites
+the passage it follows.  Page tags ([RC], [LBS], [HA], [GN], [FA]) are
+expanded in ``oracle/__init__.py``.
+
+Conventions
+-----------
+* Inputs arrive as numpy arrays (bf16 tensors are handed over as the float32
+  arrays holding the same values).  All arithmetic below is float64, except
+  the router logits, which are rounded once to float32: [LBS] "Dense vs
+  Sparse" states the router runs in float32 while the rest may be bfloat16,
+  so the top-k decision is taken on float32 logits, as the GPU takes it.
+* Stacked expert weights follow ``nn.Linear`` storage ([out, in], the input
+  dimension contiguous) with a leading expert axis:
+  GELU experts ``w1 [E,d_ff,d], b1 [E,d_ff], w2 [E,d,d_ff], b2 [E,d]``;
+  SwiGLU experts ``w_gate, w_up [E,d_ff,d], w_down [E,d,d_ff]``;
+  an always-on shared expert uses the same names with a ``shared_`` prefix
+  and no expert axis.  Any object whose ``[e]`` gives an array works, so a
+  caller may fetch one expert at a time.
+* Assignment id ``a = t*k + j`` names slot ``j`` of token ``t`` ([LBS]
+  "Gating Mechanism": the flattened expert ids, token = flat position // k).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import erf as _erf
+
+F64 = np.float64
+
+
+# ---------------------------------------------------------------------------
+# Scalars
+# ---------------------------------------------------------------------------
+
+def capacity(T: int, k: int, E: int, cf_num: int, cf_den: int) -> int:
+    """Per-expert token capacity.
+
+    [LBS] "The Capacity Factor": the ideal share is T*k/E assignments per
+    expert; capacity is that share times the capacity factor, truncated to
+    an integer, and never below 1.  The factor is taken as the exact
+    rational cf_num/cf_den so that e.g. 1.1 cannot truncate to the wrong
+    integer through a binary floating-point product.
+    """
+    if T < 0 or k < 1 or E < 1 or cf_num <= 0 or cf_den <= 0:
+        raise ValueError("capacity: need T>=0, k>=1, E>=1, cf>0")
+    return max((cf_num * T * k) // (cf_den * E), 1)
+
+
+def gelu(z):
+    """Exact (erf) GELU, z * Phi(z): the default ``nn.GELU`` inside the
+    Linear-GELU-Linear expert of [RC] "How a sparse MoE layer works"."""
+    z = np.asarray(z, F64)
+    return 0.5 * z * (1.0 + _erf(z / math.sqrt(2.0)))
+
+
+def silu(z):
+    """SiLU, z * sigmoid(z), the gate nonlinearity of the SwiGLU expert in
+    [GN] "Implementing a complete MoE layer"."""
+    z = np.asarray(z, F64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def softmax(logits):
+    """Row softmax over the expert axis ([RC], [LBS] "Gating Mechanism",
+    [GN] "The router"); the row maximum is subtracted first."""
+    l = np.asarray(logits, F64)
+    if l.shape[-1] == 0:
+        return l.copy()
+    m = l.max(axis=-1, keepdims=True)
+    e = np.exp(l - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+# ---------------------------------------------------------------------------
+# Step 1: route
+# ---------------------------------------------------------------------------
+
+def _logits64(x, w_router, router_bias=None):
+    l = np.asarray(x, F64) @ np.asarray(w_router, F64).T
+    if router_bias is not None:
+        l = l + np.asarray(router_bias, F64)
+    return l
+
+
+def route(x, w_router, k, router_bias=None, select_bias=None):
+    """Router linear, softmax, top-k and renormalised gates.
+
+    * logits = x . W_r^T (+ router bias): one linear layer from the hidden
+      state to E scores ([RC] "How a sparse MoE layer works"; [LBS]
+      "Gating Mechanism" uses no bias; [GN] "The router").  Rounded once to
+      float32, the router precision [LBS] "Dense vs Sparse" gives.
+    * probs = softmax(logits) over all E experts.
+    * The k experts with the largest key are chosen, in descending key
+      order; equal keys go to the lower expert index.  The key is the
+      float32 logit, plus (float32 add) a per-expert selection bias when
+      one is given: [GN] "DeepSeek-V3" adds a per-expert bias to the
+      routing scores to choose experts; here it moves the choice only, the
+      gates and probs still come from the unbiased softmax.  Choosing on the
+      logits is choosing on the probs, softmax being monotone.
+    * gate[t, j] = probs[t, idx[t, j]] / sum over the k chosen probs
+      ([RC]; [LBS] "Gating Mechanism"; [GN] "The router"; [FA] "Concept").
+
+    Returns a dict: logits (float32 [T,E]), keys (float32 [T,E]),
+    idx (int64 [T,k]), gate (float64 [T,k]), probs (float64 [T,E]).
+    """
+    x = np.asarray(x)
+    T = x.shape[0]
+    E = np.asarray(w_router).shape[0]
+    if not 1 <= k <= E:
+        raise ValueError("route: need 1 <= k <= E")
+    logits = _logits64(x, w_router, router_bias).astype(np.float32)
+    keys = logits.copy()
+    if select_bias is not None:
+        keys = (keys + np.asarray(select_bias, np.float32)).astype(np.float32)
+    probs = softmax(logits)
+    idx = np.zeros((T, k), np.int64)
+    for t in range(T):
+        # sort by key descending, then by expert index ascending
+        order = sorted(range(E), key=lambda e: (-float(keys[t, e]), e))
+        idx[t] = order[:k]
+    chosen = np.take_along_axis(probs, idx, axis=1)
+    gate = chosen / chosen.sum(axis=1, keepdims=True) if T else chosen
+    return {"logits": logits, "keys": keys, "idx": idx, "gate": gate,
+            "probs": probs}
+
+
+def topk_margin(x, w_router, k, router_bias=None, select_bias=None):
+    """Smallest gap between consecutive sorted selection keys around the
+    top-k boundary, per token, in float64 (no float32 rounding).
+
+    For keys sorted descending, kappa_(1) >= kappa_(2) >= ..., the gaps
+    kappa_(j) - kappa_(j+1) for j = 1..k (j = 1..k-1 when k = E) decide
+    both the chosen set and the slot order; a token whose smallest gap is
+    tiny can flip under float32 summation order.  Used only to build test
+    inputs whose routing is unique at float32 resolution.
+    """
+    keys = _logits64(x, w_router, router_bias)
+    if select_bias is not None:
+        keys = keys + np.asarray(select_bias, F64)
+    E = keys.shape[1]
+    s = -np.sort(-keys, axis=1)
+    last = min(k, E - 1)
+    if last < 1:
+        return np.full(keys.shape[0], np.inf)
+    gaps = s[:, :last] - s[:, 1:last + 1]
+    return gaps.min(axis=1)
+
+
+# ---------------------------------------------------------------------------
+# Step 2: dispatch (capacity cut, grouping by expert)
+# ---------------------------------------------------------------------------
+
+def dispatch(idx, E, cap):
+    """Group assignments by expert under a per-expert capacity.
+
+    For each expert e, the (token, slot) pairs routed to it are listed in
+    ascending token order, the order a row-major nonzero of the [T, k]
+    mask yields in [RC] "How a sparse MoE layer works"; the first ``cap``
+    are kept and the rest are dropped (their MoE output is zero and the
+    residual carries the token: [LBS] "The Capacity Factor" and "Token
+    Dropping and Overflow Handling", zero-output strategy).  cap <= 0 means
+    no limit.
+
+    Returns counts[E] (assignments routed, before the cut), kept[E],
+    offsets[E+1] (exclusive scan of kept), perm[offsets[E]] (assignment ids
+    t*k+j, grouped by expert, ascending token inside each group),
+    slot_of[T*k] (row of perm holding that assignment, -1 if dropped) and
+    n_dropped.
+    """
+    idx = np.asarray(idx, np.int64)
+    T, k = idx.shape
+    counts = np.zeros(E, np.int64)
+    kept = np.zeros(E, np.int64)
+    perm = []
+    slot_of = np.full(T * k, -1, np.int64)
+    for e in range(E):
+        rows, slots = np.nonzero(idx == e)      # row-major: ascending t
+        counts[e] = rows.size
+        n_keep = rows.size if cap <= 0 else min(rows.size, cap)
+        kept[e] = n_keep
+        for t, j in zip(rows[:n_keep], slots[:n_keep]):
+            a = int(t) * k + int(j)
+            slot_of[a] = len(perm)
+            perm.append(a)
+    offsets = np.zeros(E + 1, np.int64)
+    offsets[1:] = np.cumsum(kept)
+    n_dropped = int(T * k - offsets[E])
+    return {"counts": counts, "kept": kept, "offsets": offsets,
+            "perm": np.asarray(perm, np.int64), "slot_of": slot_of,
+            "n_dropped": n_dropped}
+
+
+# ---------------------------------------------------------------------------
+# Steps 3-4: expert FFNs over each expert's kept rows
+# ---------------------------------------------------------------------------
+
+def _ffn(X, act, w1, w_up, w2, b1, b2):
+    """One expert on a batch of rows X [n, d] (float64).
+
+    GELU expert: Linear(d, d_ff) with bias, exact GELU, Linear(d_ff, d)
+    with bias ([RC] "How a sparse MoE layer works").  SwiGLU expert:
+    w_down(silu(w_gate x) * w_up x), no biases ([GN] "Implementing a
+    complete MoE layer"; "Mixtral 8x7B" gives the three matrices).
+    """
+    if act == "gelu":
+        h = gelu(X @ np.asarray(w1, F64).T + np.asarray(b1, F64))
+        return h @ np.asarray(w2, F64).T + np.asarray(b2, F64)
+    if act == "swiglu":
+        g = X @ np.asarray(w1, F64).T
+        u = X @ np.asarray(w_up, F64).T
+        return (silu(g) * u) @ np.asarray(w2, F64).T
+    raise ValueError(f"unknown activation {act!r}")
+
+
+def _expert_args(weights, act, e):
+    if act == "gelu":
+        return (weights["w1"][e], None, weights["w2"][e],
+                weights["b1"][e], weights["b2"][e])
+    return (weights["w_gate"][e], weights["w_up"][e], weights["w_down"][e],
+            None, None)
+
+
+def _shared_args(weights, act):
+    if act == "gelu":
+        return (weights["shared_w1"], None, weights["shared_w2"],
+                weights["shared_b1"], weights["shared_b2"])
+    return (weights["shared_gate"], weights["shared_up"],
+            weights["shared_down"], None, None)
+
+
+def expert_ffn(x, perm, offsets, weights, act, k, n_shared=0, tokens=None):
+    """Run every expert once over the rows grouped to it.
+
+    Row r in [offsets[e], offsets[e+1]) of the result is expert e applied
+    to token perm[r] // k: the pages' per-expert loop (gather the tokens an
+    expert received, run the expert on them as one batch) from [RC], [LBS]
+    "Gating Mechanism" and [HA].  With an always-on shared expert ([GN]
+    "DeepSeek-V3", the shared expert pattern; [FA] "The knobs",
+    n_shared_experts) row T*k + t holds the shared expert applied to token
+    t.  Rows in [offsets[E], T*k) are unused and left zero.
+
+    If ``tokens`` is given, only rows belonging to those tokens are
+    computed (the rest stay zero); the arithmetic per row is unchanged.
+    """
+    x = np.asarray(x)
+    T, d = x.shape
+    E = len(offsets) - 1
+    y = np.zeros((T * k + n_shared * T, d), F64)
+    want = None
+    if tokens is not None:
+        want = np.zeros(T, bool)
+        want[np.asarray(tokens, np.int64)] = True
+    for e in range(E):
+        rows = np.arange(offsets[e], offsets[e + 1])
+        t_of = np.asarray(perm, np.int64)[rows] // k
+        if want is not None:
+            sel = want[t_of]
+            rows, t_of = rows[sel], t_of[sel]
+        if rows.size == 0:
+            continue
+        y[rows] = _ffn(np.asarray(x[t_of], F64), act,
+                       *_expert_args(weights, act, e))
+    if n_shared:
+        ts = np.arange(T) if want is None else np.nonzero(want)[0]
+        if ts.size:
+            y[T * k + ts] = _ffn(np.asarray(x[ts], F64), act,
+                                 *_shared_args(weights, act))
+    return y
+
+
+# ---------------------------------------------------------------------------
+# Step 5: combine
+# ---------------------------------------------------------------------------
+
+def combine(x_residual, y, slot_of, gate, k, n_shared=0, T=None,
+            tokens=None):
+    """Gate-weighted combine back into token order, plus the residual.
+
+    out[t] = x[t] + (shared row of t) + sum over kept slots j of
+    gate[t, j] * y[slot_of[t*k + j]].  A dropped slot adds nothing and the
+    surviving gates are not renormalised ([RC] "How a sparse MoE layer
+    works": the weights are taken before the capacity cut, and the residual
+    is added at the end; [LBS] "Token Dropping and Overflow Handling",
+    zero output; [FA] "Concept": the sum of gate times expert output).
+    ``x_residual=None`` omits the residual, as the [LBS], [HA] and [GN]
+    snippets do.  ``tokens`` restricts the rows computed.
+    """
+    gate = np.asarray(gate, F64)
+    if T is None:
+        T = gate.shape[0]
+    d = y.shape[1]
+    ts = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
+    out = np.zeros((ts.size, d), F64)
+    for i, t in enumerate(ts):
+        acc = np.zeros(d, F64)
+        if x_residual is not None:
+            acc += np.asarray(x_residual[t], F64)
+        if n_shared:
+            acc += y[T * k + t]
+        for j in range(k):
+            s = slot_of[t * k + j]
+            if s >= 0:
+                acc += gate[t, j] * y[s]
+        out[i] = acc
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Step 6: auxiliary load-balance loss
+# ---------------------------------------------------------------------------
+
+def aux_loss(counts, probs, alpha):
+    """Switch-style load-balance loss alpha * E * sum_e f_e * P_e.
+
+    f_e = (assignments routed to e over all k slots, before any capacity
+    cut) / T and P_e = mean over tokens of the full-softmax probability of
+    e ([LBS] "The Load Balancing Problem"; [GN] "Load balancing and expert
+    collapse" puts alpha inside, as here).  T = 0 gives 0.
+    """
+    probs = np.asarray(probs, F64)
+    T, E = probs.shape
+    if T == 0:
+        return 0.0
+    f = np.asarray(counts, F64) / T
+    P = probs.mean(axis=0)
+    return float(alpha * E * np.sum(f * P))
+
+
+# ---------------------------------------------------------------------------
+# The whole layer
+# ---------------------------------------------------------------------------
+
+def layer_forward(x, w_router, weights, *, k, cap, act, n_shared=0,
+                  alpha=0.01, router_bias=None, select_bias=None,
+                  residual=True, tokens=None):
+    """Route, dispatch, expert FFNs, combine and aux loss, in that order.
+
+    With ``tokens`` the routing, dispatch and aux loss still cover every
+    token (capacity depends on the whole batch, [FA] "Effect"), while
+    expert outputs and the combined output are produced for those tokens
+    only; ``out`` then has one row per listed token.
+    """
+    x = np.asarray(x)
+    T = x.shape[0]
+    E = np.asarray(w_router).shape[0]
+    r = route(x, w_router, k, router_bias, select_bias)
+    dsp = dispatch(r["idx"], E, cap)
+    y = expert_ffn(x, dsp["perm"], dsp["offsets"], weights, act, k,
+                   n_shared, tokens)
+    out = combine(x if residual else None, y, dsp["slot_of"], r["gate"], k,
+                  n_shared, T, tokens)
+    aux = aux_loss(dsp["counts"], r["probs"], alpha)
+    res = dict(r)
+    res.update(dsp)
+    res.update({"y": y, "out": out, "aux": aux,
+                "prob_mean": r["probs"].mean(axis=0) if T else
+                np.zeros(E, F64)})
+    return res

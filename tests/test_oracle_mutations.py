@@ -1,0 +1,236 @@
+"""Plant plausible mistakes into the CPU oracle (on the CPU, via
+monkeypatch) and check that at least one pin catches each of them."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.moe as om
+import oracle_pins
+
+F64 = np.float64
+
+
+def _patch(monkeypatch, name, fn):
+    monkeypatch.setattr(om, name, fn)
+    if hasattr(oracle, name):
+        monkeypatch.setattr(oracle, name, fn)
+
+
+_route = om.route
+_dispatch = om.dispatch
+_combine = om.combine
+_ffn = om._ffn
+_aux = om.aux_loss
+_capacity = om.capacity
+_expert_ffn = om.expert_ffn
+
+
+def m_no_renormalise(mp):
+    def route(*a, **k):
+        r = _route(*a, **k)
+        r["gate"] = np.take_along_axis(r["probs"], r["idx"], axis=1)
+        return r
+    _patch(mp, "route", route)
+
+
+def m_tie_to_higher_index(mp):
+    def route(x, w_router, k, router_bias=None, select_bias=None):
+        r = _route(x, w_router, k, router_bias, select_bias)
+        keys = r["keys"]
+        E = keys.shape[1]
+        for t in range(keys.shape[0]):
+            order = sorted(range(E), key=lambda e: (-float(keys[t, e]), -e))
+            r["idx"][t] = order[:k]
+        ch = np.take_along_axis(r["probs"], r["idx"], axis=1)
+        r["gate"] = ch / ch.sum(1, keepdims=True)
+        return r
+    _patch(mp, "route", route)
+
+
+def m_bias_in_gates(mp):
+    def route(x, w_router, k, router_bias=None, select_bias=None):
+        r = _route(x, w_router, k, router_bias, select_bias)
+        if select_bias is not None:
+            p = om.softmax(r["keys"])
+            ch = np.take_along_axis(p, r["idx"], axis=1)
+            r["gate"] = ch / ch.sum(1, keepdims=True)
+        return r
+    _patch(mp, "route", route)
+
+
+def m_capacity_by_slot(mp):
+    def dispatch(idx, E, cap):
+        idx = np.asarray(idx)
+        T, k = idx.shape
+        r = _dispatch(idx, E, 0)
+        perm, slot_of = [], np.full(T * k, -1, np.int64)
+        kept = np.zeros(E, np.int64)
+        for e in range(E):
+            slots, rows = np.nonzero(idx.T == e)   # slot-major order
+            n = rows.size if cap <= 0 else min(rows.size, cap)
+            kept[e] = n
+            for t, j in zip(rows[:n], slots[:n]):
+                slot_of[t * k + j] = len(perm)
+                perm.append(t * k + j)
+        r.update(kept=kept, perm=np.asarray(perm), slot_of=slot_of,
+                 n_dropped=int(T * k - kept.sum()))
+        r["offsets"] = np.concatenate([[0], np.cumsum(kept)])
+        return r
+    _patch(mp, "dispatch", dispatch)
+
+
+def m_keep_last(mp):
+    def dispatch(idx, E, cap):
+        idx = np.asarray(idx)
+        T, k = idx.shape
+        r = _dispatch(idx, E, 0)
+        perm, slot_of = [], np.full(T * k, -1, np.int64)
+        kept = np.zeros(E, np.int64)
+        for e in range(E):
+            rows, slots = np.nonzero(idx == e)
+            n = rows.size if cap <= 0 else min(rows.size, cap)
+            kept[e] = n
+            for t, j in zip(rows[rows.size - n:], slots[rows.size - n:]):
+                slot_of[t * k + j] = len(perm)
+                perm.append(t * k + j)
+        r.update(kept=kept, perm=np.asarray(perm), slot_of=slot_of,
+                 n_dropped=int(T * k - kept.sum()))
+        r["offsets"] = np.concatenate([[0], np.cumsum(kept)])
+        return r
+    _patch(mp, "dispatch", dispatch)
+
+
+def m_renormalise_survivors(mp):
+    def combine(x_residual, y, slot_of, gate, k, n_shared=0, T=None,
+                tokens=None):
+        g = np.array(gate, F64)
+        for t in range(g.shape[0]):
+            keep = [slot_of[t * k + j] >= 0 for j in range(k)]
+            s = sum(g[t, j] for j in range(k) if keep[j])
+            if 0 < s:
+                g[t] = g[t] / s
+        return _combine(x_residual, y, slot_of, g, k, n_shared, T, tokens)
+    _patch(mp, "combine", combine)
+
+
+def m_transposed_w2(mp):
+    def ffn(X, act, w1, w_up, w2, b1, b2):
+        w2 = np.asarray(w2)
+        if w2.shape[0] == w2.shape[1]:
+            w2 = w2.T
+        return _ffn(X, act, w1, w_up, w2, b1, b2)
+    _patch(mp, "_ffn", ffn)
+
+
+def m_drop_bias_b2(mp):
+    def ffn(X, act, w1, w_up, w2, b1, b2):
+        if b2 is not None:
+            b2 = np.zeros_like(np.asarray(b2, F64))
+        return _ffn(X, act, w1, w_up, w2, b1, b2)
+    _patch(mp, "_ffn", ffn)
+
+
+def m_gelu_tanh(mp):
+    def gelu(z):
+        z = np.asarray(z, F64)
+        return 0.5 * z * (1 + np.tanh(math.sqrt(2 / math.pi)
+                                      * (z + 0.044715 * z ** 3)))
+    _patch(mp, "gelu", gelu)
+
+
+def m_silu_is_sigmoid(mp):
+    def silu(z):
+        z = np.asarray(z, F64)
+        return 1.0 / (1.0 + np.exp(-z))
+    _patch(mp, "silu", silu)
+
+
+def m_swap_gate_up(mp):
+    def ffn(X, act, w1, w_up, w2, b1, b2):
+        if act == "swiglu":
+            return _ffn(X, act, w_up, w1, w2, b1, b2)
+        return _ffn(X, act, w1, w_up, w2, b1, b2)
+    _patch(mp, "_ffn", ffn)
+
+
+def m_aux_post_capacity(mp):
+    def layer_forward(*a, **kw):
+        r = _layer(*a, **kw)
+        r["aux"] = _aux(r["kept"], r["probs"], kw.get("alpha", 0.01))
+        return r
+    _patch(mp, "layer_forward", layer_forward)
+
+    def aux_loss(counts, probs, alpha):
+        c = np.minimum(np.asarray(counts), 2)
+        return _aux(c, probs, alpha)
+    _patch(mp, "aux_loss", aux_loss)
+
+
+def m_aux_no_E(mp):
+    def aux_loss(counts, probs, alpha):
+        E = np.asarray(probs).shape[1]
+        return _aux(counts, probs, alpha) / E
+    _patch(mp, "aux_loss", aux_loss)
+
+
+def m_capacity_ceil(mp):
+    def capacity(T, k, E, cf_num, cf_den):
+        return max(1, -(-(cf_num * T * k) // (cf_den * E)))
+    _patch(mp, "capacity", capacity)
+
+
+def m_softmax_no_shift(mp):
+    def softmax(l):
+        l = np.asarray(l, F64)
+        with np.errstate(over="ignore", invalid="ignore"):
+            e = np.exp(l)
+            return e / e.sum(-1, keepdims=True)
+    _patch(mp, "softmax", softmax)
+
+
+def m_no_shared(mp):
+    def expert_ffn(x, perm, offsets, weights, act, k, n_shared=0,
+                   tokens=None):
+        y = _expert_ffn(x, perm, offsets, weights, act, k, n_shared, tokens)
+        T = np.asarray(x).shape[0]
+        y[T * k:] = 0.0
+        return y
+    _patch(mp, "expert_ffn", expert_ffn)
+
+
+def m_token_from_assignment_by_E(mp):
+    # a wrong index: token = a // E instead of a // k
+    def expert_ffn(x, perm, offsets, weights, act, k, n_shared=0,
+                   tokens=None):
+        E = len(offsets) - 1
+        return _expert_ffn(x, perm, offsets, weights, act, E, n_shared,
+                           tokens) if E != k else \
+            _expert_ffn(x, perm, offsets, weights, act, k, n_shared, tokens)
+    _patch(mp, "expert_ffn", expert_ffn)
+
+
+_layer = om.layer_forward
+
+MUTATIONS = [m_no_renormalise, m_tie_to_higher_index, m_bias_in_gates,
+             m_capacity_by_slot, m_keep_last, m_renormalise_survivors,
+             m_transposed_w2, m_drop_bias_b2, m_gelu_tanh, m_silu_is_sigmoid,
+             m_swap_gate_up, m_aux_post_capacity, m_aux_no_E,
+             m_capacity_ceil, m_softmax_no_shift, m_no_shared,
+             m_token_from_assignment_by_E]
+
+
+@pytest.mark.parametrize("mutate", MUTATIONS, ids=[m.__name__ for m in
+                                                   MUTATIONS])
+def test_some_pin_catches(mutate, monkeypatch):
+    mutate(monkeypatch)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except Exception as exc:          # AssertionError or a crash
+            caught.append((pin.__name__, type(exc).__name__))
+    assert caught, f"no pin caught {mutate.__name__}"
