@@ -1,0 +1,250 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) sparse mixture-of-experts layer
+ * forward pass.
+ *
+ * The layer (sources: web pages on sparse MoE layers, tagged
+ *   [RC]  randomcommits.com "Mixture-of-Experts routing",
+ *   [LBS] letsbuildsolutions.com "How Mixture of Experts Works: Sparse
+ *         Gating, Expert Routing, and the Architecture Behind Efficient Large
+ *         Language Models",
+ *   [HA]  hassanahmed.net "Mixture of Experts explained",
+ *   [GN]  getnybble.com "Mixture of Experts (MoE) - conditional computation
+ *         at scale",
+ *   [FA]  foundry.adhana.ai "Mixture-of-Experts routing"):
+ *
+ *   1. route     logits = x . Wr^T (+ router bias), probs = softmax(logits),
+ *                choose the top-k experts, gates = chosen probs renormalised
+ *                to sum to 1                    ([RC], [LBS] Gating Mechanism)
+ *   2. dispatch  group the (token, slot) assignments by expert, keep the
+ *                first `capacity` per expert in token order, drop the rest
+ *                                 ([RC], [LBS] The Capacity Factor, Token
+ *                                  Dropping and Overflow Handling)
+ *   3. expert    GELU MLP or SwiGLU per expert over its kept rows, plus an
+ *                optional always-on shared expert ([RC], [GN] Implementing a
+ *                complete MoE layer, DeepSeek-V3)
+ *   4. combine   out = x + shared + sum over kept slots of gate * expert out
+ *                                 ([RC], [FA] Concept)
+ *   5. aux       alpha * E * sum_e f_e * P_e  ([LBS] The Load Balancing
+ *                Problem, [GN] Load balancing and expert collapse)
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Every pointer argument except `p`, `w` and the problem/weights structs
+ *   themselves is a DEVICE pointer on the current HIP device, row-major,
+ *   contiguous, at least 16-byte aligned.  The workspace must be 256-byte
+ *   aligned.  The caller owns every buffer; the library never allocates,
+ *   frees or synchronises.
+ * - Each call validates all its arguments on the host first; a non-zero
+ *   status means nothing was enqueued.  MOE_OK means the work was enqueued
+ *   on `stream`; results are valid when the stream reaches that point.
+ * - The library holds no mutable global state; calls are reentrant.  Two
+ *   calls that share an output or workspace buffer must not overlap.
+ * - Element types: `x`, expert weights and biases, `y` and `out` all have
+ *   the problem's dtype (MOE_DTYPE_F32 or MOE_DTYPE_BF16).  Router weights,
+ *   router/selection biases, logits, gates and probabilities are float32
+ *   ([LBS] Dense vs Sparse: the router runs in float32).  Indices and
+ *   counts are int32.
+ * - Weights use nn.Linear storage ([out, in], the input dimension
+ *   contiguous) stacked over experts on a leading axis.
+ * - Results are deterministic: the same inputs give bit-identical outputs
+ *   (no floating-point atomics; every reduction has a fixed order).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define MOE_OK 0
+#define MOE_EINVAL (-1)     /* null required pointer, bad T/E/k/capacity  */
+#define MOE_ENOTSUP (-2)    /* shape or dtype this build does not support */
+#define MOE_EWORKSPACE (-3) /* workspace smaller than moe_workspace_bytes */
+#define MOE_EHIP (-4)       /* a kernel launch failed                     */
+
+/* ---- enums --------------------------------------------------------------- */
+#define MOE_ACT_GELU 0   /* Linear(+b1) -> exact erf GELU -> Linear(+b2)   */
+#define MOE_ACT_SWIGLU 1 /* W_down (silu(W_gate x) * (W_up x)), no biases  */
+#define MOE_DTYPE_F32 0
+#define MOE_DTYPE_BF16 1
+
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_TOP_K 8
+
+/*
+ * Problem description.
+ *   T          tokens (rows of x), >= 0.  T * top_k < 2^31.
+ *   d_model    hidden size d, a positive multiple of 64.
+ *   n_experts  routed experts E, 1..256.
+ *   top_k      experts per token k, 1..min(E, 8).
+ *   d_ff       expert intermediate size, a positive multiple of 64.
+ *   n_shared   always-on shared experts, 0 or 1 ([GN] DeepSeek-V3).
+ *   capacity   per-expert cap on kept assignments; <= 0 means no cap.
+ *   act        MOE_ACT_GELU or MOE_ACT_SWIGLU.
+ *   dtype      MOE_DTYPE_F32 or MOE_DTYPE_BF16.
+ *   aux_coef   alpha of the load-balance loss (0.01 for Mixtral: [LBS]).
+ */
+typedef struct moe_problem {
+  int32_t T;
+  int32_t d_model;
+  int32_t n_experts;
+  int32_t top_k;
+  int32_t d_ff;
+  int32_t n_shared;
+  int32_t capacity;
+  int32_t act;
+  int32_t dtype;
+  float aux_coef;
+} moe_problem;
+
+/*
+ * Expert weights (device pointers, problem dtype).
+ *   GELU:   w1 = W1 [E, d_ff, d], b1 [E, d_ff], w2 = W2 [E, d, d_ff],
+ *           b2 [E, d]; w_up must be NULL.
+ *   SwiGLU: w1 = W_gate [E, d_ff, d], w_up = W_up [E, d_ff, d],
+ *           w2 = W_down [E, d, d_ff]; b1, b2 must be NULL.
+ *   Shared expert (n_shared = 1): the same tensors without the expert axis
+ *   in shared_w1 / shared_w_up / shared_w2 / shared_b1 / shared_b2.
+ */
+typedef struct moe_expert_weights {
+  const void* w1;
+  const void* w_up;
+  const void* w2;
+  const void* b1;
+  const void* b2;
+  const void* shared_w1;
+  const void* shared_w_up;
+  const void* shared_w2;
+  const void* shared_b1;
+  const void* shared_b2;
+} moe_expert_weights;
+
+/*
+ * Per-expert capacity: the ideal share T*k/E times the capacity factor
+ * cf_num/cf_den, truncated, and at least 1 ([LBS] The Capacity Factor).
+ * Exact integer arithmetic.  Host-only.  Returns -1 on bad arguments
+ * (T < 0, k < 1, E < 1, cf_num <= 0, cf_den <= 0) or overflow of int32.
+ */
+int32_t moe_capacity(int32_t T, int32_t top_k, int32_t n_experts,
+                     int32_t cf_num, int32_t cf_den);
+
+/*
+ * Workspace bytes needed by every entry point below for problem `p`
+ * (one size serves all of them).  Host-only; writes *bytes.
+ * Returns MOE_EINVAL / MOE_ENOTSUP for a problem the library rejects.
+ */
+int32_t moe_workspace_bytes(const moe_problem* p, size_t* bytes);
+
+/*
+ * Step 1, route ([RC] How a sparse MoE layer works; [LBS] Gating Mechanism;
+ * [GN] The router, DeepSeek-V3).
+ *   x            [T, d] problem dtype.
+ *   w_router     [E, d] float32.
+ *   router_bias  [E] float32 or NULL: added to the logits (changes choice
+ *                and gates).
+ *   select_bias  [E] float32 or NULL: added to the float32 logits for the
+ *                choice only; gates and probabilities ignore it.
+ *   logits       [T, E] float32 output, or NULL to skip writing it.
+ *   topk_idx     [T, k] int32 output: chosen experts in descending order of
+ *                selection key; equal keys go to the lower expert index.
+ *   topk_gate    [T, k] float32 output: gates, summing to 1 per token.
+ *   prob_mean    [E] float32 output: mean over tokens of softmax(logits),
+ *                the P of the aux loss (0 when T = 0).
+ */
+int32_t moe_route(const moe_problem* p, const void* x, const float* w_router,
+                  const float* router_bias, const float* select_bias,
+                  float* logits, int32_t* topk_idx, float* topk_gate,
+                  float* prob_mean, void* ws, size_t ws_bytes,
+                  hipStream_t stream);
+
+/*
+ * Step 2, dispatch and aux loss ([RC] capacity check; [LBS] The Capacity
+ * Factor, The Load Balancing Problem).  Assignment a = t*k + j is slot j of
+ * token t.
+ *   topk_idx   [T, k] int32 input (each row: k distinct experts in [0, E)).
+ *   prob_mean  [E] float32 input; may be NULL only if aux_loss is NULL.
+ *   counts     [E] int32 output: assignments routed to each expert, before
+ *              the capacity cut.
+ *   offsets    [E+1] int32 output: exclusive scan of kept counts
+ *              (kept = min(count, capacity), or count without a cap).
+ *   perm       [T*k] int32 output: rows [offsets[e], offsets[e+1]) hold the
+ *              kept assignment ids of expert e in ascending token order;
+ *              entries from offsets[E] on are set to -1.
+ *   slot_of    [T*k] int32 output: row of perm holding assignment a, or -1
+ *              if a was dropped.
+ *   n_dropped  [1] int32 output: T*k - offsets[E].
+ *   aux_loss   [1] float32 output or NULL: alpha*E*sum_e (count_e/T)*P_e,
+ *              0 when T = 0.
+ */
+int32_t moe_dispatch(const moe_problem* p, const int32_t* topk_idx,
+                     const float* prob_mean, int32_t* counts,
+                     int32_t* offsets, int32_t* perm, int32_t* slot_of,
+                     int32_t* n_dropped, float* aux_loss, void* ws,
+                     size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Steps 3-4, expert FFNs over each expert's kept rows ([RC]; [GN]
+ * Implementing a complete MoE layer; [HA]: group the tokens by expert and
+ * run each expert once over its batch).
+ *   x        [T, d] input.
+ *   perm, offsets  as written by moe_dispatch.
+ *   w        expert weights (see moe_expert_weights).
+ *   y        [T*k + n_shared*T, d] output, problem dtype: row r <
+ *            offsets[E] is expert e (offsets[e] <= r < offsets[e+1]) applied
+ *            to token perm[r] / k; row T*k + t is the shared expert applied
+ *            to token t.  Rows [offsets[E], T*k) are not written.
+ */
+int32_t moe_expert_ffn(const moe_problem* p, const void* x,
+                       const int32_t* perm, const int32_t* offsets,
+                       const moe_expert_weights* w, void* y, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Step 5, combine ([RC]: weighted sum plus residual; [LBS] Token Dropping:
+ * a dropped slot contributes zero; [FA] Concept).
+ *   x_residual  [T, d] or NULL (NULL omits the residual, as the [LBS], [HA]
+ *               and [GN] snippets do).
+ *   y           [T*k + n_shared*T, d] as written by moe_expert_ffn.
+ *   slot_of     [T*k], topk_gate [T, k] as written by dispatch / route.
+ *   out         [T, d] output, problem dtype:
+ *               out[t] = x[t] + y[T*k+t] (shared) + sum over slots j with
+ *               slot_of[t*k+j] >= 0 of gate[t,j] * y[slot_of[t*k+j]],
+ *               accumulated in float32 in that order and rounded once.
+ *               Surviving gates are not renormalised.
+ */
+int32_t moe_combine(const moe_problem* p, const void* x_residual,
+                    const void* y, const int32_t* slot_of,
+                    const float* topk_gate, void* out, hipStream_t stream);
+
+/*
+ * The whole layer: steps 1-5 and the aux loss, enqueued back to back with
+ * no host synchronisation.  Outputs:
+ *   out        [T, d] problem dtype (residual always added: [RC]).
+ *   aux_loss   [1] float32 or NULL.
+ *   counts     [E] int32 or NULL (pre-capacity assignments per expert).
+ *   n_dropped  [1] int32 or NULL.
+ *   topk_idx   [T, k] int32 or NULL (the routing decisions).
+ * Intermediates live in the workspace.
+ */
+int32_t moe_layer_forward(const moe_problem* p, const void* x,
+                          const float* w_router, const float* router_bias,
+                          const float* select_bias,
+                          const moe_expert_weights* w, void* out,
+                          float* aux_loss, int32_t* counts,
+                          int32_t* n_dropped, int32_t* topk_idx, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char* moe_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,270 @@
+"""MI355X (gfx950) sparse mixture-of-experts layer forward pass.
+
+Thin Python binding over the C ABI of ``libmoe.so`` (declared in
+``include/moe.h``).  The functions below have the C entry points' names and
+only marshal arguments: tensors become device pointers, ``None`` becomes
+NULL, and the stream defaults to torch's current stream.  Every step of the
+layer runs in the HIP kernels; there is no Python or CPU fallback.  If the
+library is not built the import of the binding fails loudly.
+
+PyTorch is used only for device memory and streams.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # must precede the library load: one HIP runtime per process
+
+from . import synth  # noqa: F401  (seeded workloads)
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
+MOE_ACT_GELU, MOE_ACT_SWIGLU = 0, 1
+MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
+ACT = {"gelu": MOE_ACT_GELU, "swiglu": MOE_ACT_SWIGLU}
+DTYPE = {"f32": MOE_DTYPE_F32, "bf16": MOE_DTYPE_BF16}
+TORCH_DTYPE = {MOE_DTYPE_F32: torch.float32, MOE_DTYPE_BF16: torch.bfloat16}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {moe_status_string(status)} ({status})")
+
+
+class moe_problem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("d_ff", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("act", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("aux_coef", ctypes.c_float)]
+
+
+class moe_expert_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("w1", "w_up", "w2", "b1", "b2", "shared_w1", "shared_w_up",
+                 "shared_w2", "shared_b1", "shared_b2")]
+
+
+_P = ctypes.POINTER(moe_problem)
+_W = ctypes.POINTER(moe_expert_weights)
+_V = ctypes.c_void_p
+_SZ = ctypes.c_size_t
+_I32 = ctypes.c_int32
+
+_SIGS = {
+    "moe_capacity": (_I32, [_I32, _I32, _I32, _I32, _I32]),
+    "moe_workspace_bytes": (_I32, [_P, ctypes.POINTER(_SZ)]),
+    "moe_route": (_I32, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _SZ, _V]),
+    "moe_dispatch": (_I32, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _SZ,
+                            _V]),
+    "moe_expert_ffn": (_I32, [_P, _V, _V, _V, _W, _V, _V, _SZ, _V]),
+    "moe_combine": (_I32, [_P, _V, _V, _V, _V, _V, _V]),
+    "moe_layer_forward": (_I32, [_P, _V, _V, _V, _V, _W, _V, _V, _V, _V, _V,
+                                 _V, _SZ, _V]),
+    "moe_status_string": (ctypes.c_char_p, [_I32]),
+}
+EXPORTS = tuple(_SIGS)
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run "
+            "`python -m sparse_mixture_experts_34_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGS.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status, where):
+    if status != MOE_OK:
+        raise MoEError(status, where)
+
+
+def problem(T, d_model, n_experts, top_k, d_ff, *, n_shared=0, capacity=0,
+            act="swiglu", dtype="bf16", aux_coef=0.01) -> moe_problem:
+    return moe_problem(T, d_model, n_experts, top_k, d_ff, n_shared, capacity,
+                       ACT[act] if isinstance(act, str) else act,
+                       DTYPE[dtype] if isinstance(dtype, str) else dtype,
+                       aux_coef)
+
+
+def problem_for(wl) -> moe_problem:
+    """The C problem struct of a :class:`synth.Workload`."""
+    return problem(wl.T, wl.d_model, wl.n_experts, wl.top_k, wl.d_ff,
+                   n_shared=wl.n_shared, capacity=wl.capacity, act=wl.act,
+                   dtype=wl.dtype, aux_coef=wl.aux_coef)
+
+
+def expert_weights(w: dict) -> moe_expert_weights:
+    """C weights struct from a dict of device tensors keyed like the
+    layer's weights (w1/w2/b1/b2 or w_gate/w_up/w_down, shared_*)."""
+    get = lambda *names: next((_ptr(w[n]) for n in names
+                               if w.get(n) is not None), None)
+    return moe_expert_weights(
+        get("w1", "w_gate"), get("w_up"), get("w2", "w_down"), get("b1"),
+        get("b2"), get("shared_w1", "shared_gate"), get("shared_up"),
+        get("shared_w2", "shared_down"), get("shared_b1"), get("shared_b2"))
+
+
+# ---------------------------------------------------------------------------
+# the C entry points
+# ---------------------------------------------------------------------------
+
+def moe_status_string(status: int) -> str:
+    return _lib.moe_status_string(status).decode()
+
+
+def moe_capacity(T, top_k, n_experts, cf_num, cf_den) -> int:
+    return int(_lib.moe_capacity(T, top_k, n_experts, cf_num, cf_den))
+
+
+def moe_workspace_bytes(p: moe_problem) -> int:
+    n = _SZ(0)
+    _check(_lib.moe_workspace_bytes(ctypes.byref(p), ctypes.byref(n)),
+           "moe_workspace_bytes")
+    return n.value
+
+
+def workspace(p: moe_problem, device="cuda") -> torch.Tensor:
+    """A workspace tensor of the size the library asks for (256-byte
+    aligned: torch's caching allocator aligns blocks to 512 bytes)."""
+    n = moe_workspace_bytes(p)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+    assert ws.data_ptr() % 256 == 0
+    return ws
+
+
+def moe_route(p, x, w_router, router_bias, select_bias, logits, topk_idx,
+              topk_gate, prob_mean, ws, stream=None):
+    _check(_lib.moe_route(ctypes.byref(p), _ptr(x), _ptr(w_router),
+                          _ptr(router_bias), _ptr(select_bias), _ptr(logits),
+                          _ptr(topk_idx), _ptr(topk_gate), _ptr(prob_mean),
+                          _ptr(ws), ws.numel() if ws is not None else 0,
+                          _stream(stream)), "moe_route")
+
+
+def moe_dispatch(p, topk_idx, prob_mean, counts, offsets, perm, slot_of,
+                 n_dropped, aux_loss, ws, stream=None):
+    _check(_lib.moe_dispatch(ctypes.byref(p), _ptr(topk_idx),
+                             _ptr(prob_mean), _ptr(counts), _ptr(offsets),
+                             _ptr(perm), _ptr(slot_of), _ptr(n_dropped),
+                             _ptr(aux_loss), _ptr(ws),
+                             ws.numel() if ws is not None else 0,
+                             _stream(stream)), "moe_dispatch")
+
+
+def moe_expert_ffn(p, x, perm, offsets, weights, y, ws, stream=None):
+    w = weights if isinstance(weights, moe_expert_weights) else \
+        expert_weights(weights)
+    _check(_lib.moe_expert_ffn(ctypes.byref(p), _ptr(x), _ptr(perm),
+                               _ptr(offsets), ctypes.byref(w), _ptr(y),
+                               _ptr(ws), ws.numel() if ws is not None else 0,
+                               _stream(stream)), "moe_expert_ffn")
+
+
+def moe_combine(p, x_residual, y, slot_of, topk_gate, out, stream=None):
+    _check(_lib.moe_combine(ctypes.byref(p), _ptr(x_residual), _ptr(y),
+                            _ptr(slot_of), _ptr(topk_gate), _ptr(out),
+                            _stream(stream)), "moe_combine")
+
+
+def moe_layer_forward(p, x, w_router, router_bias, select_bias, weights, out,
+                      aux_loss, counts, n_dropped, topk_idx, ws,
+                      stream=None):
+    w = weights if isinstance(weights, moe_expert_weights) else \
+        expert_weights(weights)
+    _check(_lib.moe_layer_forward(ctypes.byref(p), _ptr(x), _ptr(w_router),
+                                  _ptr(router_bias), _ptr(select_bias),
+                                  ctypes.byref(w), _ptr(out), _ptr(aux_loss),
+                                  _ptr(counts), _ptr(n_dropped),
+                                  _ptr(topk_idx), _ptr(ws),
+                                  ws.numel() if ws is not None else 0,
+                                  _stream(stream)), "moe_layer_forward")
+
+
+# ---------------------------------------------------------------------------
+# convenience: allocate outputs and run the whole layer
+# ---------------------------------------------------------------------------
+
+def layer_forward(inp: dict, wl, ws=None, stream=None, return_routing=False):
+    """Run the layer on the inputs of :func:`synth.make_inputs` (device
+    tensors).  Returns ``out``, ``aux``, ``counts``, ``n_dropped`` (and
+    ``topk_idx`` when asked) as device tensors."""
+    p = problem_for(wl)
+    dev = inp["x"].device
+    if ws is None:
+        ws = workspace(p, dev)
+    out = torch.empty_like(inp["x"])
+    aux = torch.empty(1, dtype=torch.float32, device=dev)
+    counts = torch.empty(wl.n_experts, dtype=torch.int32, device=dev)
+    nd = torch.empty(1, dtype=torch.int32, device=dev)
+    idx = (torch.empty(wl.T, wl.top_k, dtype=torch.int32, device=dev)
+           if return_routing else None)
+    moe_layer_forward(p, inp["x"], inp["w_router"], inp.get("router_bias"),
+                      inp.get("select_bias"), inp, out, aux, counts, nd, idx,
+                      ws, stream)
+    res = {"out": out, "aux": aux, "counts": counts, "n_dropped": nd}
+    if return_routing:
+        res["topk_idx"] = idx
+    return res
+
+
+def flops_and_bytes(wl, counts, kept_total) -> tuple:
+    """Algorithmic FLOPs and HBM bytes of one layer forward: 2 FLOPs per
+    multiply-add over the kept assignments (plus shared rows) and the
+    router; bytes of the touched experts' weights once plus x, out, the
+    router weight and biases.  ``counts`` are per-expert pre-capacity
+    assignment counts."""
+    esz = 2 if wl.dtype == "bf16" else 4
+    d, f, E = wl.d_model, wl.d_ff, wl.n_experts
+    per_expert = (3 if wl.act == "swiglu" else 2) * d * f
+    bias = (f + d) if wl.act == "gelu" else 0
+    rows = kept_total + wl.n_shared * wl.T
+    flops = 2 * rows * per_expert + 2 * wl.T * d * E
+    touched = sum(1 for c in counts if c > 0) + wl.n_shared
+    byts = (touched * (per_expert + bias) * esz + 2 * wl.T * d * esz
+            + E * d * 4 + (E * 4 if wl.zipf_s > 0 else 0)
+            + (E * 4 if wl.select_bias_std > 0 else 0))
+    return flops, byts
+
+
+__all__ = [n for n in dir() if n.startswith("moe_")] + [
+    "problem", "problem_for", "expert_weights", "workspace", "layer_forward",
+    "flops_and_bytes", "MoEError", "synth", "library_path", "EXPORTS"]

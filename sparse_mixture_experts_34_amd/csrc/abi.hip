@@ -1,0 +1,330 @@
+// C ABI of the MoE layer: argument validation, workspace layout, launches.
+// Every entry point validates everything on the host before enqueuing the
+// first kernel, so an error status means nothing was enqueued.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+
+namespace moe {
+int ffn_schedule(int dtype, int T, int k, int E);
+}
+
+namespace {
+
+using namespace moe;
+
+constexpr size_t ALIGN = 256;
+
+size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct Layout {
+  int ksplit;
+  int nrb;       // route blocks
+  int nchunks;   // dispatch chunks
+  size_t part, idx, gate, rpart, pmean, chunk, counts, offsets, perm, slot,
+      ndrop, aux, h, y, total;
+};
+
+Layout make_layout(const moe_problem& p) {
+  Layout L;
+  const long long T = p.T, E = p.n_experts, k = p.top_k;
+  const long long rows = T * k + (long long)p.n_shared * T;
+  const size_t esz = p.dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  L.ksplit = router_ksplit(p.T, p.d_model, p.n_experts, p.dtype);
+  L.nrb = route_blocks(p.T);
+  L.nchunks = dispatch_chunks(T * k);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + (bytes ? bytes : 1));
+    return o;
+  };
+  L.part = take((size_t)L.ksplit * T * E * 4);
+  L.idx = take((size_t)T * k * 4);
+  L.gate = take((size_t)T * k * 4);
+  L.rpart = take((size_t)L.nrb * E * 4);
+  L.pmean = take((size_t)E * 4);
+  L.chunk = take((size_t)L.nchunks * E * 4);
+  L.counts = take((size_t)E * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.perm = take((size_t)T * k * 4);
+  L.slot = take((size_t)T * k * 4);
+  L.ndrop = take(4);
+  L.aux = take(4);
+  L.h = take((size_t)rows * p.d_ff * esz);
+  L.y = take((size_t)rows * p.d_model * esz);
+  L.total = off;
+  return L;
+}
+
+int32_t check_problem(const moe_problem* p) {
+  if (!p) return MOE_EINVAL;
+  if (p->T < 0 || p->n_experts < 1 || p->n_experts > MOE_MAX_EXPERTS)
+    return MOE_EINVAL;
+  if (p->top_k < 1 || p->top_k > p->n_experts) return MOE_EINVAL;
+  if (p->top_k > MOE_MAX_TOP_K) return MOE_ENOTSUP;
+  if (p->d_model <= 0 || p->d_ff <= 0) return MOE_EINVAL;
+  if (p->d_model % 64 != 0 || p->d_ff % 64 != 0) return MOE_ENOTSUP;
+  if (p->n_shared != 0 && p->n_shared != 1) return MOE_EINVAL;
+  if (p->act != MOE_ACT_GELU && p->act != MOE_ACT_SWIGLU) return MOE_EINVAL;
+  if (p->dtype != MOE_DTYPE_F32 && p->dtype != MOE_DTYPE_BF16)
+    return MOE_EINVAL;
+  if (!isfinite(p->aux_coef)) return MOE_EINVAL;
+  const long long rows = (long long)p->T * p->top_k + (long long)p->n_shared * p->T;
+  if (rows >= (1LL << 31)) return MOE_ENOTSUP;
+  return MOE_OK;
+}
+
+int32_t check_ws(const moe_problem* p, const void* ws, size_t ws_bytes) {
+  const Layout L = make_layout(*p);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  if (!ws && L.total) return MOE_EINVAL;
+  if (((uintptr_t)ws) % ALIGN) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+int32_t check_weights(const moe_problem* p, const moe_expert_weights* w) {
+  if (!w) return MOE_EINVAL;
+  if (p->act == MOE_ACT_SWIGLU) {
+    if (!w->w1 || !w->w_up || !w->w2) return MOE_EINVAL;
+    if (w->b1 || w->b2) return MOE_EINVAL;
+    if (p->n_shared &&
+        (!w->shared_w1 || !w->shared_w_up || !w->shared_w2 || w->shared_b1 ||
+         w->shared_b2))
+      return MOE_EINVAL;
+  } else {
+    if (!w->w1 || !w->w2 || !w->b1 || !w->b2) return MOE_EINVAL;
+    if (w->w_up) return MOE_EINVAL;
+    if (p->n_shared && (!w->shared_w1 || !w->shared_w2 || !w->shared_b1 ||
+                        !w->shared_b2 || w->shared_w_up))
+      return MOE_EINVAL;
+  }
+  return MOE_OK;
+}
+
+int32_t status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+#define MOE_TRY(expr)                                    \
+  do {                                                   \
+    hipError_t e_ = (expr);                              \
+    if (e_ != hipSuccess) return status_of(e_);          \
+  } while (0)
+
+FfnArgs ffn_args(const moe_problem* p, const void* x, const int32_t* perm,
+                 const int32_t* offsets, const moe_expert_weights* w, void* h,
+                 void* y) {
+  FfnArgs a;
+  a.dtype = p->dtype;
+  a.act = p->act;
+  a.T = p->T;
+  a.d = p->d_model;
+  a.E = p->n_experts;
+  a.k = p->top_k;
+  a.d_ff = p->d_ff;
+  a.n_shared = p->n_shared;
+  a.x = x;
+  a.perm = perm;
+  a.offsets = offsets;
+  a.w1 = w->w1;
+  a.w_up = w->w_up;
+  a.w2 = w->w2;
+  a.b1 = w->b1;
+  a.b2 = w->b2;
+  a.sw1 = w->shared_w1;
+  a.sw_up = w->shared_w_up;
+  a.sw2 = w->shared_w2;
+  a.sb1 = w->shared_b1;
+  a.sb2 = w->shared_b2;
+  a.h = h;
+  a.y = y;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_capacity(int32_t T, int32_t top_k, int32_t n_experts,
+                     int32_t cf_num, int32_t cf_den) {
+  if (T < 0 || top_k < 1 || n_experts < 1 || cf_num <= 0 || cf_den <= 0)
+    return -1;
+  const long long num = (long long)cf_num * T * top_k;
+  const long long den = (long long)cf_den * n_experts;
+  const long long c = num / den;
+  if (c >= (1LL << 31)) return -1;
+  return c < 1 ? 1 : (int32_t)c;
+}
+
+int32_t moe_workspace_bytes(const moe_problem* p, size_t* bytes) {
+  int32_t st = check_problem(p);
+  if (st) return st;
+  if (!bytes) return MOE_EINVAL;
+  *bytes = make_layout(*p).total;
+  return MOE_OK;
+}
+
+int32_t moe_route(const moe_problem* p, const void* x, const float* w_router,
+                  const float* router_bias, const float* select_bias,
+                  float* logits, int32_t* topk_idx, float* topk_gate,
+                  float* prob_mean, void* ws, size_t ws_bytes,
+                  hipStream_t stream) {
+  int32_t st = check_problem(p);
+  if (st) return st;
+  if (!prob_mean) return MOE_EINVAL;
+  if (p->T > 0 && (!x || !w_router || !topk_idx || !topk_gate))
+    return MOE_EINVAL;
+  if ((st = check_ws(p, ws, ws_bytes))) return st;
+  if (p->T == 0) return status_of(launch_fill_zero32(prob_mean, p->n_experts, stream));
+  const Layout L = make_layout(*p);
+  char* w = (char*)ws;
+  float* part = (float*)(w + L.part);
+  float* rpart = (float*)(w + L.rpart);
+  MOE_TRY(launch_router_logits_partial(p->dtype, x, w_router, part, p->T,
+                                       p->d_model, p->n_experts, L.ksplit,
+                                       stream));
+  MOE_TRY(launch_route_select_from(part, L.ksplit, router_bias, select_bias,
+                                   logits, topk_idx, topk_gate, rpart, p->T,
+                                   p->n_experts, p->top_k, stream));
+  MOE_TRY(launch_prob_mean(rpart, prob_mean, L.nrb, p->T, p->n_experts,
+                           stream));
+  return MOE_OK;
+}
+
+int32_t moe_dispatch(const moe_problem* p, const int32_t* topk_idx,
+                     const float* prob_mean, int32_t* counts,
+                     int32_t* offsets, int32_t* perm, int32_t* slot_of,
+                     int32_t* n_dropped, float* aux_loss, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  int32_t st = check_problem(p);
+  if (st) return st;
+  if (!counts || !offsets || !n_dropped) return MOE_EINVAL;
+  if (p->T > 0 && (!topk_idx || !perm || !slot_of)) return MOE_EINVAL;
+  if (aux_loss && !prob_mean) return MOE_EINVAL;
+  if ((st = check_ws(p, ws, ws_bytes))) return st;
+  if (p->T == 0) {
+    MOE_TRY(launch_fill_zero32(counts, p->n_experts, stream));
+    MOE_TRY(launch_fill_zero32(offsets, p->n_experts + 1, stream));
+    MOE_TRY(launch_fill_zero32(n_dropped, 1, stream));
+    if (aux_loss) MOE_TRY(launch_fill_zero32(aux_loss, 1, stream));
+    return MOE_OK;
+  }
+  const Layout L = make_layout(*p);
+  DispatchArgs a;
+  a.idx = topk_idx;
+  a.prob_mean_in = prob_mean;
+  a.partials = nullptr;
+  a.n_partials = 0;
+  a.prob_mean_out = nullptr;
+  a.counts = counts;
+  a.offsets = offsets;
+  a.perm = perm;
+  a.slot_of = slot_of;
+  a.n_dropped = n_dropped;
+  a.aux = aux_loss;
+  a.chunk_ws = (int32_t*)((char*)ws + L.chunk);
+  a.T = p->T;
+  a.E = p->n_experts;
+  a.k = p->top_k;
+  a.capacity = p->capacity;
+  a.aux_coef = p->aux_coef;
+  return status_of(launch_dispatch(a, stream));
+}
+
+int32_t moe_expert_ffn(const moe_problem* p, const void* x,
+                       const int32_t* perm, const int32_t* offsets,
+                       const moe_expert_weights* w, void* y, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  int32_t st = check_problem(p);
+  if (st) return st;
+  if ((st = check_weights(p, w))) return st;
+  if (p->T > 0 && (!x || !perm || !offsets || !y)) return MOE_EINVAL;
+  if ((st = check_ws(p, ws, ws_bytes))) return st;
+  if (p->T == 0) return MOE_OK;
+  const Layout L = make_layout(*p);
+  FfnArgs a = ffn_args(p, x, perm, offsets, w, (char*)ws + L.h, y);
+  return status_of(launch_expert_ffn(a, stream));
+}
+
+int32_t moe_combine(const moe_problem* p, const void* x_residual,
+                    const void* y, const int32_t* slot_of,
+                    const float* topk_gate, void* out, hipStream_t stream) {
+  int32_t st = check_problem(p);
+  if (st) return st;
+  if (p->T > 0 && (!y || !slot_of || !topk_gate || !out)) return MOE_EINVAL;
+  if (p->T == 0) return MOE_OK;
+  return status_of(launch_combine(p->dtype, x_residual, y, slot_of, topk_gate,
+                                  out, p->T, p->d_model, p->top_k,
+                                  p->n_shared, stream));
+}
+
+int32_t moe_layer_forward(const moe_problem* p, const void* x,
+                          const float* w_router, const float* router_bias,
+                          const float* select_bias,
+                          const moe_expert_weights* w, void* out,
+                          float* aux_loss, int32_t* counts,
+                          int32_t* n_dropped, int32_t* topk_idx, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  int32_t st = check_problem(p);
+  if (st) return st;
+  if ((st = check_weights(p, w))) return st;
+  if (p->T > 0 && (!x || !w_router || !out)) return MOE_EINVAL;
+  if ((st = check_ws(p, ws, ws_bytes))) return st;
+  if (p->T == 0) {
+    if (aux_loss) MOE_TRY(launch_fill_zero32(aux_loss, 1, stream));
+    if (counts) MOE_TRY(launch_fill_zero32(counts, p->n_experts, stream));
+    if (n_dropped) MOE_TRY(launch_fill_zero32(n_dropped, 1, stream));
+    return MOE_OK;
+  }
+  const Layout L = make_layout(*p);
+  char* wsb = (char*)ws;
+  int32_t* idx = topk_idx ? topk_idx : (int32_t*)(wsb + L.idx);
+  float* gate = (float*)(wsb + L.gate);
+  float* part = (float*)(wsb + L.part);
+  float* rpart = (float*)(wsb + L.rpart);
+  MOE_TRY(launch_router_logits_partial(p->dtype, x, w_router, part, p->T,
+                                       p->d_model, p->n_experts, L.ksplit,
+                                       stream));
+  MOE_TRY(launch_route_select_from(part, L.ksplit, router_bias, select_bias,
+                                   nullptr, idx, gate, rpart, p->T,
+                                   p->n_experts, p->top_k, stream));
+  DispatchArgs a;
+  a.idx = idx;
+  a.prob_mean_in = nullptr;
+  a.partials = rpart;
+  a.n_partials = L.nrb;
+  a.prob_mean_out = (float*)(wsb + L.pmean);
+  a.counts = counts ? counts : (int32_t*)(wsb + L.counts);
+  a.offsets = (int32_t*)(wsb + L.offsets);
+  a.perm = (int32_t*)(wsb + L.perm);
+  a.slot_of = (int32_t*)(wsb + L.slot);
+  a.n_dropped = n_dropped ? n_dropped : (int32_t*)(wsb + L.ndrop);
+  a.aux = aux_loss ? aux_loss : (float*)(wsb + L.aux);
+  a.chunk_ws = (int32_t*)(wsb + L.chunk);
+  a.T = p->T;
+  a.E = p->n_experts;
+  a.k = p->top_k;
+  a.capacity = p->capacity;
+  a.aux_coef = p->aux_coef;
+  MOE_TRY(launch_dispatch(a, stream));
+  void* y = wsb + L.y;
+  FfnArgs f = ffn_args(p, x, a.perm, a.offsets, w, wsb + L.h, y);
+  MOE_TRY(launch_expert_ffn(f, stream));
+  MOE_TRY(launch_combine(p->dtype, x, y, a.slot_of, gate, out, p->T,
+                         p->d_model, p->top_k, p->n_shared, stream));
+  return MOE_OK;
+}
+
+const char* moe_status_string(int32_t status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK: success";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+    case MOE_ENOTSUP: return "MOE_ENOTSUP: shape or type not supported";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace too small";
+    case MOE_EHIP: return "MOE_EHIP: kernel launch failed";
+    default: return "unknown MoE status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,237 @@
+// Dispatch: group (token, slot) assignments by expert under a capacity cut,
+// and the load-balance aux loss.
+//
+// For each expert the assignments routed to it are ranked in ascending
+// token order; ranks below the capacity are kept, the rest dropped (their
+// MoE output is zero and the residual carries the token) - randomcommits.com
+// "Mixture-of-Experts routing", How a sparse MoE layer works (the capacity
+// check on a row-major nonzero of the routing mask);
+// letsbuildsolutions.com "How Mixture of Experts Works", The Capacity
+// Factor and Token Dropping and Overflow Handling.  The aux loss is
+// alpha * E * sum_e f_e P_e with f_e the pre-capacity fraction of
+// assignments routed to e per token and P_e the mean router probability
+// (same page, The Load Balancing Problem).
+//
+// Assignment a = t*k + j.  For a fixed expert, ascending a is ascending t
+// (a token never picks an expert twice), so the stable order is the
+// assignment order.  The work splits into chunks of 256 consecutive
+// assignments, one wave each:
+//   count   per-chunk expert histogram (LDS integer atomics: the final
+//           counts do not depend on their order)
+//   scan    one workgroup: per expert, exclusive scan over chunks (chunk
+//           base ranks), counts, kept = min(count, capacity), offsets =
+//           exclusive scan of kept over experts, n_dropped, prob mean and
+//           aux loss (fixed-order sums)
+//   scatter per chunk, 64 assignments at a time: an assignment's rank is its
+//           chunk base plus the number of earlier same-expert assignments
+//           (earlier rounds: LDS counter; same round: lanes below it)
+// Small batches (at most 4 chunks) run all three in one workgroup.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int DW = DISPATCH_WAVES;
+constexpr int CH = DISPATCH_CHUNK;
+
+// Histogram of chunk `c` into hist[0..E) (must start at zero).
+// Expert ids outside [0, E) are ignored here and dropped by the scatter.
+__device__ __forceinline__ void count_chunk(const int32_t* __restrict__ idx,
+                                            long long tk, int E, int c,
+                                            int* hist, int lane) {
+  for (int r = 0; r < CH / 64; ++r) {
+    long long a = (long long)c * CH + r * 64 + lane;
+    if (a < tk) {
+      const int e = idx[a];
+      if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
+    }
+  }
+}
+
+// Rank and scatter the assignments of chunk c.  base[e] holds the chunk's
+// base rank per expert and is advanced in place.
+__device__ __forceinline__ void scatter_chunk(
+    const int32_t* __restrict__ idx, long long tk, int c, int* base,
+    const int32_t* offsets, int E, int32_t* __restrict__ perm,
+    int32_t* __restrict__ slot_of, int lane) {
+  for (int r = 0; r < CH / 64; ++r) {
+    const long long a = (long long)c * CH + r * 64 + lane;
+    int e = a < tk ? idx[a] : -1;
+    if ((unsigned)e >= (unsigned)E) e = -1;
+    int before = 0;
+#pragma unroll 16
+    for (int l = 0; l < 64; ++l) {
+      const int v = __builtin_amdgcn_readlane(e, l);
+      before += (v == e && l < lane) ? 1 : 0;
+    }
+    const int rank = e >= 0 ? base[e] + before : 0;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0);
+    if (e >= 0) atomicAdd(&base[e], 1);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0);
+    if (a < tk && e < 0) slot_of[a] = -1;
+    if (e >= 0) {
+      const int keep = offsets[e + 1] - offsets[e];
+      if (rank < keep) {
+        const int p = offsets[e] + rank;
+        perm[p] = (int32_t)a;
+        slot_of[a] = p;
+      } else {
+        slot_of[a] = -1;
+      }
+    }
+  }
+  // perm rows past the kept total are set to -1
+  const int total = offsets[E];
+  for (int r = 0; r < CH / 64; ++r) {
+    const long long p = (long long)c * CH + r * 64 + lane;
+    if (p < tk && p >= total) perm[p] = -1;
+  }
+}
+
+// Scan over chunks and experts; executed by one 256-thread workgroup.
+// chunk[c*E + e] holds per-chunk counts on entry and chunk base ranks on
+// exit.  Writes counts, offsets, n_dropped, prob mean and aux.
+__device__ void scan_all(int* chunk, int nchunks, const DispatchArgs& a,
+                         int32_t* offsets_out, int* red_i, float* red_f) {
+  const int e = threadIdx.x;
+  const int E = a.E;
+  int count = 0;
+  if (e < E) {
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = chunk[c * E + e];
+      chunk[c * E + e] = count;
+      count += v;
+    }
+  }
+  int kept = (e < E) ? (a.capacity > 0 ? min(count, a.capacity) : count) : 0;
+  // exclusive scan of kept over the (<= 256) experts
+  red_i[e] = kept;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    int v = (e >= o) ? red_i[e - o] : 0;
+    __syncthreads();
+    red_i[e] += v;
+    __syncthreads();
+  }
+  const int incl = red_i[e];
+  if (e < E) {
+    a.counts[e] = count;
+    offsets_out[e] = incl - kept;
+    if (e == E - 1) {
+      offsets_out[E] = incl;
+      *a.n_dropped = (int32_t)((long long)a.T * a.k - incl);
+    }
+  }
+  // probability mean and aux loss
+  float term = 0.f;
+  if (e < E) {
+    float pm;
+    if (a.partials) {
+      float v = 0.f;
+      for (int b = 0; b < a.n_partials; ++b) v += a.partials[(size_t)b * E + e];
+      pm = v / (float)a.T;
+      if (a.prob_mean_out) a.prob_mean_out[e] = pm;
+    } else {
+      pm = a.prob_mean_in ? a.prob_mean_in[e] : 0.f;
+    }
+    term = ((float)count / (float)a.T) * pm;
+  }
+  red_f[e] = term;
+  __syncthreads();
+  for (int o = 128; o >= 1; o >>= 1) {
+    if (e < o) red_f[e] += red_f[e + o];
+    __syncthreads();
+  }
+  if (e == 0 && a.aux) *a.aux = a.aux_coef * (float)E * red_f[0];
+}
+
+__global__ __launch_bounds__(DW * 64) void dispatch_count_kernel(
+    const int32_t* __restrict__ idx, long long tk, int nchunks, int E,
+    int32_t* __restrict__ chunk_ws) {
+  __shared__ int hist[DW][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int e = lane; e < 256; e += 64) hist[wave][e] = 0;
+  __syncthreads();
+  const int c = blockIdx.x * DW + wave;
+  if (c < nchunks) count_chunk(idx, tk, E, c, hist[wave], lane);
+  __syncthreads();
+  if (c < nchunks)
+    for (int e = lane; e < E; e += 64) chunk_ws[(size_t)c * E + e] = hist[wave][e];
+}
+
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(DispatchArgs a,
+                                                            int nchunks) {
+  __shared__ int red_i[256];
+  __shared__ float red_f[256];
+  scan_all(a.chunk_ws, nchunks, a, a.offsets, red_i, red_f);
+}
+
+__global__ __launch_bounds__(DW * 64) void dispatch_scatter_kernel(
+    DispatchArgs a, int nchunks) {
+  __shared__ int base[DW][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = blockIdx.x * DW + wave;
+  const long long tk = (long long)a.T * a.k;
+  if (c >= nchunks) return;   // no workgroup barrier below
+  for (int e = lane; e < a.E; e += 64) base[wave][e] = a.chunk_ws[(size_t)c * a.E + e];
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_s_waitcnt(0);
+  scatter_chunk(a.idx, tk, c, base[wave], a.offsets, a.E, a.perm, a.slot_of,
+                lane);
+}
+
+// Everything in one workgroup when there are at most DW chunks.
+__global__ __launch_bounds__(256) void dispatch_small_kernel(DispatchArgs a,
+                                                             int nchunks) {
+  __shared__ int chunk[DW * 256];
+  __shared__ int red_i[256];
+  __shared__ float red_f[256];
+  __shared__ int32_t offs[257];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long long tk = (long long)a.T * a.k;
+  for (int i = threadIdx.x; i < DW * 256; i += 256) chunk[i] = 0;
+  __syncthreads();
+  if (wave < nchunks) count_chunk(a.idx, tk, a.E, wave, chunk + wave * a.E, lane);
+  __syncthreads();
+  scan_all(chunk, nchunks, a, offs, red_i, red_f);
+  __syncthreads();
+  for (int e = threadIdx.x; e <= a.E; e += 256) a.offsets[e] = offs[e];
+  if (wave < nchunks)
+    scatter_chunk(a.idx, tk, wave, chunk + wave * a.E, offs, a.E, a.perm,
+                  a.slot_of, lane);
+}
+
+__global__ void fill_zero32_kernel(uint32_t* p, long long n) {
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
+  const long long tk = (long long)a.T * a.k;
+  const int nchunks = dispatch_chunks(tk);
+  if (nchunks <= DW) {
+    dispatch_small_kernel<<<1, 256, 0, s>>>(a, nchunks);
+    return hipGetLastError();
+  }
+  const int blocks = (nchunks + DW - 1) / DW;
+  dispatch_count_kernel<<<blocks, DW * 64, 0, s>>>(a.idx, tk, nchunks, a.E,
+                                                   a.chunk_ws);
+  dispatch_scan_kernel<<<1, 256, 0, s>>>(a, nchunks);
+  dispatch_scatter_kernel<<<blocks, DW * 64, 0, s>>>(a, nchunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero32(void* p, long long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int bs = 256;
+  fill_zero32_kernel<<<(unsigned)((n + bs - 1) / bs), bs, 0, s>>>((uint32_t*)p, n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,481 @@
+// Expert FFNs over each expert's kept rows: the dense contraction of the
+// layer, run as grouped GEMMs on bf16 MFMA with float32 accumulation.
+//
+// Every expert runs once over the batch of tokens grouped to it
+// (hassanahmed.net "Mixture of Experts explained": a real kernel groups
+// tokens by expert and runs each expert once; letsbuildsolutions.com "How
+// Mixture of Experts Works", Gating Mechanism: grouped GEMM instead of the
+// per-expert loop).  Experts are GELU MLPs with biases (randomcommits.com
+// "Mixture-of-Experts routing", How a sparse MoE layer works) or SwiGLU
+// w_down(silu(w_gate x) * w_up x) without biases (getnybble.com "Mixture of
+// Experts (MoE)", Implementing a complete MoE layer), plus an optional
+// always-on shared expert (same page, DeepSeek-V3).
+//
+// Groups: g < E is routed expert g, rows [offsets[g], offsets[g+1]) of the
+// output, A-row r taken from x[perm[r] / k] (gather on load, no permuted
+// copy of x); g == E is the shared expert, rows T*k + t for t < T.
+//
+//   up    H[r, n]  = act(A[r,:] . W1[g, n, :]) (SwiGLU: silu(gate) * up)
+//   down  Y[r, n]  = H[r,:] . W2[g, n, :] (+ b2)
+//
+// Two bf16 schedules, picked on the host from the shapes only:
+//   stream  few rows per expert (decode): each wave owns 16 output columns
+//           and streams those weight rows once from HBM straight into MFMA
+//           B registers (16x16x32), with a 4-deep register prefetch ring;
+//           the handful of token rows ride along as the A operand.
+//   tiled   many rows per expert (prefill): 128x128 workgroup tiles, BK=64,
+//           A and B staged through XOR-swizzled LDS with double buffering,
+//           32x32x16 MFMAs, the activation fused into the epilogue, and the
+//           output tile staged through LDS for 16-byte row stores.
+// float32 problems use a plain float32 kernel (same grouping).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+enum { UP_SWIGLU = 0, UP_GELU = 1, DOWN = 2 };
+
+struct Group {
+  int rows;     // rows of this group
+  int out0;     // first output row
+  bool shared;
+};
+
+__device__ __forceinline__ Group group_of(int g, const int32_t* offsets, int E,
+                                          int T, int k) {
+  Group r;
+  if (g < E) {
+    r.out0 = offsets[g];
+    r.rows = offsets[g + 1] - r.out0;
+    r.shared = false;
+  } else {
+    r.out0 = T * k;
+    r.rows = T;
+    r.shared = true;
+  }
+  return r;
+}
+
+// Row of the A operand for output row index i (0-based inside the group).
+template <int MODE, typename ET>
+__device__ __forceinline__ const ET* a_row(const FfnArgs& a, const Group& gr,
+                                           int i, int K) {
+  if (MODE == DOWN) return (const ET*)a.h + (size_t)(gr.out0 + i) * K;
+  const int tok = gr.shared ? i : a.perm[gr.out0 + i] / a.k;
+  return (const ET*)a.x + (size_t)tok * K;
+}
+
+template <int MODE>
+__device__ __forceinline__ void group_weights(const FfnArgs& a, int g,
+                                              bool shared, int N, int K,
+                                              const void*& w0,
+                                              const void*& w1,
+                                              const void*& bias) {
+  const size_t esz = a.dtype == 1 ? 2 : 4;
+  const size_t mat = (size_t)N * K * esz;
+  if (MODE == DOWN) {
+    w0 = shared ? a.sw2 : (const char*)a.w2 + (size_t)g * mat;
+    w1 = nullptr;
+    const void* b = shared ? a.sb2 : (a.b2 ? (const char*)a.b2 + (size_t)g * N * esz : nullptr);
+    bias = b;
+  } else if (MODE == UP_SWIGLU) {
+    w0 = shared ? a.sw1 : (const char*)a.w1 + (size_t)g * mat;
+    w1 = shared ? a.sw_up : (const char*)a.w_up + (size_t)g * mat;
+    bias = nullptr;
+  } else {
+    w0 = shared ? a.sw1 : (const char*)a.w1 + (size_t)g * mat;
+    w1 = nullptr;
+    bias = shared ? a.sb1 : (const char*)a.b1 + (size_t)g * N * esz;
+  }
+}
+
+// ===========================================================================
+// stream schedule (bf16)
+// ===========================================================================
+constexpr int ST_WAVES = 4;
+constexpr int ST_COLS = 16;          // output columns per wave
+constexpr int ST_KSTEP = 64;         // K per step (two 16x16x32 MFMAs)
+constexpr int ST_PF = 4;             // prefetch ring depth (steps)
+
+template <int NMAT, int RT>
+struct StreamBuf {
+  u32x4 b[NMAT][2];   // 16 bf16 of one weight row per matrix
+  u32x4 a[RT][2];     // 16 bf16 of one token row per row tile
+};
+
+template <int MODE, int RT>
+__global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
+  constexpr int NMAT = MODE == UP_SWIGLU ? 2 : 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = blockIdx.y;
+  const Group gr = group_of(g, a.offsets, a.E, a.T, a.k);
+  if (gr.rows <= 0) return;
+  const int N = MODE == DOWN ? a.d : a.d_ff;
+  const int K = MODE == DOWN ? a.d_ff : a.d;
+  const int n0 = (blockIdx.x * ST_WAVES + wave) * ST_COLS;
+  if (n0 >= N) return;
+  const void *w0v, *w1v, *biasv;
+  group_weights<MODE>(a, g, gr.shared, N, K, w0v, w1v, biasv);
+  const bf16* wm[2] = {(const bf16*)w0v, (const bf16*)w1v};
+
+  const int col = lane & 15;   // B: weight row n0+col; A: token row
+  const int kq = lane >> 4;    // 16-wide k slice of the 64-wide step
+  const bf16* brow[NMAT];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m) brow[m] = wm[m] + (size_t)(n0 + col) * K + kq * 16;
+  const int nsteps = K / ST_KSTEP;
+
+  for (int rg = 0; rg < gr.rows; rg += RT * 16) {
+    const int ntile = min(RT, (gr.rows - rg + 15) >> 4);
+    const bf16* arow[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const int i = min(rg + t * 16 + col, gr.rows - 1);
+      arow[t] = a_row<MODE, bf16>(a, gr, i, K) + kq * 16;
+    }
+    f32x4 acc[NMAT][RT];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int t = 0; t < RT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    StreamBuf<NMAT, RT> buf[ST_PF];
+    auto load = [&](StreamBuf<NMAT, RT>& b, int s) {
+      const int k0 = s * ST_KSTEP;
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        b.b[m][0] = ldg16(brow[m] + k0);
+        b.b[m][1] = ldg16(brow[m] + k0 + 8);
+      }
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        if (t < ntile) {
+          b.a[t][0] = ldg16(arow[t] + k0);
+          b.a[t][1] = ldg16(arow[t] + k0 + 8);
+        }
+      }
+    };
+    auto compute = [&](const StreamBuf<NMAT, RT>& b) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        if (t < ntile) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            V16 av;
+            av.u = b.a[t][h];
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) {
+              V16 bv;
+              bv.u = b.b[m][h];
+              acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av.h, bv.h, acc[m][t], 0, 0, 0);
+            }
+          }
+        }
+      }
+    };
+#pragma unroll
+    for (int p = 0; p < ST_PF; ++p)
+      if (p < nsteps) load(buf[p], p);
+    for (int s0 = 0; s0 < nsteps; s0 += ST_PF) {
+#pragma unroll
+      for (int p = 0; p < ST_PF; ++p) {
+        const int s = s0 + p;
+        if (s < nsteps) {
+          compute(buf[p]);
+          if (s + ST_PF < nsteps) load(buf[p], s + ST_PF);
+        }
+      }
+    }
+
+    // epilogue: lane holds column n0+col, rows rg + 16t + 4*kq + r
+    const int n = n0 + col;
+    float bias = 0.f;
+    if (MODE != UP_SWIGLU && biasv) bias = (float)((const bf16*)biasv)[n];
+    bf16* outp = (bf16*)(MODE == DOWN ? a.y : a.h);
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      if (t < ntile) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = rg + t * 16 + kq * 4 + r;
+          if (i < gr.rows) {
+            float v;
+            if (MODE == UP_SWIGLU) v = silu(acc[0][t][r]) * acc[NMAT - 1][t][r];
+            else if (MODE == UP_GELU) v = gelu_erf(acc[0][t][r] + bias);
+            else v = acc[0][t][r] + bias;
+            outp[(size_t)(gr.out0 + i) * N + n] = (bf16)v;
+          }
+        }
+      }
+    }
+  }
+}
+
+// ===========================================================================
+// tiled schedule (bf16)
+// ===========================================================================
+constexpr int TL_BM = 128;
+constexpr int TL_BN = 128;   // B rows per tile (SwiGLU: 64 gate + 64 up)
+constexpr int TL_BK = 64;
+constexpr int TL_THREADS = 256;
+
+// Swizzled LDS offset (in bf16 elements) of 16-byte chunk c of row r in a
+// [rows][64] bf16 tile: chunk position c ^ (r & 7).
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * TL_BK + ((c ^ (r & 7)) << 3);
+}
+
+// Maps a linear row-tile id to (group, first row); returns false when the
+// id is past the last tile.  Executed by the whole workgroup.
+__device__ bool find_tile(const FfnArgs& a, int G, int BM, int tile, int* s_info) {
+  if (threadIdx.x == 0) {
+    int acc = 0, g = 0, r0 = -1;
+    for (; g < G; ++g) {
+      const int rows = g < a.E ? a.offsets[g + 1] - a.offsets[g] : a.T;
+      const int nt = (rows + BM - 1) / BM;
+      if (tile < acc + nt) {
+        r0 = (tile - acc) * BM;
+        break;
+      }
+      acc += nt;
+    }
+    s_info[0] = g;
+    s_info[1] = r0;
+  }
+  __syncthreads();
+  return s_info[1] >= 0;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(TL_THREADS) void ffn_tiled_kernel(FfnArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 lds[2][2][TL_BM * TL_BK];  // [buf][A/B]
+  __shared__ int s_info[2];
+  const int G = a.E + a.n_shared;
+  if (!find_tile(a, G, TL_BM, blockIdx.x, s_info)) return;
+  const int g = s_info[0];
+  const int r0 = s_info[1];
+  const Group gr = group_of(g, a.offsets, a.E, a.T, a.k);
+  const int N = MODE == DOWN ? a.d : a.d_ff;
+  const int K = MODE == DOWN ? a.d_ff : a.d;
+  // output columns covered by this workgroup
+  const int ncols = MODE == UP_SWIGLU ? TL_BN / 2 : TL_BN;
+  const int nbase = blockIdx.y * ncols;
+  const void *w0v, *w1v, *biasv;
+  group_weights<MODE>(a, g, gr.shared, N, K, w0v, w1v, biasv);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // global->LDS: thread owns chunk lc of rows lr + 32*i, i < 4
+  const int lc = tid & 7, lr = tid >> 3;
+  const bf16* ga[4];
+  const bf16* gb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = lr + 32 * i;
+    const int ai = min(r0 + row, gr.rows - 1);
+    ga[i] = a_row<MODE, bf16>(a, gr, ai, K) + lc * 8;
+    int wrow;
+    const bf16* wbase;
+    if (MODE == UP_SWIGLU) {
+      const int half = (row >> 5) & 1;          // 0 gate, 1 up
+      wrow = nbase + (row >> 6) * 32 + (row & 31);
+      wbase = (const bf16*)(half ? w1v : w0v);
+    } else {
+      wrow = nbase + row;
+      wbase = (const bf16*)w0v;
+    }
+    wrow = min(wrow, N - 1);
+    gb[i] = wbase + (size_t)wrow * K + lc * 8;
+  }
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  u32x4 ra[4], rb[4];
+  auto gload = [&](int kt) {
+    const int k0 = kt * TL_BK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra[i] = ldg16(ga[i] + k0);
+      rb[i] = ldg16(gb[i] + k0);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = lr + 32 * i;
+      *reinterpret_cast<u32x4*>(&lds[buf][0][swz(row, lc)]) = ra[i];
+      *reinterpret_cast<u32x4*>(&lds[buf][1][swz(row, lc)]) = rb[i];
+    }
+  };
+
+  const int nk = K / TL_BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  const int arow_base = wm * 64 + (lane & 31);
+  const int brow_base = wn * 64 + (lane & 31);
+  const int q = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+#pragma unroll
+    for (int ss = 0; ss < 4; ++ss) {
+      const int c = ss * 2 + q;
+      V16 av[2], bv[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        av[i].u = *reinterpret_cast<const u32x4*>(&lds[buf][0][swz(arow_base + 32 * i, c)]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bv[j].u = *reinterpret_cast<const u32x4*>(&lds[buf][1][swz(brow_base + 32 * j, c)]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i].h, bv[j].h, acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: activation, stage the bf16 tile in LDS, store rows ----
+  // 32x32 accumulator layout: lane holds column lane&31; item v is row
+  // (v&3) + 4*(lane>>5) + 8*(v>>2).
+  bf16* otile = &lds[0][0][0];              // [TL_BM][ncols], reuses LDS
+  const int ocol = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = wm * 64 + 32 * i + (v & 3) + 4 * q + 8 * (v >> 2);
+      if (MODE == UP_SWIGLU) {
+        const int c = wn * 32 + ocol;
+        const float h = silu(acc[i][0][v]) * acc[i][1][v];
+        otile[row * 64 + c] = (bf16)h;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int c = wn * 64 + 32 * j + ocol;
+          const int n = min(nbase + c, N - 1);
+          float bias = biasv ? (float)((const bf16*)biasv)[n] : 0.f;
+          float v2 = acc[i][j][v] + bias;
+          if (MODE == UP_GELU) v2 = gelu_erf(v2);
+          otile[row * 128 + c] = (bf16)v2;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  bf16* outp = (bf16*)(MODE == DOWN ? a.y : a.h);
+  const int chunks_per_row = ncols / 8;
+  for (int idx = tid; idx < TL_BM * chunks_per_row; idx += TL_THREADS) {
+    const int row = idx / chunks_per_row, ch = idx % chunks_per_row;
+    const int i = r0 + row;
+    const int n = nbase + ch * 8;
+    if (i < gr.rows && n < N) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&otile[row * ncols + ch * 8]);
+      stg16(outp + (size_t)(gr.out0 + i) * N + n, v);
+    }
+  }
+}
+
+// ===========================================================================
+// float32 schedule
+// ===========================================================================
+constexpr int F32_BM = 16;
+constexpr int F32_BN = 64;
+
+template <int MODE>
+__global__ __launch_bounds__(256) void ffn_f32_kernel(FfnArgs a) {
+  __shared__ int s_info[2];
+  const int G = a.E + a.n_shared;
+  if (!find_tile(a, G, F32_BM, blockIdx.x, s_info)) return;
+  const int g = s_info[0], r0 = s_info[1];
+  const Group gr = group_of(g, a.offsets, a.E, a.T, a.k);
+  const int N = MODE == DOWN ? a.d : a.d_ff;
+  const int K = MODE == DOWN ? a.d_ff : a.d;
+  const void *w0v, *w1v, *biasv;
+  group_weights<MODE>(a, g, gr.shared, N, K, w0v, w1v, biasv);
+  const float* w0 = (const float*)w0v;
+  const float* w1 = (const float*)w1v;
+  const float* bias = (const float*)biasv;
+  float* outp = (float*)(MODE == DOWN ? a.y : a.h);
+  const int c = blockIdx.y * F32_BN + (threadIdx.x & 63);
+  for (int rr = threadIdx.x >> 6; rr < F32_BM; rr += 4) {
+    const int i = r0 + rr;
+    if (i >= gr.rows || c >= N) continue;
+    const float* ar = a_row<MODE, float>(a, gr, i, K);
+    float s0 = 0.f, s1 = 0.f;
+    for (int kk = 0; kk < K; ++kk) {
+      s0 = fmaf(ar[kk], w0[(size_t)c * K + kk], s0);
+      if (MODE == UP_SWIGLU) s1 = fmaf(ar[kk], w1[(size_t)c * K + kk], s1);
+    }
+    float v;
+    if (MODE == UP_SWIGLU) v = silu(s0) * s1;
+    else if (MODE == UP_GELU) v = gelu_erf(s0 + bias[c]);
+    else v = s0 + (bias ? bias[c] : 0.f);
+    outp[(size_t)(gr.out0 + i) * N + c] = v;
+  }
+}
+
+template <int MODE>
+hipError_t launch_mode(const FfnArgs& a, hipStream_t s, int sched, int rt,
+                       int max_tiles) {
+  const int N = MODE == DOWN ? a.d : a.d_ff;
+  const int G = a.E + a.n_shared;
+  if (sched == 0) {
+    dim3 grid((N + ST_WAVES * ST_COLS - 1) / (ST_WAVES * ST_COLS), G);
+    if (rt == 1) ffn_stream_kernel<MODE, 1><<<grid, ST_WAVES * 64, 0, s>>>(a);
+    else if (rt == 2) ffn_stream_kernel<MODE, 2><<<grid, ST_WAVES * 64, 0, s>>>(a);
+    else ffn_stream_kernel<MODE, 4><<<grid, ST_WAVES * 64, 0, s>>>(a);
+  } else if (sched == 1) {
+    const int ncols = MODE == UP_SWIGLU ? TL_BN / 2 : TL_BN;
+    dim3 grid(max_tiles, (N + ncols - 1) / ncols);
+    ffn_tiled_kernel<MODE><<<grid, TL_THREADS, 0, s>>>(a);
+  } else {
+    dim3 grid(max_tiles, (N + F32_BN - 1) / F32_BN);
+    ffn_f32_kernel<MODE><<<grid, 256, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Schedule choice from shapes only (no device readback):
+//   f32 -> float32 kernel; bf16 with at most 64 assignments per expert on
+//   average -> stream; otherwise tiled.
+int ffn_schedule(int dtype, int T, int k, int E) {
+  if (dtype != 1) return 2;
+  return ((long long)T * k <= 64LL * E) ? 0 : 1;
+}
+
+hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  const int sched = ffn_schedule(a.dtype, a.T, a.k, a.E);
+  const long long tk = (long long)a.T * a.k;
+  int rt = 4;
+  if (sched == 0) {
+    const int maxrows = a.T;   // a token picks an expert at most once
+    rt = maxrows <= 16 ? 1 : (maxrows <= 32 ? 2 : 4);
+  }
+  const int bm = sched == 1 ? TL_BM : F32_BM;
+  const int max_tiles = (int)((tk + bm - 1) / bm) + a.E +
+                        (a.n_shared ? (a.T + bm - 1) / bm : 0);
+  hipError_t e;
+  if (a.act == 1) e = launch_mode<UP_SWIGLU>(a, s, sched, rt, max_tiles);
+  else e = launch_mode<UP_GELU>(a, s, sched, rt, max_tiles);
+  if (e != hipSuccess) return e;
+  return launch_mode<DOWN>(a, s, sched, rt, max_tiles);
+}
+
+}  // namespace moe

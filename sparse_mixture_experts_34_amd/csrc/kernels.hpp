@@ -1,0 +1,92 @@
+// Internal launchers of the MoE kernels (host side).  The C ABI in abi.hip
+// validates arguments and sizes the workspace; these only enqueue.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Tokens handled by one workgroup of the route-select kernel; also the
+// granularity of the per-block probability partial sums.
+constexpr int ROUTE_TOKENS_PER_BLOCK = 64;
+// Assignments (token, slot) handled by one wave in the dispatch kernels.
+constexpr int DISPATCH_CHUNK = 256;
+// Chunks (one per wave) per dispatch workgroup.
+constexpr int DISPATCH_WAVES = 4;
+
+inline int route_blocks(int T) {
+  return (T + ROUTE_TOKENS_PER_BLOCK - 1) / ROUTE_TOKENS_PER_BLOCK;
+}
+inline int dispatch_chunks(long long tk) {
+  return (int)((tk + DISPATCH_CHUNK - 1) / DISPATCH_CHUNK);
+}
+
+// ---- route -----------------------------------------------------------------
+// K slices of the router GEMM (partial logits [ksplit, T, E] in workspace).
+int router_ksplit(int T, int d, int E, int dtype);
+// part[ks, t, e] = sum over slice ks of x[t,:] . Wr[e,:]  (float32).
+hipError_t launch_router_logits_partial(int dtype, const void* x,
+                                        const float* wr, float* part, int T,
+                                        int d, int E, int ksplit,
+                                        hipStream_t s);
+// Sum the slices (+ router bias), softmax, top-k, gates, and per-block
+// probability partial sums [route_blocks(T), E].  logits may be null.
+hipError_t launch_route_select_from(const float* part, int ksplit,
+                                    const float* router_bias,
+                                    const float* select_bias, float* logits,
+                                    int32_t* idx, float* gate,
+                                    float* partials, int T, int E, int k,
+                                    hipStream_t s);
+// prob_mean[e] = sum_b partials[b,e] / T (fixed order).
+hipError_t launch_prob_mean(const float* partials, float* prob_mean, int nblk,
+                            int T, int E, hipStream_t s);
+
+// ---- dispatch --------------------------------------------------------------
+// counts/offsets/perm/slot_of/n_dropped and optionally prob_mean + aux.
+// `partials` (route partial sums, nblk rows) may be given instead of a
+// finished prob_mean; then prob_mean_out receives the mean.
+struct DispatchArgs {
+  const int32_t* idx;
+  const float* prob_mean_in;   // or nullptr
+  const float* partials;       // or nullptr
+  int n_partials;
+  float* prob_mean_out;        // written when partials != nullptr
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* slot_of;
+  int32_t* n_dropped;
+  float* aux;                  // or nullptr
+  int32_t* chunk_ws;           // [nchunks, E]
+  int T, E, k, capacity;
+  float aux_coef;
+};
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+
+// ---- expert FFN ------------------------------------------------------------
+struct FfnArgs {
+  int dtype, act;
+  int T, d, E, k, d_ff, n_shared;
+  const void* x;
+  const int32_t* perm;
+  const int32_t* offsets;
+  const void *w1, *w_up, *w2, *b1, *b2;
+  const void *sw1, *sw_up, *sw2, *sb1, *sb2;
+  void* h;   // [T*k + n_shared*T, d_ff] workspace
+  void* y;   // [T*k + n_shared*T, d]
+};
+hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s);
+
+// ---- combine ---------------------------------------------------------------
+hipError_t launch_combine(int dtype, const void* x, const void* y,
+                          const int32_t* slot_of, const float* gate,
+                          void* out, int T, int d, int k, int n_shared,
+                          hipStream_t s);
+
+// ---- misc ------------------------------------------------------------------
+// Writes zeros (int32 / float32) - used for the T = 0 outputs.
+hipError_t launch_fill_zero32(void* p, long long n, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,366 @@
+// Route: router linear, softmax, top-k, renormalised gates.
+//
+// The router is one linear layer from the hidden state to E scores,
+// followed by a softmax over all E experts and a top-k choice whose chosen
+// probabilities are renormalised to sum to one (randomcommits.com
+// "Mixture-of-Experts routing", How a sparse MoE layer works;
+// letsbuildsolutions.com "How Mixture of Experts Works", Gating Mechanism;
+// getnybble.com "Mixture of Experts (MoE)", The router).  The router runs
+// in float32 (letsbuildsolutions.com, Dense vs Sparse).
+//
+// Kernel 1 (router_logits): logits = x . Wr^T on bf16 MFMA.  Wr is float32;
+// each weight is split exactly into hi + mid + lo bf16 parts, so with bf16
+// x every product is exact in float32 and the three MFMAs accumulate a
+// float32-accurate dot product at matrix-core speed.  A float32 x is split
+// the same way (six part products).  Large T: 64 tokens x 64 experts per
+// workgroup; small T: the K dimension is split across workgroups and the
+// partial sums are added, in a fixed order, by kernel 2.
+//
+// Kernel 2 (route_select): one wave per token.  Sum the K-split partials,
+// add the router bias, softmax (max-subtracted), choose k experts by k
+// rounds of wave argmax on (key, index) with equal keys going to the lower
+// index, gates = exp-values of the chosen experts over their sum.  Each
+// workgroup also writes the sum over its tokens of the probabilities
+// (fixed order) for the aux loss.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int RL_THREADS = 256;
+constexpr int RL_EXP_TILE = 64;   // experts per workgroup (4 MFMA N-tiles)
+constexpr int RL_KSTEP = 64;      // K per step (two 16x16x32 MFMAs)
+
+// Load 16 consecutive x values as float.
+template <typename XT>
+__device__ __forceinline__ void load16(const XT* p, float* out);
+
+template <>
+__device__ __forceinline__ void load16<bf16>(const bf16* p, float* out) {
+  V16 a, b;
+  a.u = ldg16(p);
+  b.u = ldg16(p + 8);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    out[i] = (float)a.h[i];
+    out[8 + i] = (float)b.h[i];
+  }
+}
+template <>
+__device__ __forceinline__ void load16<float>(const float* p, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    V16 v;
+    v.u = ldg16(p + 4 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[4 * i + j] = v.f[j];
+  }
+}
+
+// XPARTS: 1 for bf16 x (exact), 3 for float32 x.
+// TT: token tiles of 16 per wave.
+template <typename XT, int XPARTS, int TT>
+__global__ __launch_bounds__(RL_THREADS) void router_logits_kernel(
+    const XT* __restrict__ x, const float* __restrict__ wr,
+    float* __restrict__ part, int T, int d, int E, int ksplit) {
+  __shared__ float red[3][TT * 16 * RL_EXP_TILE];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int row = lane & 15;   // token row (A) / expert row (B) in a tile
+  const int kq = lane >> 4;    // which 16-wide k slice of the 64-wide step
+  const int t0 = blockIdx.x * (TT * 16);
+  const int e0 = blockIdx.y * RL_EXP_TILE;
+  const int ks = blockIdx.z;
+  const int klen = d / ksplit;             // multiple of 64 (host checks)
+  const int kbeg = ks * klen;
+  const int nsteps = klen / RL_KSTEP;
+  const int ntile = min(4, (E - e0 + 15) >> 4);
+  const int ttok = min(TT, (T - t0 + 15) >> 4);
+
+  const XT* xr[TT];
+#pragma unroll
+  for (int i = 0; i < TT; ++i) {
+    int t = min(t0 + 16 * i + row, T - 1);
+    xr[i] = x + (size_t)t * d + kbeg + kq * 16;
+  }
+  const float* wrow[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int e = min(e0 + 16 * j + row, E - 1);
+    wrow[j] = wr + (size_t)e * d + kbeg + kq * 16;
+  }
+
+  f32x4 acc[TT][4];
+#pragma unroll
+  for (int i = 0; i < TT; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int s = wave; s < nsteps; s += 4) {
+    const int k0 = s * RL_KSTEP;
+    // A operands: x rows, split into XPARTS bf16 parts, two 8-wide halves
+    bf16x8 a[TT][XPARTS][2];
+#pragma unroll
+    for (int i = 0; i < TT; ++i) {
+      float xv[16];
+      load16<XT>(xr[i] + k0, xv);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          bf16 pr[3];
+          split3(xv[8 * h + q], pr[0], pr[1], pr[2]);
+#pragma unroll
+          for (int p = 0; p < XPARTS; ++p) a[i][p][h][q] = pr[p];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j < ntile) {
+        float wv[16];
+        load16<float>(wrow[j] + k0, wv);
+        bf16x8 b[3][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            bf16 hi, mid, lo;
+            split3(wv[8 * h + q], hi, mid, lo);
+            b[0][h][q] = hi;
+            b[1][h][q] = mid;
+            b[2][h][q] = lo;
+          }
+#pragma unroll
+        for (int i = 0; i < TT; ++i) {
+          if (i < ttok) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              f32x4 c = acc[i][j];
+              // parts whose ranks sum to <= 2 (hi=0, mid=1, lo=2)
+#pragma unroll
+              for (int pa = 0; pa < XPARTS; ++pa)
+#pragma unroll
+                for (int pb = 0; pb < 3; ++pb)
+                  if (pa + pb <= 2)
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        a[i][pa][h], b[pb][h], c, 0, 0, 0);
+              acc[i][j] = c;
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // Reduce the four waves' partial sums in the fixed order 0,1,2,3.
+  // Accumulator layout: lane holds column (expert) lane&15 and rows
+  // (tokens) 4*(lane>>4) + r.
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < TT; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int m = 16 * i + 4 * kq + r, n = 16 * j + row;
+          red[wave - 1][m * RL_EXP_TILE + n] = acc[i][j][r];
+        }
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < TT; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          int m = 16 * i + 4 * kq + r, n = 16 * j + row;
+          float v = acc[i][j][r];
+          v += red[0][m * RL_EXP_TILE + n];
+          v += red[1][m * RL_EXP_TILE + n];
+          v += red[2][m * RL_EXP_TILE + n];
+          int t = t0 + m, e = e0 + n;
+          if (t < T && e < E) part[((size_t)ks * T + t) * E + e] = v;
+        }
+  }
+}
+
+constexpr int RS_WAVES = 4;
+constexpr int RS_TOK_PER_WAVE = ROUTE_TOKENS_PER_BLOCK / RS_WAVES;
+constexpr int RS_MAXC = 4;   // experts per lane: E <= 256
+
+__global__ __launch_bounds__(RS_WAVES * 64) void route_select_kernel(
+    const float* __restrict__ part, int ksplit,
+    const float* __restrict__ router_bias,
+    const float* __restrict__ select_bias, float* __restrict__ logits_out,
+    int32_t* __restrict__ idx_out, float* __restrict__ gate_out,
+    float* __restrict__ partials, int T, int E, int k) {
+  __shared__ float psum_s[RS_WAVES][256];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  float psum[RS_MAXC];
+#pragma unroll
+  for (int c = 0; c < RS_MAXC; ++c) psum[c] = 0.f;
+
+  const int tbeg = blockIdx.x * ROUTE_TOKENS_PER_BLOCK + wave * RS_TOK_PER_WAVE;
+  for (int i = 0; i < RS_TOK_PER_WAVE; ++i) {
+    const int t = tbeg + i;
+    if (t >= T) break;   // wave-uniform
+    float l[RS_MAXC], key[RS_MAXC];
+#pragma unroll
+    for (int c = 0; c < RS_MAXC; ++c) {
+      const int e = lane + 64 * c;
+      l[c] = -INFINITY;
+      key[c] = -INFINITY;
+      if (e < E) {
+        float v = 0.f;
+        for (int s = 0; s < ksplit; ++s) v += part[((size_t)s * T + t) * E + e];
+        if (router_bias) v += router_bias[e];
+        l[c] = v;
+        key[c] = select_bias ? v + select_bias[e] : v;
+        if (logits_out) logits_out[(size_t)t * E + e] = v;
+      }
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < RS_MAXC; ++c) m = fmaxf(m, l[c]);
+    m = wave_max(m);
+    float ex[RS_MAXC], se = 0.f;
+#pragma unroll
+    for (int c = 0; c < RS_MAXC; ++c) {
+      const int e = lane + 64 * c;
+      ex[c] = (e < E) ? __expf(l[c] - m) : 0.f;
+      se += ex[c];
+    }
+    se = wave_sum(se);
+    const float inv = 1.0f / se;
+#pragma unroll
+    for (int c = 0; c < RS_MAXC; ++c) psum[c] += ex[c] * inv;
+
+    // k rounds of wave argmax on (key desc, index asc); lane j keeps the
+    // winner of round j (slot j) and its logit.
+    bool taken[RS_MAXC];
+#pragma unroll
+    for (int c = 0; c < RS_MAXC; ++c) taken[c] = (lane + 64 * c) >= E;
+    int my_idx = 0;
+    float my_l = -INFINITY;
+    for (int j = 0; j < k; ++j) {
+      float bk = -INFINITY, bl = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int c = 0; c < RS_MAXC; ++c) {
+        // indices rise with c: strict > keeps the lower index on ties
+        if (!taken[c] && (bi == 0x7fffffff || key[c] > bk)) {
+          bk = key[c];
+          bi = lane + 64 * c;
+          bl = l[c];
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        float ok = __shfl_xor(bk, o, 64);
+        int oi = __shfl_xor(bi, o, 64);
+        float ol = __shfl_xor(bl, o, 64);
+        bool better = (oi != 0x7fffffff) &&
+                      (bi == 0x7fffffff || ok > bk || (ok == bk && oi < bi));
+        if (better) {
+          bk = ok;
+          bi = oi;
+          bl = ol;
+        }
+      }
+      // every lane now holds the same winner
+#pragma unroll
+      for (int c = 0; c < RS_MAXC; ++c)
+        if (lane + 64 * c == bi) taken[c] = true;
+      if (lane == j) {
+        my_idx = bi;
+        my_l = bl;
+      }
+    }
+    // gates: chosen probabilities over their sum, i.e. a softmax over the
+    // chosen logits (the shared normaliser cancels)
+    const float mc = wave_max(lane < k ? my_l : -INFINITY);
+    const float ej = lane < k ? __expf(my_l - mc) : 0.f;
+    const float sj = wave_sum(ej);
+    if (lane < k) {
+      idx_out[(size_t)t * k + lane] = my_idx;
+      gate_out[(size_t)t * k + lane] = ej / sj;
+    }
+  }
+  // per-block probability partial sums, waves added in order 0..3
+#pragma unroll
+  for (int c = 0; c < RS_MAXC; ++c) {
+    const int e = lane + 64 * c;
+    if (e < 256) psum_s[wave][e] = psum[c];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    float v = psum_s[0][e];
+    v += psum_s[1][e];
+    v += psum_s[2][e];
+    v += psum_s[3][e];
+    partials[(size_t)blockIdx.x * E + e] = v;
+  }
+}
+
+__global__ void prob_mean_kernel(const float* __restrict__ partials,
+                                 float* __restrict__ pm, int nblk, int T,
+                                 int E) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    float v = 0.f;
+    for (int b = 0; b < nblk; ++b) v += partials[(size_t)b * E + e];
+    pm[e] = T > 0 ? v / (float)T : 0.f;
+  }
+}
+
+}  // namespace
+
+// Number of K slices for the router GEMM: enough workgroups to cover the
+// chip when T is small, each slice a multiple of 256 (4 waves x 64).
+int router_ksplit(int T, int d, int E, int dtype) {
+  const int tt = dtype == 1 ? 64 : 16;
+  const long long blocks = (long long)((T + tt - 1) / tt) *
+                           ((E + RL_EXP_TILE - 1) / RL_EXP_TILE);
+  int ks = 1;
+  while (blocks * ks * 2 <= 256 && d % (ks * 2 * 256) == 0) ks *= 2;
+  return ks;
+}
+
+hipError_t launch_router_logits_partial(int dtype, const void* x,
+                                        const float* wr, float* part, int T,
+                                        int d, int E, int ksplit,
+                                        hipStream_t s) {
+  if (dtype == 1) {
+    dim3 grid((T + 63) / 64, (E + RL_EXP_TILE - 1) / RL_EXP_TILE, ksplit);
+    router_logits_kernel<bf16, 1, 4><<<grid, RL_THREADS, 0, s>>>(
+        (const bf16*)x, wr, part, T, d, E, ksplit);
+  } else {
+    dim3 grid((T + 15) / 16, (E + RL_EXP_TILE - 1) / RL_EXP_TILE, ksplit);
+    router_logits_kernel<float, 3, 1><<<grid, RL_THREADS, 0, s>>>(
+        (const float*)x, wr, part, T, d, E, ksplit);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_route_select_from(const float* part, int ksplit,
+                                    const float* router_bias,
+                                    const float* select_bias, float* logits,
+                                    int32_t* idx, float* gate,
+                                    float* partials, int T, int E, int k,
+                                    hipStream_t s) {
+  route_select_kernel<<<route_blocks(T), RS_WAVES * 64, 0, s>>>(
+      part, ksplit, router_bias, select_bias, logits, idx, gate, partials, T,
+      E, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_prob_mean(const float* partials, float* prob_mean, int nblk,
+                            int T, int E, hipStream_t s) {
+  prob_mean_kernel<<<1, 256, 0, s>>>(partials, prob_mean, nblk, T, E);
+  return hipGetLastError();
+}
+
+}  // namespace moe

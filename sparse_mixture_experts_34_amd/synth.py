@@ -153,7 +153,7 @@ def make_inputs(wl: Workload, device="cpu", seed: int | None = None,
     are drawn as float32 normals and rounded (RNE) to the workload dtype;
     the router weight and the biases on the router stay float32.
 
-    ``margin_fn(x64, w_router64, router_bias64, select_bias64, k)`` may
+    ``margin_fn(x64, w_router64, k, router_bias64, select_bias64)`` may
     return a per-token top-k margin; tokens at or below ``min_margin`` get
     their x row redrawn from a per-(token, attempt) generator.  The number
     of redraws is returned under ``"redraws"``.
@@ -211,7 +211,7 @@ def _redraw_close_tokens(inp, wl, seed, dev, margin_fn, min_margin,
     rb = _host64(inp["router_bias"])
     sb = _host64(inp["select_bias"])
     x = inp["x"]
-    bad = np.nonzero(margin_fn(_host64(x), wr, rb, sb, wl.top_k)
+    bad = np.nonzero(margin_fn(_host64(x), wr, wl.top_k, rb, sb)
                      <= min_margin)[0]
     for t in bad:
         t = int(t)
@@ -219,7 +219,7 @@ def _redraw_close_tokens(inp, wl, seed, dev, margin_fn, min_margin,
             g = torch.Generator(device=dev)
             g.manual_seed(_row_seed(seed, t, attempt))
             row = _randn((1, wl.d_model), g, dev, 1.0, wl.torch_dtype)
-            m = margin_fn(_host64(row), wr, rb, sb, wl.top_k)[0]
+            m = margin_fn(_host64(row), wr, wl.top_k, rb, sb)[0]
             inp["redraws"] += 1
             if m > min_margin:
                 x[t] = row[0]
