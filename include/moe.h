@@ -206,6 +206,30 @@ int32_t moe_expert_ffn(const moe_problem* p, const void* x,
                        size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Step 3 alone, the up projection ([RC]; [GN] Implementing a complete MoE
+ * layer): h[r] = act(x[token(r)] . W1^T) for every routed row
+ * r < offsets[E] (token(r) = perm[r] / k) and every shared row T*k + t
+ * (token t).  SwiGLU: silu(x . W_gate^T) * (x . W_up^T); GELU:
+ * gelu(x . W1^T + b1).
+ *   h   [T*k + n_shared*T, d_ff] output, problem dtype; rows
+ *       [offsets[E], T*k) are not written.
+ */
+int32_t moe_expert_up(const moe_problem* p, const void* x,
+                      const int32_t* perm, const int32_t* offsets,
+                      const moe_expert_weights* w, void* h,
+                      hipStream_t stream);
+
+/*
+ * Step 4 alone, the down projection: y[r] = h[r] . W2^T (+ b2 for GELU) for
+ * the same rows as moe_expert_up.
+ *   h   [T*k + n_shared*T, d_ff] input as written by moe_expert_up.
+ *   y   [T*k + n_shared*T, d] output, problem dtype.
+ */
+int32_t moe_expert_down(const moe_problem* p, const void* h,
+                        const int32_t* offsets, const moe_expert_weights* w,
+                        void* y, hipStream_t stream);
+
+/*
  * Step 5, combine ([RC]: weighted sum plus residual; [LBS] Token Dropping:
  * a dropped slot contributes zero; [FA] Concept).
  *   x_residual  [T, d] or NULL (NULL omits the residual, as the [LBS], [HA]

@@ -244,7 +244,33 @@ int32_t moe_expert_ffn(const moe_problem* p, const void* x,
   if (p->T == 0) return MOE_OK;
   const Layout L = make_layout(*p);
   FfnArgs a = ffn_args(p, x, perm, offsets, w, (char*)ws + L.h, y);
-  return status_of(launch_expert_ffn(a, stream));
+  MOE_TRY(launch_expert_up(a, stream));
+  return status_of(launch_expert_down(a, stream));
+}
+
+int32_t moe_expert_up(const moe_problem* p, const void* x,
+                      const int32_t* perm, const int32_t* offsets,
+                      const moe_expert_weights* w, void* h,
+                      hipStream_t stream) {
+  int32_t st = check_problem(p);
+  if (st) return st;
+  if ((st = check_weights(p, w))) return st;
+  if (p->T > 0 && (!x || !perm || !offsets || !h)) return MOE_EINVAL;
+  if (p->T == 0) return MOE_OK;
+  FfnArgs a = ffn_args(p, x, perm, offsets, w, h, nullptr);
+  return status_of(launch_expert_up(a, stream));
+}
+
+int32_t moe_expert_down(const moe_problem* p, const void* h,
+                        const int32_t* offsets, const moe_expert_weights* w,
+                        void* y, hipStream_t stream) {
+  int32_t st = check_problem(p);
+  if (st) return st;
+  if ((st = check_weights(p, w))) return st;
+  if (p->T > 0 && (!h || !offsets || !y)) return MOE_EINVAL;
+  if (p->T == 0) return MOE_OK;
+  FfnArgs a = ffn_args(p, nullptr, nullptr, offsets, w, (void*)h, y);
+  return status_of(launch_expert_down(a, stream));
 }
 
 int32_t moe_combine(const moe_problem* p, const void* x_residual,
@@ -310,7 +336,8 @@ int32_t moe_layer_forward(const moe_problem* p, const void* x,
   MOE_TRY(launch_dispatch(a, stream));
   void* y = wsb + L.y;
   FfnArgs f = ffn_args(p, x, a.perm, a.offsets, w, wsb + L.h, y);
-  MOE_TRY(launch_expert_ffn(f, stream));
+  MOE_TRY(launch_expert_up(f, stream));
+  MOE_TRY(launch_expert_down(f, stream));
   MOE_TRY(launch_combine(p->dtype, x, y, a.slot_of, gate, out, p->T,
                          p->d_model, p->top_k, p->n_shared, stream));
   return MOE_OK;

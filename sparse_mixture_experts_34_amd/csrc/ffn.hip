@@ -459,23 +459,37 @@ int ffn_schedule(int dtype, int T, int k, int E) {
   return ((long long)T * k <= 64LL * E) ? 0 : 1;
 }
 
-hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s) {
-  if (a.T == 0) return hipSuccess;
-  const int sched = ffn_schedule(a.dtype, a.T, a.k, a.E);
+namespace {
+struct Plan {
+  int sched, rt, max_tiles;
+};
+Plan plan_of(const FfnArgs& a) {
+  Plan p;
+  p.sched = ffn_schedule(a.dtype, a.T, a.k, a.E);
   const long long tk = (long long)a.T * a.k;
-  int rt = 4;
-  if (sched == 0) {
+  p.rt = 4;
+  if (p.sched == 0) {
     const int maxrows = a.T;   // a token picks an expert at most once
-    rt = maxrows <= 16 ? 1 : (maxrows <= 32 ? 2 : 4);
+    p.rt = maxrows <= 16 ? 1 : (maxrows <= 32 ? 2 : 4);
   }
-  const int bm = sched == 1 ? TL_BM : F32_BM;
-  const int max_tiles = (int)((tk + bm - 1) / bm) + a.E +
-                        (a.n_shared ? (a.T + bm - 1) / bm : 0);
-  hipError_t e;
-  if (a.act == 1) e = launch_mode<UP_SWIGLU>(a, s, sched, rt, max_tiles);
-  else e = launch_mode<UP_GELU>(a, s, sched, rt, max_tiles);
-  if (e != hipSuccess) return e;
-  return launch_mode<DOWN>(a, s, sched, rt, max_tiles);
+  const int bm = p.sched == 1 ? TL_BM : F32_BM;
+  p.max_tiles = (int)((tk + bm - 1) / bm) + a.E +
+                (a.n_shared ? (a.T + bm - 1) / bm : 0);
+  return p;
+}
+}  // namespace
+
+hipError_t launch_expert_up(const FfnArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  const Plan p = plan_of(a);
+  if (a.act == 1) return launch_mode<UP_SWIGLU>(a, s, p.sched, p.rt, p.max_tiles);
+  return launch_mode<UP_GELU>(a, s, p.sched, p.rt, p.max_tiles);
+}
+
+hipError_t launch_expert_down(const FfnArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  const Plan p = plan_of(a);
+  return launch_mode<DOWN>(a, s, p.sched, p.rt, p.max_tiles);
 }
 
 }  // namespace moe

@@ -77,7 +77,8 @@ struct FfnArgs {
   void* h;   // [T*k + n_shared*T, d_ff] workspace
   void* y;   // [T*k + n_shared*T, d]
 };
-hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t s);
+hipError_t launch_expert_up(const FfnArgs& a, hipStream_t s);
+hipError_t launch_expert_down(const FfnArgs& a, hipStream_t s);
 
 // ---- combine ---------------------------------------------------------------
 hipError_t launch_combine(int dtype, const void* x, const void* y,
