@@ -132,6 +132,7 @@ __device__ void scan_all(int* chunk, int nchunks, const DispatchArgs& a,
     float pm;
     if (a.partials) {
       float v = 0.f;
+#pragma unroll 8
       for (int b = 0; b < a.n_partials; ++b) v += a.partials[(size_t)b * E + e];
       pm = v / (float)a.T;
       if (a.prob_mean_out) a.prob_mean_out[e] = pm;

@@ -19,10 +19,11 @@
 //   down  Y[r, n]  = H[r,:] . W2[g, n, :] (+ b2)
 //
 // Two bf16 schedules, picked on the host from the shapes only:
-//   stream  few rows per expert (decode): each wave owns 16 output columns
-//           and streams those weight rows once from HBM straight into MFMA
-//           B registers (16x16x32), with a 4-deep register prefetch ring;
-//           the handful of token rows ride along as the A operand.
+//   stream  few rows per expert (decode): a workgroup owns 16 output
+//           columns, its waves split K, and each streams its weight rows
+//           once from HBM straight into MFMA B registers (16x16x32) with a
+//           4-deep register prefetch ring; the handful of token rows ride
+//           along as the A operand; partial sums meet in LDS.
 //   tiled   many rows per expert (prefill): 128x128 workgroup tiles, BK=64,
 //           A and B staged through XOR-swizzled LDS with double buffering,
 //           32x32x16 MFMAs, the activation fused into the epilogue, and the
@@ -94,8 +95,12 @@ __device__ __forceinline__ void group_weights(const FfnArgs& a, int g,
 // ===========================================================================
 // stream schedule (bf16)
 // ===========================================================================
+// A workgroup owns 16 output columns of one group; its 4 waves split the K
+// steps into contiguous quarters, stream their weight rows straight into
+// MFMA B registers (4-deep prefetch ring) and add their partial sums through
+// LDS in the fixed order 0,1,2,3.
 constexpr int ST_WAVES = 4;
-constexpr int ST_COLS = 16;          // output columns per wave
+constexpr int ST_COLS = 16;          // output columns per workgroup
 constexpr int ST_KSTEP = 64;         // K per step (two 16x16x32 MFMAs)
 constexpr int ST_PF = 4;             // prefetch ring depth (steps)
 
@@ -108,24 +113,28 @@ struct StreamBuf {
 template <int MODE, int RT>
 __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
   constexpr int NMAT = MODE == UP_SWIGLU ? 2 : 1;
+  __shared__ f32x4 red[ST_WAVES - 1][NMAT * RT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = blockIdx.y;
   const Group gr = group_of(g, a.offsets, a.E, a.T, a.k);
-  if (gr.rows <= 0) return;
+  if (gr.rows <= 0) return;                 // uniform over the workgroup
   const int N = MODE == DOWN ? a.d : a.d_ff;
   const int K = MODE == DOWN ? a.d_ff : a.d;
-  const int n0 = (blockIdx.x * ST_WAVES + wave) * ST_COLS;
-  if (n0 >= N) return;
+  const int n0 = blockIdx.x * ST_COLS;
+  if (n0 >= N) return;                      // uniform over the workgroup
   const void *w0v, *w1v, *biasv;
   group_weights<MODE>(a, g, gr.shared, N, K, w0v, w1v, biasv);
   const bf16* wm[2] = {(const bf16*)w0v, (const bf16*)w1v};
 
   const int col = lane & 15;   // B: weight row n0+col; A: token row
   const int kq = lane >> 4;    // 16-wide k slice of the 64-wide step
+  const int nsteps = K / ST_KSTEP;
+  const int s_beg = wave * nsteps / ST_WAVES;
+  const int my_steps = (wave + 1) * nsteps / ST_WAVES - s_beg;
+  const int koff = s_beg * ST_KSTEP + kq * 16;
   const bf16* brow[NMAT];
 #pragma unroll
-  for (int m = 0; m < NMAT; ++m) brow[m] = wm[m] + (size_t)(n0 + col) * K + kq * 16;
-  const int nsteps = K / ST_KSTEP;
+  for (int m = 0; m < NMAT; ++m) brow[m] = wm[m] + (size_t)(n0 + col) * K + koff;
 
   for (int rg = 0; rg < gr.rows; rg += RT * 16) {
     const int ntile = min(RT, (gr.rows - rg + 15) >> 4);
@@ -133,7 +142,7 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int i = min(rg + t * 16 + col, gr.rows - 1);
-      arow[t] = a_row<MODE, bf16>(a, gr, i, K) + kq * 16;
+      arow[t] = a_row<MODE, bf16>(a, gr, i, K) + koff;
     }
     f32x4 acc[NMAT][RT];
 #pragma unroll
@@ -177,39 +186,56 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
     };
 #pragma unroll
     for (int p = 0; p < ST_PF; ++p)
-      if (p < nsteps) load(buf[p], p);
-    for (int s0 = 0; s0 < nsteps; s0 += ST_PF) {
+      if (p < my_steps) load(buf[p], p);
+    for (int s0 = 0; s0 < my_steps; s0 += ST_PF) {
 #pragma unroll
       for (int p = 0; p < ST_PF; ++p) {
         const int s = s0 + p;
-        if (s < nsteps) {
+        if (s < my_steps) {
           compute(buf[p]);
-          if (s + ST_PF < nsteps) load(buf[p], s + ST_PF);
+          if (s + ST_PF < my_steps) load(buf[p], s + ST_PF);
         }
       }
     }
 
-    // epilogue: lane holds column n0+col, rows rg + 16t + 4*kq + r
-    const int n = n0 + col;
-    float bias = 0.f;
-    if (MODE != UP_SWIGLU && biasv) bias = (float)((const bf16*)biasv)[n];
-    bf16* outp = (bf16*)(MODE == DOWN ? a.y : a.h);
+    // K-split reduction: waves 1..3 park their sums, wave 0 adds in order
+    if (wave > 0) {
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      if (t < ntile) {
+      for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = rg + t * 16 + kq * 4 + r;
-          if (i < gr.rows) {
-            float v;
-            if (MODE == UP_SWIGLU) v = silu(acc[0][t][r]) * acc[NMAT - 1][t][r];
-            else if (MODE == UP_GELU) v = gelu_erf(acc[0][t][r] + bias);
-            else v = acc[0][t][r] + bias;
-            outp[(size_t)(gr.out0 + i) * N + n] = (bf16)v;
+        for (int t = 0; t < RT; ++t) red[wave - 1][m * RT + t][lane] = acc[m][t];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 0; w < ST_WAVES - 1; ++w)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int t = 0; t < RT; ++t) acc[m][t] += red[w][m * RT + t][lane];
+      // epilogue: lane holds column n0+col, rows rg + 16t + 4*kq + r
+      const int n = n0 + col;
+      float bias = 0.f;
+      if (MODE != UP_SWIGLU && biasv) bias = (float)((const bf16*)biasv)[n];
+      bf16* outp = (bf16*)(MODE == DOWN ? a.y : a.h);
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        if (t < ntile) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = rg + t * 16 + kq * 4 + r;
+            if (i < gr.rows) {
+              float v;
+              if (MODE == UP_SWIGLU) v = silu(acc[0][t][r]) * acc[NMAT - 1][t][r];
+              else if (MODE == UP_GELU) v = gelu_erf(acc[0][t][r] + bias);
+              else v = acc[0][t][r] + bias;
+              outp[(size_t)(gr.out0 + i) * N + n] = (bf16)v;
+            }
           }
         }
       }
     }
+    __syncthreads();   // red is reused by the next row group
   }
 }
 
@@ -434,7 +460,7 @@ hipError_t launch_mode(const FfnArgs& a, hipStream_t s, int sched, int rt,
   const int N = MODE == DOWN ? a.d : a.d_ff;
   const int G = a.E + a.n_shared;
   if (sched == 0) {
-    dim3 grid((N + ST_WAVES * ST_COLS - 1) / (ST_WAVES * ST_COLS), G);
+    dim3 grid((N + ST_COLS - 1) / ST_COLS, G);
     if (rt == 1) ffn_stream_kernel<MODE, 1><<<grid, ST_WAVES * 64, 0, s>>>(a);
     else if (rt == 2) ffn_stream_kernel<MODE, 2><<<grid, ST_WAVES * 64, 0, s>>>(a);
     else ffn_stream_kernel<MODE, 4><<<grid, ST_WAVES * 64, 0, s>>>(a);

@@ -8,17 +8,26 @@
 
 namespace moe {
 
-// Tokens handled by one workgroup of the route-select kernel; also the
-// granularity of the per-block probability partial sums.
-constexpr int ROUTE_TOKENS_PER_BLOCK = 64;
+// Route-select: 4 waves per workgroup, route_tpw(T) tokens per wave (one
+// token per wave for small batches, up to 16 for large ones, so that about
+// 256 workgroups cover the batch).  A workgroup writes one row of
+// probability partial sums.
+constexpr int ROUTE_WAVES = 4;
+inline int route_tpw(int T) {
+  const int t = (T + 1023) / 1024;
+  return t < 1 ? 1 : (t > 16 ? 16 : t);
+}
+inline int route_blocks(int T) {
+  const int per = ROUTE_WAVES * route_tpw(T);
+  return (T + per - 1) / per;
+}
+// Largest K split of the router GEMM.
+constexpr int ROUTER_MAX_KSPLIT = 16;
 // Assignments (token, slot) handled by one wave in the dispatch kernels.
 constexpr int DISPATCH_CHUNK = 256;
 // Chunks (one per wave) per dispatch workgroup.
 constexpr int DISPATCH_WAVES = 4;
 
-inline int route_blocks(int T) {
-  return (T + ROUTE_TOKENS_PER_BLOCK - 1) / ROUTE_TOKENS_PER_BLOCK;
-}
 inline int dispatch_chunks(long long tk) {
   return (int)((tk + DISPATCH_CHUNK - 1) / DISPATCH_CHUNK);
 }

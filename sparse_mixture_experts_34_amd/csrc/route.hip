@@ -187,8 +187,7 @@ __global__ __launch_bounds__(RL_THREADS) void router_logits_kernel(
   }
 }
 
-constexpr int RS_WAVES = 4;
-constexpr int RS_TOK_PER_WAVE = ROUTE_TOKENS_PER_BLOCK / RS_WAVES;
+constexpr int RS_WAVES = ROUTE_WAVES;
 constexpr int RS_MAXC = 4;   // experts per lane: E <= 256
 
 __global__ __launch_bounds__(RS_WAVES * 64) void route_select_kernel(
@@ -196,7 +195,7 @@ __global__ __launch_bounds__(RS_WAVES * 64) void route_select_kernel(
     const float* __restrict__ router_bias,
     const float* __restrict__ select_bias, float* __restrict__ logits_out,
     int32_t* __restrict__ idx_out, float* __restrict__ gate_out,
-    float* __restrict__ partials, int T, int E, int k) {
+    float* __restrict__ partials, int T, int E, int k, int tpw) {
   __shared__ float psum_s[RS_WAVES][256];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -204,8 +203,8 @@ __global__ __launch_bounds__(RS_WAVES * 64) void route_select_kernel(
 #pragma unroll
   for (int c = 0; c < RS_MAXC; ++c) psum[c] = 0.f;
 
-  const int tbeg = blockIdx.x * ROUTE_TOKENS_PER_BLOCK + wave * RS_TOK_PER_WAVE;
-  for (int i = 0; i < RS_TOK_PER_WAVE; ++i) {
+  const int tbeg = (blockIdx.x * RS_WAVES + wave) * tpw;
+  for (int i = 0; i < tpw; ++i) {
     const int t = tbeg + i;
     if (t >= T) break;   // wave-uniform
     float l[RS_MAXC], key[RS_MAXC];
@@ -215,8 +214,15 @@ __global__ __launch_bounds__(RS_WAVES * 64) void route_select_kernel(
       l[c] = -INFINITY;
       key[c] = -INFINITY;
       if (e < E) {
-        float v = 0.f;
-        for (int s = 0; s < ksplit; ++s) v += part[((size_t)s * T + t) * E + e];
+        // independent loads of the K-slice partial sums, added in order
+        float pv[ROUTER_MAX_KSPLIT];
+#pragma unroll
+        for (int s = 0; s < ROUTER_MAX_KSPLIT; ++s)
+          pv[s] = s < ksplit ? part[((size_t)s * T + t) * E + e] : 0.f;
+        float v = pv[0];
+#pragma unroll
+        for (int s = 1; s < ROUTER_MAX_KSPLIT; ++s)
+          if (s < ksplit) v += pv[s];
         if (router_bias) v += router_bias[e];
         l[c] = v;
         key[c] = select_bias ? v + select_bias[e] : v;
@@ -311,6 +317,7 @@ __global__ void prob_mean_kernel(const float* __restrict__ partials,
                                  int E) {
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     float v = 0.f;
+#pragma unroll 8
     for (int b = 0; b < nblk; ++b) v += partials[(size_t)b * E + e];
     pm[e] = T > 0 ? v / (float)T : 0.f;
   }
@@ -325,7 +332,9 @@ int router_ksplit(int T, int d, int E, int dtype) {
   const long long blocks = (long long)((T + tt - 1) / tt) *
                            ((E + RL_EXP_TILE - 1) / RL_EXP_TILE);
   int ks = 1;
-  while (blocks * ks * 2 <= 256 && d % (ks * 2 * 256) == 0) ks *= 2;
+  while (blocks * ks * 2 <= 256 && ks * 2 <= ROUTER_MAX_KSPLIT &&
+         d % (ks * 2 * 256) == 0)
+    ks *= 2;
   return ks;
 }
 
@@ -353,7 +362,7 @@ hipError_t launch_route_select_from(const float* part, int ksplit,
                                     hipStream_t s) {
   route_select_kernel<<<route_blocks(T), RS_WAVES * 64, 0, s>>>(
       part, ksplit, router_bias, select_bias, logits, idx, gate, partials, T,
-      E, k);
+      E, k, route_tpw(T));
   return hipGetLastError();
 }
 
