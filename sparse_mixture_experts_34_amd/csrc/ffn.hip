@@ -242,19 +242,354 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
 // ===========================================================================
 // tiled schedule (bf16)
 // ===========================================================================
-constexpr int TL_BM = 128;
-constexpr int TL_BN = 128;   // B rows per tile (SwiGLU: 64 gate + 64 up)
-constexpr int TL_BK = 64;
-constexpr int TL_THREADS = 256;
+// Workgroup tile BM x 256 (BM = 128 or 256) over BK = 64 slices of K, eight
+// waves (two per SIMD) in a 2 x 4 grid, each wave (BM/2) x 64 of 32x32x16
+// MFMA tiles.
+//
+// A and B slices go from global memory straight into LDS (direct-to-LDS
+// loads, 16 bytes per lane, one instruction = 8 rows x 128 bytes, so every
+// row segment is read whole).  LDS rows are 128 bytes; 16-byte chunk c of
+// row r sits at position c ^ key(r) so that the MFMA operand reads (32 rows,
+// one chunk) spread over all banks.  The key depends only on the low row
+// bits, which makes the swizzled offset of a lane the same for every 32-row
+// tile: one register per K-substep, tile offsets are immediates.  Two stages
+// live in four distinct arrays so the compiler sees that the stage being
+// loaded never aliases the stage being read: the next slice loads during the
+// MFMAs.
+//
+// Tile order: logical tiles run expert by expert, and inside an expert
+// n-block by n-block with the m-tiles innermost, so neighbouring tiles share
+// weight (B) slices and token (A) slices.  Workgroups are handed to the 8
+// XCDs round-robin by id; the id is remapped so that each XCD receives a
+// contiguous run of logical tiles and its L2 serves the shared slices.
+constexpr int TL_BN = 256;   // B rows per tile (SwiGLU: 128 gate + 128 up)
+constexpr int N_XCD = 8;
+#ifndef MOE_TL_WAVES
+#define MOE_TL_WAVES 8
+#endif
 
-// Swizzled LDS offset (in bf16 elements) of 16-byte chunk c of row r in a
-// [rows][64] bf16 tile: chunk position c ^ (r & 7).
-__device__ __forceinline__ int swz(int r, int c) {
-  return r * TL_BK + ((c ^ (r & 7)) << 3);
+// Logical tile L -> (group, first row, n-block).  Whole workgroup; false
+// past the last tile.
+__device__ bool find_tile_n(const FfnArgs& a, int G, int BM, int NB, int L,
+                            int* s_info) {
+  if (threadIdx.x == 0) {
+    int acc = 0, g = 0, r0 = -1, nb = 0;
+    for (; g < G; ++g) {
+      const int rows = g < a.E ? a.offsets[g + 1] - a.offsets[g] : a.T;
+      const int nt = (rows + BM - 1) / BM;
+      const int span = nt * NB;
+      if (L < acc + span) {
+        const int r = L - acc;
+        nb = r / nt;
+        r0 = (r - nb * nt) * BM;
+        break;
+      }
+      acc += span;
+    }
+    s_info[0] = g;
+    s_info[1] = r0;
+    s_info[2] = nb;
+  }
+  __syncthreads();
+  return s_info[1] >= 0;
 }
 
-// Maps a linear row-tile id to (group, first row); returns false when the
-// id is past the last tile.  Executed by the whole workgroup.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds_base + 16*l (lds_base must be the same for the whole wave).  The
+// instruction has no destination registers.  It is written as inline asm so
+// that the compiler does not track it: its own waitcnt analysis would
+// otherwise make every later LDS read wait for all loads in flight.  The
+// kernel orders these loads itself with s_waitcnt vmcnt at each slice
+// barrier; a compiler-generated vmcnt wait can only wait longer (vector
+// loads complete in order).
+__device__ __forceinline__ void dma16(const void* src, bf16* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(lds_void_t*)lds_base);   // wave-uniform
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(m0)
+      : "memory", "m0");
+}
+
+// End of a K slice: wait until at most N of this wave's vector-memory loads
+// (the later slices' direct-to-LDS loads) are in flight and all its LDS
+// reads are done, then meet the other waves.  A plain s_barrier: the
+// workgroup fence of __syncthreads would also wait for the later slices.
+template <int N>
+__device__ __forceinline__ void slice_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N)
+               : "memory");
+}
+
+// LDS geometry of one K slice of BK bf16 per row: rows of BK*2 bytes, CPR
+// 16-byte chunks per row; chunk c of row r sits at position c ^ key(r).  The
+// key spreads a 32-row MFMA operand read (one chunk of 32 consecutive rows)
+// over all LDS banks and depends only on the row's low bits, so it is the
+// same for every 32-row tile.
+template <int BK>
+struct SliceGeom {
+  static constexpr int CPR = BK / 8;         // chunks per row
+  static constexpr int RPI = 64 / CPR;       // rows per load instruction
+  static constexpr int SUB = BK / 16;        // 32x32x16 MFMA K-substeps
+  __device__ static int key(int r) {
+    return BK == 64 ? (r >> 1) & 7 : (r >> 2) & 3;
+  }
+};
+
+template <int MODE, int BM, int BK, int NS, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
+                                                                  int NB) {
+  using Geo = SliceGeom<BK>;
+  constexpr int TL_WAVES = WAVES;
+  constexpr int TL_THREADS = WAVES * 64;
+  constexpr int WGN = WAVES / 2;      // waves along N (2 along M)
+  constexpr int WM = BM / 2;          // rows per wave
+  constexpr int WN = TL_BN / WGN;     // B rows per wave (128 or 64)
+  constexpr int MT = WM / 32;         // 32-row MFMA tiles per wave
+  constexpr int NT = WN / 32;         // 32-col MFMA tiles per wave
+  constexpr int IA = BM / Geo::RPI / TL_WAVES;      // A loads per wave, slice
+  constexpr int IB = TL_BN / Geo::RPI / TL_WAVES;   // B loads per wave, slice
+  constexpr int PER = IA + IB;                      // loads per wave, slice
+  constexpr int D = NS - 1;                         // slices in flight
+  constexpr int SA = BM * BK, SB = TL_BN * BK;      // elements per slice
+  static_assert(IA >= 1 && IB >= 1, "every wave loads A and B rows");
+  // NS stages of A and B slices; every stage index below is a compile-time
+  // constant, so the compiler can see that the stage being loaded never
+  // aliases the stage being read and does not make LDS reads wait for the
+  // loads in flight.
+  static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
+  __shared__ __attribute__((aligned(16))) bf16 A0[SA];
+  __shared__ __attribute__((aligned(16))) bf16 A1[SA];
+  __shared__ __attribute__((aligned(16))) bf16 A2[NS > 2 ? SA : 8];
+  __shared__ __attribute__((aligned(16))) bf16 A3[NS > 3 ? SA : 8];
+  __shared__ __attribute__((aligned(16))) bf16 B0[SB];
+  __shared__ __attribute__((aligned(16))) bf16 B1[SB];
+  __shared__ __attribute__((aligned(16))) bf16 B2[NS > 2 ? SB : 8];
+  __shared__ __attribute__((aligned(16))) bf16 B3[NS > 3 ? SB : 8];
+  __shared__ int s_info[3];
+  // stage s's arrays (s is a constant after unrolling, so each access names
+  // one distinct object)
+  auto As = [&](int st) -> bf16* {
+    return st == 0 ? A0 : (st == 1 ? A1 : (st == 2 ? A2 : A3));
+  };
+  auto Bs = [&](int st) -> bf16* {
+    return st == 0 ? B0 : (st == 1 ? B1 : (st == 2 ? B2 : B3));
+  };
+
+  const int G = a.E + a.n_shared;
+  const int per_xcd = gridDim.x / N_XCD;          // grid is a multiple of 8
+  const int L = (blockIdx.x % N_XCD) * per_xcd + blockIdx.x / N_XCD;
+  if (!find_tile_n(a, G, BM, NB, L, s_info)) return;
+  const int g = s_info[0], r0 = s_info[1], nb = s_info[2];
+  const Group gr = group_of(g, a.offsets, a.E, a.T, a.k);
+  const int N = MODE == DOWN ? a.d : a.d_ff;
+  const int K = MODE == DOWN ? a.d_ff : a.d;
+  const int ncols = MODE == UP_SWIGLU ? TL_BN / 2 : TL_BN;   // outputs per tile
+  const int nbase = nb * ncols;
+  const void *w0v, *w1v, *biasv;
+  group_weights<MODE>(a, g, gr.shared, N, K, w0v, w1v, biasv);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int l31 = lane & 31, q = lane >> 5;
+
+  // Loads: wave w fills A rows [w*IA*RPI, (w+1)*IA*RPI) and B rows likewise,
+  // RPI rows per instruction; lane l covers row RPI*i + l/CPR, LDS position
+  // l%CPR, i.e. global chunk (l%CPR) ^ key(row).  32-bit element offsets.
+  const int lr = lane / Geo::CPR;
+  const int lp = lane % Geo::CPR;
+  const bf16* abase_g = (const bf16*)(MODE == DOWN ? a.h : a.x);
+  uint32_t ao[IA];
+#pragma unroll
+  for (int i = 0; i < IA; ++i) {
+    const int row = (wave * IA + i) * Geo::RPI + lr;
+    const int ai = min(r0 + row, gr.rows - 1);
+    const int arow_g = MODE == DOWN ? gr.out0 + ai
+                                    : (gr.shared ? ai : a.perm[gr.out0 + ai] / a.k);
+    ao[i] = (uint32_t)arow_g * (uint32_t)K + ((lp ^ Geo::key(row)) << 3);
+  }
+  // B rows: SwiGLU block b = r >> 6 holds gate cols [32b, 32b+32) in rows
+  // [64b, 64b+32) and the matching up cols in [64b+32, 64b+64), so wave
+  // column wn's two N-tiles are a gate tile and its up tile.
+  uint32_t bo[IB];
+  const bf16* bb[IB];
+#pragma unroll
+  for (int i = 0; i < IB; ++i) {
+    const int row = (wave * IB + i) * Geo::RPI + lr;
+    int wrow;
+    if (MODE == UP_SWIGLU) {
+      bb[i] = (const bf16*)(((row >> 5) & 1) ? w1v : w0v);
+      wrow = nbase + 32 * (row >> 6) + (row & 31);
+    } else {
+      bb[i] = (const bf16*)w0v;
+      wrow = nbase + row;
+    }
+    wrow = min(wrow, N - 1);
+    bo[i] = (uint32_t)wrow * (uint32_t)K + ((lp ^ Geo::key(row)) << 3);
+  }
+  auto issue = [&](int kt, bf16* Ad, bf16* Bd) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < IA; ++i)
+      dma16(abase_g + ao[i] + k0, Ad + (wave * IA + i) * Geo::RPI * BK);
+#pragma unroll
+    for (int i = 0; i < IB; ++i)
+      dma16(bb[i] + bo[i] + k0, Bd + (wave * IB + i) * Geo::RPI * BK);
+  };
+
+  f32x16 acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int nk = K / BK;
+  // MFMA operand rows: A rows wm*WM + 32i + l31, B rows wn*64 + 32j + l31;
+  // their swizzle key is key(l31) for every tile
+  const int akey = Geo::key(l31);
+  const int arow0 = (wm * WM + l31) * BK;
+  const int brow0 = (wn * WN + l31) * BK;
+  // Operands of substep ss+1 are read from LDS before the MFMAs of substep
+  // ss are issued, so LDS latency overlaps matrix work.
+  auto compute = [&](const bf16* Ab, const bf16* Bb) {
+    V16 av[2][MT], bv[2][NT];
+    auto fetch = [&](int ss, int set) {
+      const int pos = ((ss * 2 + q) ^ akey) << 3;
+      const bf16* ap = Ab + arow0 + pos;
+      const bf16* bp = Bb + brow0 + pos;
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+        av[set][i].u = *reinterpret_cast<const u32x4*>(ap + i * 32 * BK);
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        bv[set][j].u = *reinterpret_cast<const u32x4*>(bp + j * 32 * BK);
+    };
+    fetch(0, 0);
+#pragma unroll
+    for (int ss = 0; ss < Geo::SUB; ++ss) {
+      const int cur = ss & 1;
+      if (ss + 1 < Geo::SUB) fetch(ss + 1, cur ^ 1);
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cur][i].h, bv[cur][j].h, acc[i][j], 0, 0, 0);
+      // schedule: the next substep's LDS reads interleaved one by one with
+      // this substep's MFMAs
+      if (ss + 1 < Geo::SUB) {
+#pragma unroll
+        for (int r = 0; r < MT + NT; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one DS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, MT * NT - (MT + NT), 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, MT * NT, 0);
+      }
+    }
+  };
+
+  // prologue: slices 0..D-1 in flight, then wait for slice 0
+#pragma unroll
+  for (int s = 0; s < D; ++s)
+    if (s < nk) issue(s, As(s), Bs(s));
+  if (nk >= D) slice_barrier<(D - 1) * PER>();   // later prologue slices fly
+  else slice_barrier<0>();
+  // Main loop, NS slices per trip with constant stage indices.  Slice k
+  // reads stage k % NS; before it, slice k + D is issued into stage
+  // (k + D) % NS, last read by slice k - 1 (one barrier ago).  After slice k
+  // the wave waits until slice k + 1 has landed: all later slices may stay
+  // in flight.
+  for (int kt = 0; kt < nk; kt += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int k = kt + u;
+      if (k < nk) {
+        const bool more = k + D < nk;
+        if (more) issue(k + D, As((u + D) % NS), Bs((u + D) % NS));
+        compute(As(u), Bs(u));
+        if (more) slice_barrier<(D - 1) * PER>();
+        else slice_barrier<0>();
+      }
+    }
+  }
+
+  // ---- epilogue: activation, stage the bf16 tile in LDS, store rows ----
+  // The output tile (BM x ncols bf16, row-major) is staged in the A stages
+  // and, past their end, in the B stages.
+  static_assert(BM * TL_BN <= NS * (SA + SB), "output tile fits the LDS");
+  __syncthreads();
+  auto ot = [&](int row, int col) -> bf16& {
+    const int idx = row * ncols + col;
+    const int st = idx / SA;
+    if (st < NS) return As(st)[idx - st * SA];
+    const int rb = idx - NS * SA;
+    return Bs(rb / SB)[rb % SB];
+  };
+  // 32x32 accumulator layout: lane holds column lane&31; item v is row
+  // (v&3) + 4*(lane>>5) + 8*(v>>2).
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = wm * WM + 32 * i + (v & 3) + 4 * q + 8 * (v >> 2);
+      if (MODE == UP_SWIGLU) {
+        // N-tiles (2p, 2p+1) are a gate tile and its up tile
+#pragma unroll
+        for (int p = 0; p < NT / 2; ++p) {
+          const int c = 32 * (wn * (NT / 2) + p) + l31;
+          const float h = silu(acc[i][2 * p][v]) * acc[i][2 * p + 1][v];
+          ot(row, c) = (bf16)h;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const int c = wn * WN + 32 * j + l31;
+          const int n = min(nbase + c, N - 1);
+          const float bias = biasv ? (float)((const bf16*)biasv)[n] : 0.f;
+          float v2 = acc[i][j][v] + bias;
+          if (MODE == UP_GELU) v2 = gelu_erf(v2);
+          ot(row, c) = (bf16)v2;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  bf16* outp = (bf16*)(MODE == DOWN ? a.y : a.h);
+  const int cpr = ncols / 8;   // 16-byte chunks per output row
+  for (int idx = tid; idx < BM * cpr; idx += TL_THREADS) {
+    const int row = idx / cpr, ch = idx - row * cpr;
+    const int i = r0 + row;
+    const int n = nbase + ch * 8;
+    if (i < gr.rows && n < N) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&ot(row, ch * 8));
+      stg16(outp + (size_t)(gr.out0 + i) * N + n, v);
+    }
+  }
+}
+
+#ifndef MOE_TL_BK
+#define MOE_TL_BK 64
+#endif
+#ifndef MOE_TL_NS
+#define MOE_TL_NS 2
+#endif
+
+// ===========================================================================
+// float32 schedule
+// ===========================================================================
+// Linear row-tile id -> (group, first row); false past the last tile.
+// Whole workgroup.
 __device__ bool find_tile(const FfnArgs& a, int G, int BM, int tile, int* s_info) {
   if (threadIdx.x == 0) {
     int acc = 0, g = 0, r0 = -1;
@@ -274,150 +609,6 @@ __device__ bool find_tile(const FfnArgs& a, int G, int BM, int tile, int* s_info
   return s_info[1] >= 0;
 }
 
-template <int MODE>
-__global__ __launch_bounds__(TL_THREADS) void ffn_tiled_kernel(FfnArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 lds[2][2][TL_BM * TL_BK];  // [buf][A/B]
-  __shared__ int s_info[2];
-  const int G = a.E + a.n_shared;
-  if (!find_tile(a, G, TL_BM, blockIdx.x, s_info)) return;
-  const int g = s_info[0];
-  const int r0 = s_info[1];
-  const Group gr = group_of(g, a.offsets, a.E, a.T, a.k);
-  const int N = MODE == DOWN ? a.d : a.d_ff;
-  const int K = MODE == DOWN ? a.d_ff : a.d;
-  // output columns covered by this workgroup
-  const int ncols = MODE == UP_SWIGLU ? TL_BN / 2 : TL_BN;
-  const int nbase = blockIdx.y * ncols;
-  const void *w0v, *w1v, *biasv;
-  group_weights<MODE>(a, g, gr.shared, N, K, w0v, w1v, biasv);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-
-  // global->LDS: thread owns chunk lc of rows lr + 32*i, i < 4
-  const int lc = tid & 7, lr = tid >> 3;
-  const bf16* ga[4];
-  const bf16* gb[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = lr + 32 * i;
-    const int ai = min(r0 + row, gr.rows - 1);
-    ga[i] = a_row<MODE, bf16>(a, gr, ai, K) + lc * 8;
-    int wrow;
-    const bf16* wbase;
-    if (MODE == UP_SWIGLU) {
-      const int half = (row >> 5) & 1;          // 0 gate, 1 up
-      wrow = nbase + (row >> 6) * 32 + (row & 31);
-      wbase = (const bf16*)(half ? w1v : w0v);
-    } else {
-      wrow = nbase + row;
-      wbase = (const bf16*)w0v;
-    }
-    wrow = min(wrow, N - 1);
-    gb[i] = wbase + (size_t)wrow * K + lc * 8;
-  }
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  u32x4 ra[4], rb[4];
-  auto gload = [&](int kt) {
-    const int k0 = kt * TL_BK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = ldg16(ga[i] + k0);
-      rb[i] = ldg16(gb[i] + k0);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = lr + 32 * i;
-      *reinterpret_cast<u32x4*>(&lds[buf][0][swz(row, lc)]) = ra[i];
-      *reinterpret_cast<u32x4*>(&lds[buf][1][swz(row, lc)]) = rb[i];
-    }
-  };
-
-  const int nk = K / TL_BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  const int arow_base = wm * 64 + (lane & 31);
-  const int brow_base = wn * 64 + (lane & 31);
-  const int q = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-#pragma unroll
-    for (int ss = 0; ss < 4; ++ss) {
-      const int c = ss * 2 + q;
-      V16 av[2], bv[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        av[i].u = *reinterpret_cast<const u32x4*>(&lds[buf][0][swz(arow_base + 32 * i, c)]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bv[j].u = *reinterpret_cast<const u32x4*>(&lds[buf][1][swz(brow_base + 32 * j, c)]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i].h, bv[j].h, acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue: activation, stage the bf16 tile in LDS, store rows ----
-  // 32x32 accumulator layout: lane holds column lane&31; item v is row
-  // (v&3) + 4*(lane>>5) + 8*(v>>2).
-  bf16* otile = &lds[0][0][0];              // [TL_BM][ncols], reuses LDS
-  const int ocol = lane & 31;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = wm * 64 + 32 * i + (v & 3) + 4 * q + 8 * (v >> 2);
-      if (MODE == UP_SWIGLU) {
-        const int c = wn * 32 + ocol;
-        const float h = silu(acc[i][0][v]) * acc[i][1][v];
-        otile[row * 64 + c] = (bf16)h;
-      } else {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int c = wn * 64 + 32 * j + ocol;
-          const int n = min(nbase + c, N - 1);
-          float bias = biasv ? (float)((const bf16*)biasv)[n] : 0.f;
-          float v2 = acc[i][j][v] + bias;
-          if (MODE == UP_GELU) v2 = gelu_erf(v2);
-          otile[row * 128 + c] = (bf16)v2;
-        }
-      }
-    }
-  }
-  __syncthreads();
-  bf16* outp = (bf16*)(MODE == DOWN ? a.y : a.h);
-  const int chunks_per_row = ncols / 8;
-  for (int idx = tid; idx < TL_BM * chunks_per_row; idx += TL_THREADS) {
-    const int row = idx / chunks_per_row, ch = idx % chunks_per_row;
-    const int i = r0 + row;
-    const int n = nbase + ch * 8;
-    if (i < gr.rows && n < N) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(&otile[row * ncols + ch * 8]);
-      stg16(outp + (size_t)(gr.out0 + i) * N + n, v);
-    }
-  }
-}
-
-// ===========================================================================
-// float32 schedule
-// ===========================================================================
 constexpr int F32_BM = 16;
 constexpr int F32_BN = 64;
 
@@ -464,10 +655,18 @@ hipError_t launch_mode(const FfnArgs& a, hipStream_t s, int sched, int rt,
     if (rt == 1) ffn_stream_kernel<MODE, 1><<<grid, ST_WAVES * 64, 0, s>>>(a);
     else if (rt == 2) ffn_stream_kernel<MODE, 2><<<grid, ST_WAVES * 64, 0, s>>>(a);
     else ffn_stream_kernel<MODE, 4><<<grid, ST_WAVES * 64, 0, s>>>(a);
-  } else if (sched == 1) {
+  } else if (sched == 1 || sched == 3) {
+    // sched 1: BM = 256, sched 3: BM = 128; max_tiles counts m-tiles
     const int ncols = MODE == UP_SWIGLU ? TL_BN / 2 : TL_BN;
-    dim3 grid(max_tiles, (N + ncols - 1) / ncols);
-    ffn_tiled_kernel<MODE><<<grid, TL_THREADS, 0, s>>>(a);
+    const int NB = (N + ncols - 1) / ncols;
+    long long tiles = (long long)max_tiles * NB;
+    tiles = (tiles + N_XCD - 1) / N_XCD * N_XCD;
+    if (sched == 1)
+      ffn_tiled_kernel<MODE, 256, MOE_TL_BK, MOE_TL_NS, MOE_TL_WAVES>
+          <<<(unsigned)tiles, MOE_TL_WAVES * 64, 0, s>>>(a, NB);
+    else
+      ffn_tiled_kernel<MODE, 128, MOE_TL_BK, MOE_TL_NS, MOE_TL_WAVES>
+          <<<(unsigned)tiles, MOE_TL_WAVES * 64, 0, s>>>(a, NB);
   } else {
     dim3 grid(max_tiles, (N + F32_BN - 1) / F32_BN);
     ffn_f32_kernel<MODE><<<grid, 256, 0, s>>>(a);
@@ -482,7 +681,10 @@ hipError_t launch_mode(const FfnArgs& a, hipStream_t s, int sched, int rt,
 //   average -> stream; otherwise tiled.
 int ffn_schedule(int dtype, int T, int k, int E) {
   if (dtype != 1) return 2;
-  return ((long long)T * k <= 64LL * E) ? 0 : 1;
+  const long long tk = (long long)T * k;
+  if (tk <= 64LL * E) return 0;        // stream
+  if (tk >= 1024LL * E) return 1;      // tiled, 256-row tiles
+  return 3;                            // tiled, 128-row tiles
 }
 
 namespace {
@@ -498,7 +700,7 @@ Plan plan_of(const FfnArgs& a) {
     const int maxrows = a.T;   // a token picks an expert at most once
     p.rt = maxrows <= 16 ? 1 : (maxrows <= 32 ? 2 : 4);
   }
-  const int bm = p.sched == 1 ? TL_BM : F32_BM;
+  const int bm = p.sched == 1 ? 256 : (p.sched == 3 ? 128 : F32_BM);
   p.max_tiles = (int)((tk + bm - 1) / bm) + a.E +
                 (a.n_shared ? (a.T + bm - 1) / bm : 0);
   return p;

@@ -53,6 +53,12 @@ SMALL = [
     W("gelu_bf16_tiled_shared_drops", T=900, d_model=128, n_experts=4,
       top_k=2, d_ff=192, act="gelu", dtype="bf16", capacity=400, n_shared=1,
       seed_index=22),
+    # 256-row tiles (T*k >= 1024*E), ragged M and partial N blocks
+    W("swiglu_bm256", T=2200, d_model=128, n_experts=2, top_k=1, d_ff=384,
+      act="swiglu", dtype="bf16", capacity=0, seed_index=23),
+    W("gelu_bm256_shared_drops", T=2100, d_model=320, n_experts=2, top_k=2,
+      d_ff=384, act="gelu", dtype="bf16", capacity=2000, n_shared=1,
+      seed_index=24),
 ]
 IDS = [w.name for w in SMALL]
 
