@@ -264,30 +264,59 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
 // contiguous run of logical tiles and its L2 serves the shared slices.
 constexpr int TL_BN = 256;   // B rows per tile (SwiGLU: 128 gate + 128 up)
 constexpr int N_XCD = 8;
-#ifndef MOE_TL_WAVES
-#define MOE_TL_WAVES 8
-#endif
+// Tile configurations: many rows per expert (compute-bound) use 256-row
+// tiles with two 64-wide K stages; fewer rows (weight-streaming) use 128-row
+// tiles with six 32-wide K stages, five in flight, to keep enough weight
+// bytes in flight per CU to cover HBM latency.
+constexpr int TL_WAVES = 8;
 
-// Logical tile L -> (group, first row, n-block).  Whole workgroup; false
-// past the last tile.
-__device__ bool find_tile_n(const FfnArgs& a, int G, int BM, int NB, int L,
+// Workgroup -> (group, first row, n-block); whole workgroup of NTHR (>=
+// number of groups) threads.  Thread g takes group g's tile count
+// ceil(rows/BM) * NB; a workgroup prefix scan (wave shuffles, then wave
+// totals through LDS) gives each group's first logical tile and the total.
+// Logical tiles run group by group, n-block by n-block, m-tiles innermost.
+// Workgroups reach the 8 XCDs round-robin by id, so id p is mapped to the
+// logical tile (p % 8) * ceil(total / 8) + p / 8: each XCD gets a contiguous
+// run of the real tiles (the grid is an upper bound, a multiple of 8).
+// False for a workgroup with no tile.
+template <int NTHR>
+__device__ bool find_tile_n(const FfnArgs& a, int G, int BM, int NB,
                             int* s_info) {
-  if (threadIdx.x == 0) {
-    int acc = 0, g = 0, r0 = -1, nb = 0;
-    for (; g < G; ++g) {
-      const int rows = g < a.E ? a.offsets[g + 1] - a.offsets[g] : a.T;
-      const int nt = (rows + BM - 1) / BM;
-      const int span = nt * NB;
-      if (L < acc + span) {
-        const int r = L - acc;
-        nb = r / nt;
-        r0 = (r - nb * nt) * BM;
-        break;
-      }
-      acc += span;
-    }
-    s_info[0] = g;
-    s_info[1] = r0;
+  __shared__ int s_wsum[NTHR / 64];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  if (t == 0) s_info[1] = -1;
+  int span = 0;
+  if (t < G) {
+    const int rows = t < a.E ? a.offsets[t + 1] - a.offsets[t] : a.T;
+    span = ((rows + BM - 1) / BM) * NB;
+  }
+  int incl = span;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NTHR / 64; ++w) {
+    const int ws = s_wsum[w];
+    if (w < wave) base += ws;
+    total += ws;
+  }
+  incl += base;
+  const int excl = incl - span;
+  const int per_xcd = (total + N_XCD - 1) / N_XCD;
+  const int slot = blockIdx.x / N_XCD;
+  const int L = slot < per_xcd ? (blockIdx.x % N_XCD) * per_xcd + slot : total;
+  if (t < G && L >= excl && L < incl) {
+    const int nt = span / NB;
+    const int r = L - excl;
+    const int nb = r / nt;
+    s_info[0] = t;
+    s_info[1] = (r - nb * nt) * BM;
     s_info[2] = nb;
   }
   __syncthreads();
@@ -347,15 +376,14 @@ template <int MODE, int BM, int BK, int NS, int WAVES>
 __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
                                                                   int NB) {
   using Geo = SliceGeom<BK>;
-  constexpr int TL_WAVES = WAVES;
   constexpr int TL_THREADS = WAVES * 64;
   constexpr int WGN = WAVES / 2;      // waves along N (2 along M)
   constexpr int WM = BM / 2;          // rows per wave
   constexpr int WN = TL_BN / WGN;     // B rows per wave (128 or 64)
   constexpr int MT = WM / 32;         // 32-row MFMA tiles per wave
   constexpr int NT = WN / 32;         // 32-col MFMA tiles per wave
-  constexpr int IA = BM / Geo::RPI / TL_WAVES;      // A loads per wave, slice
-  constexpr int IB = TL_BN / Geo::RPI / TL_WAVES;   // B loads per wave, slice
+  constexpr int IA = BM / Geo::RPI / WAVES;      // A loads per wave, slice
+  constexpr int IB = TL_BN / Geo::RPI / WAVES;   // B loads per wave, slice
   constexpr int PER = IA + IB;                      // loads per wave, slice
   constexpr int D = NS - 1;                         // slices in flight
   constexpr int SA = BM * BK, SB = TL_BN * BK;      // elements per slice
@@ -364,29 +392,45 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
   // constant, so the compiler can see that the stage being loaded never
   // aliases the stage being read and does not make LDS reads wait for the
   // loads in flight.
-  static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
+  static_assert(NS >= 2 && NS <= 6, "2 to 6 stages");
   __shared__ __attribute__((aligned(16))) bf16 A0[SA];
   __shared__ __attribute__((aligned(16))) bf16 A1[SA];
   __shared__ __attribute__((aligned(16))) bf16 A2[NS > 2 ? SA : 8];
   __shared__ __attribute__((aligned(16))) bf16 A3[NS > 3 ? SA : 8];
+  __shared__ __attribute__((aligned(16))) bf16 A4[NS > 4 ? SA : 8];
+  __shared__ __attribute__((aligned(16))) bf16 A5[NS > 5 ? SA : 8];
   __shared__ __attribute__((aligned(16))) bf16 B0[SB];
   __shared__ __attribute__((aligned(16))) bf16 B1[SB];
   __shared__ __attribute__((aligned(16))) bf16 B2[NS > 2 ? SB : 8];
   __shared__ __attribute__((aligned(16))) bf16 B3[NS > 3 ? SB : 8];
+  __shared__ __attribute__((aligned(16))) bf16 B4[NS > 4 ? SB : 8];
+  __shared__ __attribute__((aligned(16))) bf16 B5[NS > 5 ? SB : 8];
   __shared__ int s_info[3];
   // stage s's arrays (s is a constant after unrolling, so each access names
   // one distinct object)
   auto As = [&](int st) -> bf16* {
-    return st == 0 ? A0 : (st == 1 ? A1 : (st == 2 ? A2 : A3));
+    switch (st) {
+      case 0: return A0;
+      case 1: return A1;
+      case 2: return A2;
+      case 3: return A3;
+      case 4: return A4;
+      default: return A5;
+    }
   };
   auto Bs = [&](int st) -> bf16* {
-    return st == 0 ? B0 : (st == 1 ? B1 : (st == 2 ? B2 : B3));
+    switch (st) {
+      case 0: return B0;
+      case 1: return B1;
+      case 2: return B2;
+      case 3: return B3;
+      case 4: return B4;
+      default: return B5;
+    }
   };
 
   const int G = a.E + a.n_shared;
-  const int per_xcd = gridDim.x / N_XCD;          // grid is a multiple of 8
-  const int L = (blockIdx.x % N_XCD) * per_xcd + blockIdx.x / N_XCD;
-  if (!find_tile_n(a, G, BM, NB, L, s_info)) return;
+  if (!find_tile_n<TL_THREADS>(a, G, BM, NB, s_info)) return;
   const int g = s_info[0], r0 = s_info[1], nb = s_info[2];
   const Group gr = group_of(g, a.offsets, a.E, a.T, a.k);
   const int N = MODE == DOWN ? a.d : a.d_ff;
@@ -578,12 +622,6 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
   }
 }
 
-#ifndef MOE_TL_BK
-#define MOE_TL_BK 64
-#endif
-#ifndef MOE_TL_NS
-#define MOE_TL_NS 2
-#endif
 
 // ===========================================================================
 // float32 schedule
@@ -662,11 +700,11 @@ hipError_t launch_mode(const FfnArgs& a, hipStream_t s, int sched, int rt,
     long long tiles = (long long)max_tiles * NB;
     tiles = (tiles + N_XCD - 1) / N_XCD * N_XCD;
     if (sched == 1)
-      ffn_tiled_kernel<MODE, 256, MOE_TL_BK, MOE_TL_NS, MOE_TL_WAVES>
-          <<<(unsigned)tiles, MOE_TL_WAVES * 64, 0, s>>>(a, NB);
+      ffn_tiled_kernel<MODE, 256, 64, 2, TL_WAVES>
+          <<<(unsigned)tiles, TL_WAVES * 64, 0, s>>>(a, NB);
     else
-      ffn_tiled_kernel<MODE, 128, MOE_TL_BK, MOE_TL_NS, MOE_TL_WAVES>
-          <<<(unsigned)tiles, MOE_TL_WAVES * 64, 0, s>>>(a, NB);
+      ffn_tiled_kernel<MODE, 128, 32, 6, TL_WAVES>
+          <<<(unsigned)tiles, TL_WAVES * 64, 0, s>>>(a, NB);
   } else {
     dim3 grid(max_tiles, (N + F32_BN - 1) / F32_BN);
     ffn_f32_kernel<MODE><<<grid, 256, 0, s>>>(a);
