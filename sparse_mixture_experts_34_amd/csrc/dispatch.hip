@@ -92,48 +92,92 @@ __device__ __forceinline__ void scatter_chunk(
   }
 }
 
-// Scan over chunks and experts; executed by one 256-thread workgroup.
+// Scan over chunks and experts, executed by one workgroup of NTHR threads.
 // chunk[c*E + e] holds per-chunk counts on entry and chunk base ranks on
 // exit.  Writes counts, offsets, n_dropped, prob mean and aux.
+//
+// Each expert gets TPE = NTHR / E (a power of two) threads: thread j scans a
+// contiguous range of chunks and sums an interleaved share of the
+// probability partial rows; the TPE pieces are combined in the fixed order
+// j = 0, 1, ... (deterministic).  red_* hold NTHR entries.
+template <int NTHR>
 __device__ void scan_all(int* chunk, int nchunks, const DispatchArgs& a,
                          int32_t* offsets_out, int* red_i, float* red_f) {
-  const int e = threadIdx.x;
+  const int t = threadIdx.x;
   const int E = a.E;
-  int count = 0;
-  if (e < E) {
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = chunk[c * E + e];
-      chunk[c * E + e] = count;
+  int tpe = 1;
+  while (tpe * 2 * E <= NTHR) tpe *= 2;
+  const int e = t / tpe, j = t % tpe;
+  const bool act = e < E;
+  // ---- per-chunk counts -> chunk base ranks, per-expert totals ----------
+  const int cpt = (nchunks + tpe - 1) / tpe;
+  const int c0 = min(j * cpt, nchunks), c1 = min(c0 + cpt, nchunks);
+  int local = 0;
+  if (act) {
+#pragma unroll 8
+    for (int c = c0; c < c1; ++c) local += chunk[c * E + e];
+  }
+  red_i[t] = local;
+  __syncthreads();
+  int base = 0, count = 0;
+  if (act) {
+    for (int jj = 0; jj < tpe; ++jj) {
+      const int v = red_i[e * tpe + jj];
+      if (jj < j) base += v;
       count += v;
     }
+    int run = base;
+    for (int c = c0; c < c1; ++c) {
+      const int v = chunk[c * E + e];
+      chunk[c * E + e] = run;
+      run += v;
+    }
   }
-  int kept = (e < E) ? (a.capacity > 0 ? min(count, a.capacity) : count) : 0;
-  // exclusive scan of kept over the (<= 256) experts
-  red_i[e] = kept;
+  __syncthreads();
+  // ---- kept counts, exclusive scan over experts --------------------------
+  const int kept_e = (act && j == 0)
+                         ? (a.capacity > 0 ? min(count, a.capacity) : count)
+                         : 0;
+  if (t < 256) red_i[t] = 0;
+  __syncthreads();
+  if (act && j == 0) red_i[e] = kept_e;
   __syncthreads();
   for (int o = 1; o < 256; o <<= 1) {
-    int v = (e >= o) ? red_i[e - o] : 0;
+    int v = (t < 256 && t >= o) ? red_i[t - o] : 0;
     __syncthreads();
-    red_i[e] += v;
+    if (t < 256) red_i[t] += v;
     __syncthreads();
   }
-  const int incl = red_i[e];
-  if (e < E) {
+  if (act && j == 0) {
+    const int incl = red_i[e];
     a.counts[e] = count;
-    offsets_out[e] = incl - kept;
+    offsets_out[e] = incl - kept_e;
     if (e == E - 1) {
       offsets_out[E] = incl;
       *a.n_dropped = (int32_t)((long long)a.T * a.k - incl);
     }
   }
-  // probability mean and aux loss
+  // ---- probability mean (fixed-order sums) and aux loss ------------------
+  float pm_part = 0.f;
+  if (act && a.partials) {
+    float accs[4] = {0.f, 0.f, 0.f, 0.f};
+    int q = 0;
+#pragma unroll 4
+    for (int b = j; b < a.n_partials; b += tpe) {
+      accs[q & 3] += a.partials[(size_t)b * E + e];
+      ++q;
+    }
+    pm_part = (accs[0] + accs[1]) + (accs[2] + accs[3]);
+  }
+  __syncthreads();
+  red_f[t] = pm_part;
+  __syncthreads();
   float term = 0.f;
-  if (e < E) {
+  if (act && j == 0) {
     float pm;
     if (a.partials) {
       float v = 0.f;
-#pragma unroll 8
-      for (int b = 0; b < a.n_partials; ++b) v += a.partials[(size_t)b * E + e];
+      for (int jj = 0; jj < tpe; ++jj) v += red_f[e * tpe + jj];
       pm = v / (float)a.T;
       if (a.prob_mean_out) a.prob_mean_out[e] = pm;
     } else {
@@ -141,13 +185,16 @@ __device__ void scan_all(int* chunk, int nchunks, const DispatchArgs& a,
     }
     term = ((float)count / (float)a.T) * pm;
   }
-  red_f[e] = term;
+  __syncthreads();
+  if (t < 256) red_f[t] = 0.f;
+  __syncthreads();
+  if (act && j == 0) red_f[e] = term;
   __syncthreads();
   for (int o = 128; o >= 1; o >>= 1) {
-    if (e < o) red_f[e] += red_f[e + o];
+    if (t < o) red_f[t] += red_f[t + o];
     __syncthreads();
   }
-  if (e == 0 && a.aux) *a.aux = a.aux_coef * (float)E * red_f[0];
+  if (t == 0 && a.aux) *a.aux = a.aux_coef * (float)E * red_f[0];
 }
 
 __global__ __launch_bounds__(DW * 64) void dispatch_count_kernel(
@@ -164,11 +211,13 @@ __global__ __launch_bounds__(DW * 64) void dispatch_count_kernel(
     for (int e = lane; e < E; e += 64) chunk_ws[(size_t)c * E + e] = hist[wave][e];
 }
 
-__global__ __launch_bounds__(256) void dispatch_scan_kernel(DispatchArgs a,
-                                                            int nchunks) {
-  __shared__ int red_i[256];
-  __shared__ float red_f[256];
-  scan_all(a.chunk_ws, nchunks, a, a.offsets, red_i, red_f);
+constexpr int SCAN_THREADS = 1024;
+
+__global__ __launch_bounds__(SCAN_THREADS) void dispatch_scan_kernel(
+    DispatchArgs a, int nchunks) {
+  __shared__ int red_i[SCAN_THREADS];
+  __shared__ float red_f[SCAN_THREADS];
+  scan_all<SCAN_THREADS>(a.chunk_ws, nchunks, a, a.offsets, red_i, red_f);
 }
 
 __global__ __launch_bounds__(DW * 64) void dispatch_scatter_kernel(
@@ -198,7 +247,7 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(DispatchArgs a,
   __syncthreads();
   if (wave < nchunks) count_chunk(a.idx, tk, a.E, wave, chunk + wave * a.E, lane);
   __syncthreads();
-  scan_all(chunk, nchunks, a, offs, red_i, red_f);
+  scan_all<256>(chunk, nchunks, a, offs, red_i, red_f);
   __syncthreads();
   for (int e = threadIdx.x; e <= a.E; e += 256) a.offsets[e] = offs[e];
   if (wave < nchunks)
@@ -223,7 +272,7 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   const int blocks = (nchunks + DW - 1) / DW;
   dispatch_count_kernel<<<blocks, DW * 64, 0, s>>>(a.idx, tk, nchunks, a.E,
                                                    a.chunk_ws);
-  dispatch_scan_kernel<<<1, 256, 0, s>>>(a, nchunks);
+  dispatch_scan_kernel<<<1, SCAN_THREADS, 0, s>>>(a, nchunks);
   dispatch_scatter_kernel<<<blocks, DW * 64, 0, s>>>(a, nchunks);
   return hipGetLastError();
 }

@@ -10,11 +10,11 @@ namespace moe {
 
 // Route-select: 4 waves per workgroup, route_tpw(T) tokens per wave (one
 // token per wave for small batches, up to 16 for large ones, so that about
-// 256 workgroups cover the batch).  A workgroup writes one row of
+// 512 workgroups cover the batch).  A workgroup writes one row of
 // probability partial sums.
 constexpr int ROUTE_WAVES = 4;
 inline int route_tpw(int T) {
-  const int t = (T + 1023) / 1024;
+  const int t = (T + 2047) / 2048;
   return t < 1 ? 1 : (t > 16 ? 16 : t);
 }
 inline int route_blocks(int T) {

@@ -188,8 +188,11 @@ __global__ __launch_bounds__(RL_THREADS) void router_logits_kernel(
 }
 
 constexpr int RS_WAVES = ROUTE_WAVES;
-constexpr int RS_MAXC = 4;   // experts per lane: E <= 256
 
+// MAXC experts per lane (E <= 64*MAXC), KSM = largest K split, PF: load the
+// next token's partial logits while the current token is processed (used
+// when a wave handles several tokens; the K split is then at most 2).
+template <int MAXC, int KSM, bool PF>
 __global__ __launch_bounds__(RS_WAVES * 64) void route_select_kernel(
     const float* __restrict__ part, int ksplit,
     const float* __restrict__ router_bias,
@@ -199,30 +202,46 @@ __global__ __launch_bounds__(RS_WAVES * 64) void route_select_kernel(
   __shared__ float psum_s[RS_WAVES][256];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  float psum[RS_MAXC];
+  float psum[MAXC];
 #pragma unroll
-  for (int c = 0; c < RS_MAXC; ++c) psum[c] = 0.f;
+  for (int c = 0; c < MAXC; ++c) psum[c] = 0.f;
 
   const int tbeg = (blockIdx.x * RS_WAVES + wave) * tpw;
+  const int tend = min(tbeg + tpw, T);
+  constexpr int NB = PF ? 2 : 1;
+  float pv[NB][MAXC][KSM];
+  auto fetch = [&](int t, int buf) {
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const int e = lane + 64 * c;
+#pragma unroll
+      for (int s = 0; s < KSM; ++s)
+        pv[buf][c][s] = (e < E && s < ksplit)
+                            ? part[((size_t)s * T + t) * E + e] : 0.f;
+    }
+  };
+  if (PF && tbeg < tend) fetch(tbeg, 0);
   for (int i = 0; i < tpw; ++i) {
     const int t = tbeg + i;
-    if (t >= T) break;   // wave-uniform
-    float l[RS_MAXC], key[RS_MAXC];
+    if (t >= tend) break;   // wave-uniform
+    const int cur = PF ? (i & 1) : 0;
+    if (PF) {
+      if (t + 1 < tend) fetch(t + 1, cur ^ 1);
+    } else {
+      fetch(t, 0);
+    }
+    float l[MAXC], key[MAXC];
 #pragma unroll
-    for (int c = 0; c < RS_MAXC; ++c) {
+    for (int c = 0; c < MAXC; ++c) {
       const int e = lane + 64 * c;
       l[c] = -INFINITY;
       key[c] = -INFINITY;
       if (e < E) {
-        // independent loads of the K-slice partial sums, added in order
-        float pv[ROUTER_MAX_KSPLIT];
+        // K-slice partial sums added in slice order
+        float v = pv[cur][c][0];
 #pragma unroll
-        for (int s = 0; s < ROUTER_MAX_KSPLIT; ++s)
-          pv[s] = s < ksplit ? part[((size_t)s * T + t) * E + e] : 0.f;
-        float v = pv[0];
-#pragma unroll
-        for (int s = 1; s < ROUTER_MAX_KSPLIT; ++s)
-          if (s < ksplit) v += pv[s];
+        for (int s = 1; s < KSM; ++s)
+          if (s < ksplit) v += pv[cur][c][s];
         if (router_bias) v += router_bias[e];
         l[c] = v;
         key[c] = select_bias ? v + select_bias[e] : v;
@@ -231,11 +250,11 @@ __global__ __launch_bounds__(RS_WAVES * 64) void route_select_kernel(
     }
     float m = -INFINITY;
 #pragma unroll
-    for (int c = 0; c < RS_MAXC; ++c) m = fmaxf(m, l[c]);
+    for (int c = 0; c < MAXC; ++c) m = fmaxf(m, l[c]);
     m = wave_max(m);
-    float ex[RS_MAXC], se = 0.f;
+    float ex[MAXC], se = 0.f;
 #pragma unroll
-    for (int c = 0; c < RS_MAXC; ++c) {
+    for (int c = 0; c < MAXC; ++c) {
       const int e = lane + 64 * c;
       ex[c] = (e < E) ? __expf(l[c] - m) : 0.f;
       se += ex[c];
@@ -243,20 +262,20 @@ __global__ __launch_bounds__(RS_WAVES * 64) void route_select_kernel(
     se = wave_sum(se);
     const float inv = 1.0f / se;
 #pragma unroll
-    for (int c = 0; c < RS_MAXC; ++c) psum[c] += ex[c] * inv;
+    for (int c = 0; c < MAXC; ++c) psum[c] += ex[c] * inv;
 
     // k rounds of wave argmax on (key desc, index asc); lane j keeps the
     // winner of round j (slot j) and its logit.
-    bool taken[RS_MAXC];
+    bool taken[MAXC];
 #pragma unroll
-    for (int c = 0; c < RS_MAXC; ++c) taken[c] = (lane + 64 * c) >= E;
+    for (int c = 0; c < MAXC; ++c) taken[c] = (lane + 64 * c) >= E;
     int my_idx = 0;
     float my_l = -INFINITY;
     for (int j = 0; j < k; ++j) {
       float bk = -INFINITY, bl = -INFINITY;
       int bi = 0x7fffffff;
 #pragma unroll
-      for (int c = 0; c < RS_MAXC; ++c) {
+      for (int c = 0; c < MAXC; ++c) {
         // indices rise with c: strict > keeps the lower index on ties
         if (!taken[c] && (bi == 0x7fffffff || key[c] > bk)) {
           bk = key[c];
@@ -279,7 +298,7 @@ __global__ __launch_bounds__(RS_WAVES * 64) void route_select_kernel(
       }
       // every lane now holds the same winner
 #pragma unroll
-      for (int c = 0; c < RS_MAXC; ++c)
+      for (int c = 0; c < MAXC; ++c)
         if (lane + 64 * c == bi) taken[c] = true;
       if (lane == j) {
         my_idx = bi;
@@ -297,11 +316,9 @@ __global__ __launch_bounds__(RS_WAVES * 64) void route_select_kernel(
     }
   }
   // per-block probability partial sums, waves added in order 0..3
+  for (int e = lane; e < 256; e += 64) psum_s[wave][e] = 0.f;
 #pragma unroll
-  for (int c = 0; c < RS_MAXC; ++c) {
-    const int e = lane + 64 * c;
-    if (e < 256) psum_s[wave][e] = psum[c];
-  }
+  for (int c = 0; c < MAXC; ++c) psum_s[wave][lane + 64 * c] = psum[c];
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     float v = psum_s[0][e];
@@ -325,17 +342,26 @@ __global__ void prob_mean_kernel(const float* __restrict__ partials,
 
 }  // namespace
 
-// Number of K slices for the router GEMM: enough workgroups to cover the
-// chip when T is small, each slice a multiple of 256 (4 waves x 64).
+// Number of K slices for the router GEMM: each slice a whole number of
+// 64-wide steps (at least 4, one per wave), the largest split up to
+// ROUTER_MAX_KSPLIT that keeps the grid within about 1024 workgroups, so
+// that small batches and wide routers still fill the chip with independent
+// load chains.
 int router_ksplit(int T, int d, int E, int dtype) {
   const int tt = dtype == 1 ? 64 : 16;
   const long long blocks = (long long)((T + tt - 1) / tt) *
                            ((E + RL_EXP_TILE - 1) / RL_EXP_TILE);
-  int ks = 1;
-  while (blocks * ks * 2 <= 256 && ks * 2 <= ROUTER_MAX_KSPLIT &&
-         d % (ks * 2 * 256) == 0)
-    ks *= 2;
-  return ks;
+  const int steps = d / RL_KSTEP;
+  // a wave of the select kernel that handles several tokens sums at most
+  // two slices per token
+  const int kmax = route_tpw(T) > 1 ? 2 : ROUTER_MAX_KSPLIT;
+  int best = 1;
+  for (int ks = 2; ks <= kmax; ++ks) {
+    if (steps % ks != 0 || steps / ks < 4) continue;
+    if (blocks * ks > 1024) break;
+    best = ks;
+  }
+  return best;
 }
 
 hipError_t launch_router_logits_partial(int dtype, const void* x,
@@ -360,9 +386,23 @@ hipError_t launch_route_select_from(const float* part, int ksplit,
                                     int32_t* idx, float* gate,
                                     float* partials, int T, int E, int k,
                                     hipStream_t s) {
-  route_select_kernel<<<route_blocks(T), RS_WAVES * 64, 0, s>>>(
-      part, ksplit, router_bias, select_bias, logits, idx, gate, partials, T,
-      E, k, route_tpw(T));
+  const int tpw = route_tpw(T);
+  const dim3 grid(route_blocks(T)), block(RS_WAVES * 64);
+#define MOE_SELECT(C, KS, PF)                                                 \
+  route_select_kernel<C, KS, PF><<<grid, block, 0, s>>>(                      \
+      part, ksplit, router_bias, select_bias, logits, idx, gate, partials, T, \
+      E, k, tpw)
+  const int mc = (E + 63) / 64;
+  if (tpw > 1) {   // several tokens per wave: K split <= 2, prefetch
+    if (mc == 1) MOE_SELECT(1, 2, true);
+    else if (mc == 2) MOE_SELECT(2, 2, true);
+    else MOE_SELECT(4, 2, true);
+  } else {
+    if (mc == 1) MOE_SELECT(1, ROUTER_MAX_KSPLIT, false);
+    else if (mc == 2) MOE_SELECT(2, ROUTER_MAX_KSPLIT, false);
+    else MOE_SELECT(4, ROUTER_MAX_KSPLIT, false);
+  }
+#undef MOE_SELECT
   return hipGetLastError();
 }
 
