@@ -48,16 +48,23 @@ def parse():
     ap.add_argument("--workload", default="mixtral_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=None)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the benchmark, run a plain device-to-device "
+                    "copy of this many MiB three times (a known-size "
+                    "reference for the profiler's HBM byte counters)")
     return ap.parse_args()
+
+
+# the sources the expert GEMM kernels are compiled from
+GEMM_SOURCES = ("common.hpp", "kernels.hpp", "ffn.hip")
 
 
 def kernel_sources_digest() -> str:
     d = os.path.join(ROOT, "sparse_mixture_experts_34_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".hpp")):
-            h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
+    for f in GEMM_SOURCES:
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -241,6 +248,20 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_tokens)
     print(json.dumps(res), flush=True)
+    if args.copy_calibration_mib > 0:
+        copy_calibration(args.copy_calibration_mib)
+
+
+def copy_calibration(mib):
+    """A plain copy of known size: reads and writes mib MiB per launch."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4}), flush=True)
 
 
 def kept_total_rows(kept_total, wl):
