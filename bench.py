@@ -104,27 +104,46 @@ def main():
     T, E, k, d, f = wl.T, wl.n_experts, wl.top_k, wl.d_model, wl.d_ff
     rows = T * k + wl.n_shared * T
     dt = wl.torch_dtype
-    W = moe.expert_weights(inp)
+    # Two copies of the expert weights, used on alternate steps: a step's
+    # weights were last read two steps earlier, with the other copy read in
+    # between, so the 256 MB memory-side cache gives no reuse across steps.
+    wnames = [n for n in synth.weight_shapes(wl) if n != "w_router"]
+    inp_b = dict(inp)
+    for n in wnames:
+        inp_b[n] = inp[n].clone()
+    Ws = [moe.expert_weights(inp), moe.expert_weights(inp_b)]
+    W = Ws[0]
 
     out = torch.empty_like(inp["x"])
     aux = torch.empty(1, dtype=torch.float32, device=dev)
     counts = torch.empty(E, dtype=torch.int32, device=dev)
     nd = torch.empty(1, dtype=torch.int32, device=dev)
 
-    def step():
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record()
         moe.moe_layer_forward(p, inp["x"], inp["w_router"],
-                              inp["router_bias"], inp["select_bias"], W, out,
-                              aux, counts, nd, None, ws)
+                              inp["router_bias"], inp["select_bias"],
+                              Ws[i & 1], out, aux, counts, nd, None, ws)
+        if ev is not None:
+            ev[1].record()
 
     # ---- headline pass: K whole-layer calls ------------------------------
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(i)
     torch.cuda.synchronize()
     t_step = (time.perf_counter() - t0) / args.steps
+    # per-step spread: a second pass with HIP events around every call
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, sev[i])
+    torch.cuda.synchronize()
+    st = np.array([e[0].elapsed_time(e[1]) for e in sev])
 
     cnt = counts.cpu().tolist()
     n_dropped = int(nd.item())
@@ -145,7 +164,8 @@ def main():
     out2 = torch.empty_like(out)
     names = ["route", "dispatch", "expert_up", "expert_down", "combine"]
 
-    def step_parts(ev):
+    def step_parts(ev, i):
+        W = Ws[i & 1]
         ev[0].record()
         moe.moe_route(p, inp["x"], inp["w_router"], inp["router_bias"],
                       inp["select_bias"], logits, idx, gate, pm, ws)
@@ -161,12 +181,12 @@ def main():
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)]
            for _ in range(args.steps)]
-    for _ in range(args.warmup):
-        step_parts(evs[0])
+    for i in range(args.warmup):
+        step_parts(evs[0], i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step_parts(evs[i])
+        step_parts(evs[i], i)
     torch.cuda.synchronize()
     t_parts = (time.perf_counter() - t0) / args.steps
     per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
@@ -237,6 +257,11 @@ def main():
             "bound": "mfma" if F / PEAK_BF16 > B / PEAK_HBM else "hbm"},
         "kernels_us": {n: round(v * 1e6, 2) for n, v in per.items()},
         "parts_ms_per_step": round(t_parts * 1e3, 4),
+        "step_ms_percentiles": {
+            "p10": round(float(np.percentile(st, 10)), 4),
+            "p50": round(float(np.percentile(st, 50)), 4),
+            "p90": round(float(np.percentile(st, 90)), 4)},
+        "weight_copies": 2,
         "parts_match_layer_output": same,
         "routing": {"counts": cnt, "touched_experts": touched - wl.n_shared,
                     "n_dropped": n_dropped,
@@ -246,7 +271,8 @@ def main():
                     "aux_loss": float(aux.item())},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_tokens)
+        res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_tokens,
+                                           gpu_idx=idx.cpu().numpy())
     print(json.dumps(res), flush=True)
     if args.copy_calibration_mib > 0:
         copy_calibration(args.copy_calibration_mib)
@@ -268,11 +294,12 @@ def kept_total_rows(kept_total, wl):
     return kept_total + wl.n_shared * wl.T
 
 
-def cpu_baseline(wl, inp, n_tokens=None):
+def cpu_baseline(wl, inp, n_tokens=None, gpu_idx=None):
     """The CPU oracle (float64, numpy/OpenBLAS) on a bounded sample: routing
     and capacity dispatch over the whole batch plus the expert FFNs and
     combine of a token sample.  Weights are copied to host memory before
-    the clock starts."""
+    the clock starts.  With ``gpu_idx``, also counts the tokens whose
+    selected experts differ from the oracle's (expected 0)."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info
@@ -289,6 +316,9 @@ def cpu_baseline(wl, inp, n_tokens=None):
     # route once (untimed) to find the experts the sample needs
     r = oracle.route(x, wr, wl.top_k, rb, sb)
     need = sorted(set(int(e) for e in r["idx"][tokens].ravel()))
+    flips = None
+    if gpu_idx is not None:
+        flips = int((np.asarray(gpu_idx) != r["idx"]).any(axis=1).sum())
     names = (["w1", "b1", "w2", "b2"] if wl.act == "gelu"
              else ["w_gate", "w_up", "w_down"])
     w = {}
@@ -310,6 +340,7 @@ def cpu_baseline(wl, inp, n_tokens=None):
                   or [1])
     return {"value": round(n / dt, 4), "unit": "tokens/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 3),
+            "routing_flips_vs_gpu": flips,
             "sample": f"{n} of {wl.T} tokens: float64 routing + capacity "
                       f"dispatch over all {wl.T} tokens, expert FFNs and "
                       f"combine for the {n} sampled tokens"}
