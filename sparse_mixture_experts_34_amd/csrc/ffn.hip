@@ -19,15 +19,15 @@
 //   down  Y[r, n]  = H[r,:] . W2[g, n, :] (+ b2)
 //
 // Two bf16 schedules, picked on the host from the shapes only:
-//   stream  few rows per expert (decode): a workgroup owns 16 output
+//   stream  few rows per expert (decode): a workgroup owns 32 output
 //           columns, its waves split K, and each streams its weight rows
 //           once from HBM straight into MFMA B registers (16x16x32) with a
-//           4-deep register prefetch ring; the handful of token rows ride
+//           3-deep register prefetch ring; the handful of token rows ride
 //           along as the A operand; partial sums meet in LDS.
-//   tiled   many rows per expert (prefill): 128x128 workgroup tiles, BK=64,
-//           A and B staged through XOR-swizzled LDS with double buffering,
-//           32x32x16 MFMAs, the activation fused into the epilogue, and the
-//           output tile staged through LDS for 16-byte row stores.
+//   tiled   many rows per expert (prefill): 256- or 128-row by 256-column
+//           workgroup tiles, A and B loaded straight into XOR-swizzled LDS
+//           stages, 32x32x16 MFMAs, the activation fused into the epilogue,
+//           and the output tile staged through LDS for 16-byte row stores.
 // float32 problems use a plain float32 kernel (same grouping).
 #include "common.hpp"
 #include "kernels.hpp"
@@ -95,25 +95,27 @@ __device__ __forceinline__ void group_weights(const FfnArgs& a, int g,
 // ===========================================================================
 // stream schedule (bf16)
 // ===========================================================================
-// A workgroup owns 16 output columns of one group; its 4 waves split the K
-// steps into contiguous quarters, stream their weight rows straight into
-// MFMA B registers (4-deep prefetch ring) and add their partial sums through
-// LDS in the fixed order 0,1,2,3.
+// A workgroup owns 32 output columns (two groups of 16) of one group; its 4
+// waves split the K steps into contiguous quarters, stream their weight rows
+// straight into MFMA B registers (3-deep prefetch ring) and add their
+// partial sums through LDS in the fixed order 0,1,2,3.  Two column groups
+// per workgroup halve the token-row (A) reads per weight byte.
 constexpr int ST_WAVES = 4;
-constexpr int ST_COLS = 16;          // output columns per workgroup
+constexpr int ST_CG = 2;             // 16-column groups per workgroup
+constexpr int ST_COLS = 16 * ST_CG;  // output columns per workgroup
 constexpr int ST_KSTEP = 64;         // K per step (two 16x16x32 MFMAs)
-constexpr int ST_PF = 4;             // prefetch ring depth (steps)
+constexpr int ST_PF = 3;             // prefetch ring depth (steps)
 
 template <int NMAT, int RT>
 struct StreamBuf {
-  u32x4 b[NMAT][2];   // 16 bf16 of one weight row per matrix
-  u32x4 a[RT][2];     // 16 bf16 of one token row per row tile
+  u32x4 b[NMAT][ST_CG][2];   // 16 bf16 of one weight row per matrix, group
+  u32x4 a[RT][2];            // 16 bf16 of one token row per row tile
 };
 
 template <int MODE, int RT>
 __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
   constexpr int NMAT = MODE == UP_SWIGLU ? 2 : 1;
-  __shared__ f32x4 red[ST_WAVES - 1][NMAT * RT][64];
+  __shared__ f32x4 red[ST_WAVES - 1][NMAT * ST_CG * RT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = blockIdx.y;
   const Group gr = group_of(g, a.offsets, a.E, a.T, a.k);
@@ -132,9 +134,14 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
   const int s_beg = wave * nsteps / ST_WAVES;
   const int my_steps = (wave + 1) * nsteps / ST_WAVES - s_beg;
   const int koff = s_beg * ST_KSTEP + kq * 16;
-  const bf16* brow[NMAT];
+  // weight row of column group c; a partial last group re-reads row N-1
+  // and stores nothing for it
+  const bf16* brow[NMAT][ST_CG];
 #pragma unroll
-  for (int m = 0; m < NMAT; ++m) brow[m] = wm[m] + (size_t)(n0 + col) * K + koff;
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int c = 0; c < ST_CG; ++c)
+      brow[m][c] = wm[m] + (size_t)min(n0 + 16 * c + col, N - 1) * K + koff;
 
   for (int rg = 0; rg < gr.rows; rg += RT * 16) {
     const int ntile = min(RT, (gr.rows - rg + 15) >> 4);
@@ -144,20 +151,24 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
       const int i = min(rg + t * 16 + col, gr.rows - 1);
       arow[t] = a_row<MODE, bf16>(a, gr, i, K) + koff;
     }
-    f32x4 acc[NMAT][RT];
+    f32x4 acc[NMAT][ST_CG][RT];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-      for (int t = 0; t < RT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < ST_CG; ++c)
+#pragma unroll
+        for (int t = 0; t < RT; ++t) acc[m][c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     StreamBuf<NMAT, RT> buf[ST_PF];
     auto load = [&](StreamBuf<NMAT, RT>& b, int s) {
       const int k0 = s * ST_KSTEP;
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) {
-        b.b[m][0] = ldg16(brow[m] + k0);
-        b.b[m][1] = ldg16(brow[m] + k0 + 8);
-      }
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int c = 0; c < ST_CG; ++c) {
+          b.b[m][c][0] = ldg16(brow[m][c] + k0);
+          b.b[m][c][1] = ldg16(brow[m][c] + k0 + 8);
+        }
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         if (t < ntile) {
@@ -175,11 +186,14 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
             V16 av;
             av.u = b.a[t][h];
 #pragma unroll
-            for (int m = 0; m < NMAT; ++m) {
-              V16 bv;
-              bv.u = b.b[m][h];
-              acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av.h, bv.h, acc[m][t], 0, 0, 0);
-            }
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+              for (int c = 0; c < ST_CG; ++c) {
+                V16 bv;
+                bv.u = b.b[m][c][h];
+                acc[m][c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    av.h, bv.h, acc[m][c][t], 0, 0, 0);
+              }
           }
         }
       }
@@ -203,7 +217,10 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int t = 0; t < RT; ++t) red[wave - 1][m * RT + t][lane] = acc[m][t];
+        for (int c = 0; c < ST_CG; ++c)
+#pragma unroll
+          for (int t = 0; t < RT; ++t)
+            red[wave - 1][(m * ST_CG + c) * RT + t][lane] = acc[m][c][t];
     }
     __syncthreads();
     if (wave == 0) {
@@ -212,24 +229,32 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-          for (int t = 0; t < RT; ++t) acc[m][t] += red[w][m * RT + t][lane];
-      // epilogue: lane holds column n0+col, rows rg + 16t + 4*kq + r
-      const int n = n0 + col;
-      float bias = 0.f;
-      if (MODE != UP_SWIGLU && biasv) bias = (float)((const bf16*)biasv)[n];
+          for (int c = 0; c < ST_CG; ++c)
+#pragma unroll
+            for (int t = 0; t < RT; ++t)
+              acc[m][c][t] += red[w][(m * ST_CG + c) * RT + t][lane];
+      // epilogue: lane holds column n0+16c+col, rows rg + 16t + 4*kq + r
       bf16* outp = (bf16*)(MODE == DOWN ? a.y : a.h);
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        if (t < ntile) {
+      for (int c = 0; c < ST_CG; ++c) {
+        const int n = n0 + 16 * c + col;
+        if (n >= N) continue;
+        float bias = 0.f;
+        if (MODE != UP_SWIGLU && biasv) bias = (float)((const bf16*)biasv)[n];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = rg + t * 16 + kq * 4 + r;
-            if (i < gr.rows) {
-              float v;
-              if (MODE == UP_SWIGLU) v = silu(acc[0][t][r]) * acc[NMAT - 1][t][r];
-              else if (MODE == UP_GELU) v = gelu_erf(acc[0][t][r] + bias);
-              else v = acc[0][t][r] + bias;
-              outp[(size_t)(gr.out0 + i) * N + n] = (bf16)v;
+        for (int t = 0; t < RT; ++t) {
+          if (t < ntile) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int i = rg + t * 16 + kq * 4 + r;
+              if (i < gr.rows) {
+                float v;
+                if (MODE == UP_SWIGLU)
+                  v = silu(acc[0][c][t][r]) * acc[NMAT - 1][c][t][r];
+                else if (MODE == UP_GELU) v = gelu_erf(acc[0][c][t][r] + bias);
+                else v = acc[0][c][t][r] + bias;
+                outp[(size_t)(gr.out0 + i) * N + n] = (bf16)v;
+              }
             }
           }
         }
