@@ -101,28 +101,27 @@ __device__ __forceinline__ void group_weights(const FfnArgs& a, int g,
 // partial sums through LDS in the fixed order 0,1,2,3.  Two column groups
 // per workgroup halve the token-row (A) reads per weight byte.
 constexpr int ST_WAVES = 4;
-constexpr int ST_CG = 2;             // 16-column groups per workgroup
-constexpr int ST_COLS = 16 * ST_CG;  // output columns per workgroup
 constexpr int ST_KSTEP = 64;         // K per step (two 16x16x32 MFMAs)
 constexpr int ST_PF = 3;             // prefetch ring depth (steps)
 
-template <int NMAT, int RT>
+template <int NMAT, int RT, int CG>
 struct StreamBuf {
-  u32x4 b[NMAT][ST_CG][2];   // 16 bf16 of one weight row per matrix, group
+  u32x4 b[NMAT][CG][2];      // 16 bf16 of one weight row per matrix, group
   u32x4 a[RT][2];            // 16 bf16 of one token row per row tile
 };
 
-template <int MODE, int RT>
+// CG = 16-column groups per workgroup.
+template <int MODE, int RT, int CG>
 __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
   constexpr int NMAT = MODE == UP_SWIGLU ? 2 : 1;
-  __shared__ f32x4 red[ST_WAVES - 1][NMAT * ST_CG * RT][64];
+  __shared__ f32x4 red[ST_WAVES - 1][NMAT * CG * RT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = blockIdx.y;
   const Group gr = group_of(g, a.offsets, a.E, a.T, a.k);
   if (gr.rows <= 0) return;                 // uniform over the workgroup
   const int N = MODE == DOWN ? a.d : a.d_ff;
   const int K = MODE == DOWN ? a.d_ff : a.d;
-  const int n0 = blockIdx.x * ST_COLS;
+  const int n0 = blockIdx.x * 16 * CG;
   if (n0 >= N) return;                      // uniform over the workgroup
   const void *w0v, *w1v, *biasv;
   group_weights<MODE>(a, g, gr.shared, N, K, w0v, w1v, biasv);
@@ -136,11 +135,11 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
   const int koff = s_beg * ST_KSTEP + kq * 16;
   // weight row of column group c; a partial last group re-reads row N-1
   // and stores nothing for it
-  const bf16* brow[NMAT][ST_CG];
+  const bf16* brow[NMAT][CG];
 #pragma unroll
   for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-    for (int c = 0; c < ST_CG; ++c)
+    for (int c = 0; c < CG; ++c)
       brow[m][c] = wm[m] + (size_t)min(n0 + 16 * c + col, N - 1) * K + koff;
 
   for (int rg = 0; rg < gr.rows; rg += RT * 16) {
@@ -151,21 +150,21 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
       const int i = min(rg + t * 16 + col, gr.rows - 1);
       arow[t] = a_row<MODE, bf16>(a, gr, i, K) + koff;
     }
-    f32x4 acc[NMAT][ST_CG][RT];
+    f32x4 acc[NMAT][CG][RT];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-      for (int c = 0; c < ST_CG; ++c)
+      for (int c = 0; c < CG; ++c)
 #pragma unroll
         for (int t = 0; t < RT; ++t) acc[m][c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    StreamBuf<NMAT, RT> buf[ST_PF];
-    auto load = [&](StreamBuf<NMAT, RT>& b, int s) {
+    StreamBuf<NMAT, RT, CG> buf[ST_PF];
+    auto load = [&](StreamBuf<NMAT, RT, CG>& b, int s) {
       const int k0 = s * ST_KSTEP;
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int c = 0; c < ST_CG; ++c) {
+        for (int c = 0; c < CG; ++c) {
           b.b[m][c][0] = ldg16(brow[m][c] + k0);
           b.b[m][c][1] = ldg16(brow[m][c] + k0 + 8);
         }
@@ -177,7 +176,7 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
         }
       }
     };
-    auto compute = [&](const StreamBuf<NMAT, RT>& b) {
+    auto compute = [&](const StreamBuf<NMAT, RT, CG>& b) {
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         if (t < ntile) {
@@ -188,7 +187,7 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-              for (int c = 0; c < ST_CG; ++c) {
+              for (int c = 0; c < CG; ++c) {
                 V16 bv;
                 bv.u = b.b[m][c][h];
                 acc[m][c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -217,10 +216,10 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int c = 0; c < ST_CG; ++c)
+        for (int c = 0; c < CG; ++c)
 #pragma unroll
           for (int t = 0; t < RT; ++t)
-            red[wave - 1][(m * ST_CG + c) * RT + t][lane] = acc[m][c][t];
+            red[wave - 1][(m * CG + c) * RT + t][lane] = acc[m][c][t];
     }
     __syncthreads();
     if (wave == 0) {
@@ -229,14 +228,14 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-          for (int c = 0; c < ST_CG; ++c)
+          for (int c = 0; c < CG; ++c)
 #pragma unroll
             for (int t = 0; t < RT; ++t)
-              acc[m][c][t] += red[w][(m * ST_CG + c) * RT + t][lane];
+              acc[m][c][t] += red[w][(m * CG + c) * RT + t][lane];
       // epilogue: lane holds column n0+16c+col, rows rg + 16t + 4*kq + r
       bf16* outp = (bf16*)(MODE == DOWN ? a.y : a.h);
 #pragma unroll
-      for (int c = 0; c < ST_CG; ++c) {
+      for (int c = 0; c < CG; ++c) {
         const int n = n0 + 16 * c + col;
         if (n >= N) continue;
         float bias = 0.f;
@@ -714,10 +713,19 @@ hipError_t launch_mode(const FfnArgs& a, hipStream_t s, int sched, int rt,
   const int N = MODE == DOWN ? a.d : a.d_ff;
   const int G = a.E + a.n_shared;
   if (sched == 0) {
-    dim3 grid((N + ST_COLS - 1) / ST_COLS, G);
-    if (rt == 1) ffn_stream_kernel<MODE, 1><<<grid, ST_WAVES * 64, 0, s>>>(a);
-    else if (rt == 2) ffn_stream_kernel<MODE, 2><<<grid, ST_WAVES * 64, 0, s>>>(a);
-    else ffn_stream_kernel<MODE, 4><<<grid, ST_WAVES * 64, 0, s>>>(a);
+    // two column groups per workgroup unless that leaves too few
+    // workgroups to cover the chip
+    const int cg = (long long)((N + 31) / 32) * G >= 512 ? 2 : 1;
+    dim3 grid((N + 16 * cg - 1) / (16 * cg), G);
+    if (cg == 2) {
+      if (rt == 1) ffn_stream_kernel<MODE, 1, 2><<<grid, ST_WAVES * 64, 0, s>>>(a);
+      else if (rt == 2) ffn_stream_kernel<MODE, 2, 2><<<grid, ST_WAVES * 64, 0, s>>>(a);
+      else ffn_stream_kernel<MODE, 4, 2><<<grid, ST_WAVES * 64, 0, s>>>(a);
+    } else {
+      if (rt == 1) ffn_stream_kernel<MODE, 1, 1><<<grid, ST_WAVES * 64, 0, s>>>(a);
+      else if (rt == 2) ffn_stream_kernel<MODE, 2, 1><<<grid, ST_WAVES * 64, 0, s>>>(a);
+      else ffn_stream_kernel<MODE, 4, 1><<<grid, ST_WAVES * 64, 0, s>>>(a);
+    }
   } else if (sched == 1 || sched == 3) {
     // sched 1: BM = 256, sched 3: BM = 128; max_tiles counts m-tiles
     const int ncols = MODE == UP_SWIGLU ? TL_BN / 2 : TL_BN;

@@ -24,6 +24,11 @@ SMALL = [
     W("mixtral_s_stream", T=200, d_model=256, n_experts=8, top_k=2,
       d_ff=512, act="swiglu", dtype="bf16", capacity=0, router_std=0.02,
       seed_index=11),
+    # enough columns for two 16-column groups per workgroup (up GEMM) and
+    # one group (down GEMM)
+    W("mixtral_s_stream_wide", T=24, d_model=1024, n_experts=8, top_k=2,
+      d_ff=2048, act="swiglu", dtype="bf16", capacity=0, router_std=0.02,
+      seed_index=25),
     W("mixtral_s_tiled", T=700, d_model=256, n_experts=8, top_k=2,
       d_ff=384, act="swiglu", dtype="bf16", capacity=0, router_std=0.02,
       seed_index=12),
