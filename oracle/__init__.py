@@ -34,4 +34,10 @@ from .moe import (  # noqa: F401
     combine,
     aux_loss,
     layer_forward,
+    Q4_GROUP,
+    quantize_int4,
+    dequantize_int4,
+    pack_int4,
+    unpack_int4,
+    int4_bytes,
 )

@@ -363,3 +363,91 @@ def layer_forward(x, w_router, weights, *, k, cap, act, n_shared=0,
                 "prob_mean": r["probs"].mean(axis=0) if T else
                 np.zeros(E, F64)})
     return res
+
+
+# ---------------------------------------------------------------------------
+# 4-bit expert weights (decode path)
+# ---------------------------------------------------------------------------
+# [LBS] "Production Considerations", Quantization for MoE: storing expert
+# weights in 4 bits shrinks Mixtral 8x7B's weights from about 93 GB to about
+# 26 GB; the calibrated methods the page names need data, so the reading
+# kept here is plain round-to-nearest with one affine pair (scale, offset)
+# per group of Q4_GROUP consecutive input-dimension weights of one output
+# row.  The code of every weight is an integer decided by floating point,
+# so the decision is taken in float32 with correctly rounded division, the
+# precision the GPU quantiser uses.
+
+Q4_GROUP = 128
+
+
+def quantize_int4(w):
+    """Group-wise 4-bit round-to-nearest codes of a weight matrix.
+
+    ``w`` [rows, K] (K a multiple of 128) holds bf16 values as float32.  Per
+    group of 128 consecutive weights of a row: lo = min, hi = max,
+    s = (hi - lo) / 15, code q = rint((w - lo) / s) clamped to 0..15
+    (ties to even); a constant group gets s = 0 and q = 0.  The weight is
+    represented as lo + q * s.  Returns ``(q [rows, K] uint8, scale
+    [rows, K/128] float32, offset [rows, K/128] float32)``."""
+    w = np.asarray(w, np.float32)
+    rows, K = w.shape
+    assert K % Q4_GROUP == 0
+    g = w.reshape(rows, K // Q4_GROUP, Q4_GROUP)
+    lo = g.min(axis=2)
+    hi = g.max(axis=2)
+    s = ((hi - lo) / np.float32(15.0)).astype(np.float32)
+    q = np.zeros(g.shape, np.uint8)
+    for r in range(rows):
+        for j in range(K // Q4_GROUP):
+            if s[r, j] == 0:
+                continue
+            v = (g[r, j] - lo[r, j]) / s[r, j]          # float32 arithmetic
+            q[r, j] = np.clip(np.rint(v), 0, 15).astype(np.uint8)
+    return q.reshape(rows, K), s, lo.astype(np.float32)
+
+
+def dequantize_int4(q, scale, offset):
+    """Weights represented by 4-bit codes: offset + q * scale per group, in
+    float64 ([rows, K])."""
+    q = np.asarray(q, F64)
+    rows, K = q.shape
+    s = np.repeat(np.asarray(scale, F64), Q4_GROUP, axis=1)
+    o = np.repeat(np.asarray(offset, F64), Q4_GROUP, axis=1)
+    return o + q * s
+
+
+def pack_int4(q):
+    """Pack codes [rows, K] into the library's storage bytes [rows, K/2].
+
+    Eight consecutive weights k0..k7 share one little-endian 32-bit word:
+    nibble i (bits 4i..4i+3) holds k_(2i) for i < 4 and k_(2(i-4)+1) for
+    i >= 4, so even weights sit in the low half-word and odd weights in the
+    high half-word.  (A storage format of this library, not of the
+    pages.)"""
+    q = np.asarray(q, np.uint32)
+    rows, K = q.shape
+    assert K % 8 == 0
+    k8 = q.reshape(rows, K // 8, 8)
+    word = np.zeros((rows, K // 8), np.uint32)
+    for i in range(4):
+        word |= k8[:, :, 2 * i] << np.uint32(4 * i)
+        word |= k8[:, :, 2 * i + 1] << np.uint32(16 + 4 * i)
+    return word.astype("<u4").view(np.uint8).reshape(rows, K // 2)
+
+
+def unpack_int4(packed, K):
+    """Inverse of :func:`pack_int4`."""
+    b = np.ascontiguousarray(np.asarray(packed, np.uint8))
+    rows = b.shape[0]
+    word = b.reshape(rows, K // 8, 4).view("<u4").reshape(rows, K // 8)
+    q = np.zeros((rows, K // 8, 8), np.uint8)
+    for i in range(4):
+        q[:, :, 2 * i] = (word >> np.uint32(4 * i)) & 15
+        q[:, :, 2 * i + 1] = (word >> np.uint32(16 + 4 * i)) & 15
+    return q.reshape(rows, K)
+
+
+def int4_bytes(rows, K):
+    """Storage bytes of a [rows, K] matrix in this format: K/2 code bytes
+    per row plus a float32 scale and offset per group."""
+    return rows * (K // 2) + rows * (K // Q4_GROUP) * 8

@@ -481,5 +481,92 @@ def pin_param_counts():
         synth.weight_shapes(demo)["w_router"]) == dm["expert_params"]
 
 
+# ---------------------------------------------------------------------------
+# 4-bit expert weights
+# ---------------------------------------------------------------------------
+
+def _bf16_grid_group(rng, lo, s, n=128):
+    """Weights lo + q*s (exactly representable) whose codes include 0 and
+    15, so the group's min and max are lo and lo + 15 s."""
+    q = rng.integers(0, 16, n)
+    q[rng.integers(0, n)] = 0
+    q[(rng.integers(1, n) + np.argmin(q)) % n] = 15
+    return q, (lo + q * s).astype(np.float32)
+
+
+def pin_int4_exact_grid():
+    # weights already on a 4-bit grid come back as the same codes, scale
+    # and offset, and dequantise exactly
+    rng = _rng(41)
+    rows = []
+    qs = []
+    for lo, s in [(-0.25, 2.0 ** -6), (0.5, 2.0 ** -4), (-3.0, 0.25),
+                  (1.0 / 64, 2.0 ** -10)]:
+        qq, ww = [], []
+        for _ in range(2):
+            q, w = _bf16_grid_group(rng, lo, s)
+            qq.append(q)
+            ww.append(w)
+        rows.append(np.concatenate(ww))
+        qs.append((np.concatenate(qq), lo, s))
+    w = np.stack(rows)
+    q, scale, off = oracle.quantize_int4(w)
+    for r, (qq, lo, s) in enumerate(qs):
+        assert q[r].tolist() == qq.tolist()
+        assert (scale[r] == np.float32(s)).all()
+        assert (off[r] == np.float32(lo)).all()
+    assert (oracle.dequantize_int4(q, scale, off) == w.astype(np.float64)).all()
+
+
+def pin_int4_nearest_code():
+    # round to nearest: every code is a closest of the 16 grid points (brute
+    # force in float64), so the error is at most half a step
+    rng = _rng(42)
+    w = torch.randn(6, 384, generator=torch.Generator().manual_seed(42))
+    w = (w * torch.linspace(0.01, 3.0, 384)).to(torch.bfloat16).float().numpy()
+    q, scale, off = oracle.quantize_int4(w)
+    d = oracle.dequantize_int4(q, scale, off)
+    s64 = np.repeat(scale.astype(np.float64), 128, axis=1)
+    o64 = np.repeat(off.astype(np.float64), 128, axis=1)
+    cand = o64[..., None] + np.arange(16)[None, None, :] * s64[..., None]
+    best = np.abs(cand - w[..., None]).min(axis=2)
+    err = np.abs(d - w)
+    assert (err <= best + 1e-6 * s64).all()
+    assert (err <= 0.5 * s64 * (1 + 1e-5)).all()
+    assert q.min() == 0 and q.max() == 15
+    # the group's own min and max are represented exactly
+    g = w.reshape(6, 3, 128)
+    assert np.allclose(off, g.min(axis=2), rtol=0, atol=0)
+    top = (off.astype(np.float64) + 15 * scale.astype(np.float64))
+    assert np.allclose(top, g.max(axis=2), rtol=1e-6, atol=0)
+    del rng
+
+
+def pin_int4_constant_group():
+    w = np.full((2, 256), 0.375, np.float32)
+    w[1, 128:] = -2.5
+    q, scale, off = oracle.quantize_int4(w)
+    assert (q == 0).all() and (scale == 0).all()
+    assert (oracle.dequantize_int4(q, scale, off) == w).all()
+
+
+def pin_int4_packing_hand_example():
+    g = _golden("int4_format.json")
+    packed = oracle.pack_int4(np.array([g["codes"]], np.uint8))
+    assert packed.tolist() == [g["packed_bytes"]]
+    rng = _rng(43)
+    q = rng.integers(0, 16, (5, 256)).astype(np.uint8)
+    assert (oracle.unpack_int4(oracle.pack_int4(q), 256) == q).all()
+
+
+def pin_int4_footprint_matches_page():
+    # 93 GB of bfloat16 weights in this format: roughly 26 GB
+    g = _golden("int4_format.json")
+    rows, K = 14336, 4096
+    ratio = oracle.int4_bytes(rows, K) / (2 * rows * K)
+    gb = g["mixtral_bf16_gb"] * ratio
+    assert abs(gb - g["mixtral_4bit_gb"]) <= 0.05 * g["mixtral_4bit_gb"], gb
+
+
 ALL_PINS = [v for k, v in sorted(globals().items())
             if k.startswith("pin_") and callable(v)]

@@ -213,13 +213,52 @@ def m_token_from_assignment_by_E(mp):
 
 
 _layer = om.layer_forward
+_quantize = om.quantize_int4
+_dequantize = om.dequantize_int4
+_pack = om.pack_int4
+
+
+def m_q4_floor(mp):
+    def quantize_int4(w):
+        w = np.asarray(w, np.float32)
+        rows, K = w.shape
+        g = w.reshape(rows, K // 128, 128)
+        lo, hi = g.min(axis=2), g.max(axis=2)
+        s = ((hi - lo) / np.float32(15.0)).astype(np.float32)
+        safe = np.where(s == 0, np.float32(1), s)
+        q = np.clip(np.floor((g - lo[..., None]) / safe[..., None]), 0, 15)
+        q = np.where(s[..., None] == 0, 0, q).astype(np.uint8)
+        return q.reshape(rows, K), s, lo
+    _patch(mp, "quantize_int4", quantize_int4)
+
+
+def m_q4_sixteen_steps(mp):
+    def quantize_int4(w):
+        q, s, o = _quantize(w)
+        return q, (s * np.float32(15.0 / 16.0)).astype(np.float32), o
+    _patch(mp, "quantize_int4", quantize_int4)
+
+
+def m_q4_dequant_no_offset(mp):
+    def dequantize_int4(q, scale, offset):
+        return _dequantize(q, scale, np.zeros_like(np.asarray(offset)))
+    _patch(mp, "dequantize_int4", dequantize_int4)
+
+
+def m_q4_pack_natural_order(mp):
+    def pack_int4(q):
+        q = np.asarray(q, np.uint8)
+        rows, K = q.shape
+        return (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    _patch(mp, "pack_int4", pack_int4)
 
 MUTATIONS = [m_no_renormalise, m_tie_to_higher_index, m_bias_in_gates,
              m_capacity_by_slot, m_keep_last, m_renormalise_survivors,
              m_transposed_w2, m_drop_bias_b2, m_gelu_tanh, m_silu_is_sigmoid,
              m_swap_gate_up, m_aux_post_capacity, m_aux_no_E,
              m_capacity_ceil, m_softmax_no_shift, m_no_shared,
-             m_token_from_assignment_by_E]
+             m_token_from_assignment_by_E, m_q4_floor, m_q4_sixteen_steps,
+             m_q4_dequant_no_offset, m_q4_pack_natural_order]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=[m.__name__ for m in
