@@ -35,7 +35,8 @@ METRIC = ("MoE layer fwd tokens/s + % of bf16 MFMA / HBM roofline "
           "(Mixtral-shaped layer)")
 # oracle sample (tokens whose expert outputs the oracle evaluates); routing
 # and dispatch of the oracle always cover the whole batch
-CPU_SAMPLE = {"mixtral_decode": 16, "mixtral_prefill": 48,
+CPU_SAMPLE = {"mixtral_decode": 16, "mixtral_decode_int4": 2,
+              "mixtral_prefill": 48,
               "switch_top1_cf1": 256, "switch_top1_cf125": 256,
               "deepseek_v3": 12, "tiny_gelu_f32": 64}
 
@@ -107,10 +108,17 @@ def main():
     # Two copies of the expert weights, used on alternate steps: a step's
     # weights were last read two steps earlier, with the other copy read in
     # between, so the 256 MB memory-side cache gives no reuse across steps.
-    wnames = [n for n in synth.weight_shapes(wl) if n != "w_router"]
+    q4 = wl.wquant == "int4"
+    bf16_inp = inp
+    if q4:
+        # 4-bit expert weights, quantised on the device before timing
+        inp = moe.quantize_weights(bf16_inp)
+    wnames = [n for n in inp if n in moe.QUANT_MATRICES or
+              n.endswith("_q") or n in ("b1", "b2", "shared_b1", "shared_b2")]
     inp_b = dict(inp)
     for n in wnames:
-        inp_b[n] = inp[n].clone()
+        if inp[n] is not None:
+            inp_b[n] = inp[n].clone()
     Ws = [moe.expert_weights(inp), moe.expert_weights(inp_b)]
     W = Ws[0]
 
@@ -197,8 +205,16 @@ def main():
     esz = 2 if wl.dtype == "bf16" else 4
     touched = sum(1 for c in cnt if c > 0) + wl.n_shared
     nmat_up = 2 if wl.act == "swiglu" else 1
-    up_w = touched * (nmat_up * f * d + (f if wl.act == "gelu" else 0)) * esz
-    dn_w = touched * (d * f + (d if wl.act == "gelu" else 0)) * esz
+    if q4:
+        # codes (half a byte per weight) + float32 (scale, offset) per 128
+        qb = lambda n: n // 2 + (n // 128) * 8
+        up_w = touched * (nmat_up * qb(f * d) +
+                          (f * esz if wl.act == "gelu" else 0))
+        dn_w = touched * (qb(d * f) + (d * esz if wl.act == "gelu" else 0))
+    else:
+        up_w = touched * (nmat_up * f * d +
+                          (f if wl.act == "gelu" else 0)) * esz
+        dn_w = touched * (d * f + (d if wl.act == "gelu" else 0)) * esz
     krn = {
         "expert_up": {
             "bytes": up_w + kept_total_rows(kept_total, wl) * (d + f) * esz,
@@ -247,7 +263,9 @@ def main():
         "data": "synthetic (seeded; random-init weights of the layer shape)",
         "config": {"workload": wl.name, "T": T, "d_model": d,
                    "n_experts": E, "top_k": k, "d_ff": f, "act": wl.act,
-                   "capacity": wl.capacity, "n_shared": wl.n_shared},
+                   "capacity": wl.capacity, "n_shared": wl.n_shared,
+                   "expert_weights": "int4 (group 128, fp32 scale/offset)"
+                   if q4 else wl.dtype},
         "roofline": roof,
         "layer_roofline": {
             "flops": F, "bytes": B, "t_roof_us": round(t_roof * 1e6, 2),
@@ -271,7 +289,7 @@ def main():
                     "aux_loss": float(aux.item())},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_tokens,
+        res["cpu_baseline"] = cpu_baseline(wl, bf16_inp, args.cpu_tokens,
                                            gpu_idx=idx.cpu().numpy())
     print(json.dumps(res), flush=True)
     if args.copy_calibration_mib > 0:
@@ -322,14 +340,24 @@ def cpu_baseline(wl, inp, n_tokens=None, gpu_idx=None):
     names = (["w1", "b1", "w2", "b2"] if wl.act == "gelu"
              else ["w_gate", "w_up", "w_down"])
     w = {}
+    # 4-bit weights: the oracle evaluates the weights its own codes
+    # represent (quantised and dequantised here, before the clock starts)
+    q4 = wl.wquant == "int4"
+
+    def prep(a, name):
+        if not q4 or name.startswith("b") or name.startswith("shared_b"):
+            return a
+        q, sc, off = oracle.quantize_int4(a.reshape(-1, a.shape[-1]))
+        return oracle.dequantize_int4(q, sc, off).reshape(a.shape)
+
     for nme in names:
         full = {}
         for e in need:
-            full[e] = hx(inp[nme][e])
+            full[e] = prep(hx(inp[nme][e]), nme)
         w[nme] = full
     for nme in list(inp):
         if nme.startswith("shared_"):
-            w[nme] = hx(inp[nme])
+            w[nme] = prep(hx(inp[nme]), nme)
     t0 = time.perf_counter()
     oracle.layer_forward(x, wr, w, k=wl.top_k, cap=wl.capacity, act=wl.act,
                          n_shared=wl.n_shared, alpha=wl.aux_coef,
@@ -341,7 +369,9 @@ def cpu_baseline(wl, inp, n_tokens=None, gpu_idx=None):
     return {"value": round(n / dt, 4), "unit": "tokens/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 3),
             "routing_flips_vs_gpu": flips,
-            "sample": f"{n} of {wl.T} tokens: float64 routing + capacity "
+            "sample": ("4-bit weights quantised and dequantised by the oracle "
+                       "before timing; " if q4 else "") +
+                      f"{n} of {wl.T} tokens: float64 routing + capacity "
                       f"dispatch over all {wl.T} tokens, expert FFNs and "
                       f"combine for the {n} sampled tokens"}
 

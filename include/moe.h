@@ -74,6 +74,10 @@ extern "C" {
 #define MOE_DTYPE_F32 0
 #define MOE_DTYPE_BF16 1
 
+#define MOE_WQUANT_NONE 0 /* expert weights in the problem dtype          */
+#define MOE_WQUANT_INT4 1 /* expert weights as 4-bit codes, see below     */
+#define MOE_Q4_GROUP 128  /* weights per (scale, offset) pair             */
+
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOP_K 8
 
@@ -89,6 +93,10 @@ extern "C" {
  *   act        MOE_ACT_GELU or MOE_ACT_SWIGLU.
  *   dtype      MOE_DTYPE_F32 or MOE_DTYPE_BF16.
  *   aux_coef   alpha of the load-balance loss (0.01 for Mixtral: [LBS]).
+ *   wquant     MOE_WQUANT_NONE, or MOE_WQUANT_INT4 for 4-bit expert
+ *              weights ([LBS] Production Considerations, Quantization for
+ *              MoE); INT4 requires dtype BF16 and d_model, d_ff multiples
+ *              of 128.  Zero-initialised structs get NONE.
  */
 typedef struct moe_problem {
   int32_t T;
@@ -101,6 +109,7 @@ typedef struct moe_problem {
   int32_t act;
   int32_t dtype;
   float aux_coef;
+  int32_t wquant;
 } moe_problem;
 
 /*
@@ -111,6 +120,13 @@ typedef struct moe_problem {
  *           w2 = W_down [E, d, d_ff]; b1, b2 must be NULL.
  *   Shared expert (n_shared = 1): the same tensors without the expert axis
  *   in shared_w1 / shared_w_up / shared_w2 / shared_b1 / shared_b2.
+ *
+ * With wquant = MOE_WQUANT_INT4 the matrices w1, w_up, w2 (and the shared
+ * ones) hold 4-bit codes as written by moe_quantize_int4 (uint8
+ * [rows, K/2] for a [rows, K] matrix, stacked over experts), and *_q point
+ * to their float32 [rows, K/128, 2] (scale, offset) pairs; the weight is
+ * offset + code * scale.  Biases stay in the problem dtype.  The *_q
+ * pointers are ignored (may be NULL) without quantisation.
  */
 typedef struct moe_expert_weights {
   const void* w1;
@@ -123,6 +139,12 @@ typedef struct moe_expert_weights {
   const void* shared_w2;
   const void* shared_b1;
   const void* shared_b2;
+  const float* w1_q;
+  const float* w_up_q;
+  const float* w2_q;
+  const float* shared_w1_q;
+  const float* shared_w_up_q;
+  const float* shared_w2_q;
 } moe_expert_weights;
 
 /*
@@ -263,6 +285,26 @@ int32_t moe_layer_forward(const moe_problem* p, const void* x,
                           float* aux_loss, int32_t* counts,
                           int32_t* n_dropped, int32_t* topk_idx, void* ws,
                           size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Group-wise 4-bit round-to-nearest quantisation of a bf16 weight matrix
+ * ([LBS] Production Considerations, Quantization for MoE: 4-bit expert
+ * weights cut Mixtral 8x7B's weights from about 93 GB to about 26 GB).
+ *   w        [rows, K] bf16 input (K a positive multiple of 128).
+ *   codes    [rows, K/2] uint8 output.  Per group of 128 consecutive
+ *            weights of a row: lo = min, hi = max, scale = (hi - lo) / 15,
+ *            code = rint((w - lo) / scale) clamped to 0..15, ties to even,
+ *            in float32 with correctly rounded division; a constant group
+ *            gets scale 0 and code 0.  Eight consecutive weights k0..k7
+ *            share one little-endian 32-bit word: nibble i holds k_(2i)
+ *            for i < 4 and k_(2(i-4)+1) for i >= 4.
+ *   qparams  [rows, K/128, 2] float32 output: (scale, lo) per group.
+ * rows may be 0.  Returns MOE_EINVAL for null pointers or rows < 0,
+ * MOE_ENOTSUP when K is not a positive multiple of 128 or rows * K / 8
+ * reaches 2^32 (split larger matrices by rows).
+ */
+int32_t moe_quantize_int4(const void* w, int64_t rows, int32_t K,
+                          void* codes, float* qparams, hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char* moe_status_string(int32_t status);

@@ -396,13 +396,11 @@ def quantize_int4(w):
     lo = g.min(axis=2)
     hi = g.max(axis=2)
     s = ((hi - lo) / np.float32(15.0)).astype(np.float32)
-    q = np.zeros(g.shape, np.uint8)
-    for r in range(rows):
-        for j in range(K // Q4_GROUP):
-            if s[r, j] == 0:
-                continue
-            v = (g[r, j] - lo[r, j]) / s[r, j]          # float32 arithmetic
-            q[r, j] = np.clip(np.rint(v), 0, 15).astype(np.uint8)
+    const = s == 0
+    safe = np.where(const, np.float32(1.0), s)[..., None]
+    v = (g - lo[..., None]) / safe                      # float32 arithmetic
+    q = np.clip(np.rint(v), 0, 15)
+    q = np.where(const[..., None], 0, q).astype(np.uint8)
     return q.reshape(rows, K), s, lo.astype(np.float32)
 
 

@@ -26,6 +26,10 @@ LIB_PATH = os.path.join(PKG, "libmoe.so")
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_ACT_GELU, MOE_ACT_SWIGLU = 0, 1
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
+MOE_WQUANT_NONE, MOE_WQUANT_INT4 = 0, 1
+MOE_Q4_GROUP = 128
+WQUANT = {None: MOE_WQUANT_NONE, "none": MOE_WQUANT_NONE,
+          "int4": MOE_WQUANT_INT4}
 ACT = {"gelu": MOE_ACT_GELU, "swiglu": MOE_ACT_SWIGLU}
 DTYPE = {"f32": MOE_DTYPE_F32, "bf16": MOE_DTYPE_BF16}
 TORCH_DTYPE = {MOE_DTYPE_F32: torch.float32, MOE_DTYPE_BF16: torch.bfloat16}
@@ -42,13 +46,15 @@ class moe_problem(ctypes.Structure):
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("d_ff", ctypes.c_int32), ("n_shared", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("act", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("aux_coef", ctypes.c_float)]
+                ("dtype", ctypes.c_int32), ("aux_coef", ctypes.c_float),
+                ("wquant", ctypes.c_int32)]
 
 
 class moe_expert_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("w1", "w_up", "w2", "b1", "b2", "shared_w1", "shared_w_up",
-                 "shared_w2", "shared_b1", "shared_b2")]
+                 "shared_w2", "shared_b1", "shared_b2", "w1_q", "w_up_q",
+                 "w2_q", "shared_w1_q", "shared_w_up_q", "shared_w2_q")]
 
 
 _P = ctypes.POINTER(moe_problem)
@@ -69,6 +75,7 @@ _SIGS = {
     "moe_combine": (_I32, [_P, _V, _V, _V, _V, _V, _V]),
     "moe_layer_forward": (_I32, [_P, _V, _V, _V, _V, _W, _V, _V, _V, _V, _V,
                                  _V, _SZ, _V]),
+    "moe_quantize_int4": (_I32, [_V, ctypes.c_int64, _I32, _V, _V, _V]),
     "moe_status_string": (ctypes.c_char_p, [_I32]),
 }
 EXPORTS = tuple(_SIGS)
@@ -120,29 +127,39 @@ def _check(status, where):
 
 
 def problem(T, d_model, n_experts, top_k, d_ff, *, n_shared=0, capacity=0,
-            act="swiglu", dtype="bf16", aux_coef=0.01) -> moe_problem:
+            act="swiglu", dtype="bf16", aux_coef=0.01,
+            wquant=None) -> moe_problem:
     return moe_problem(T, d_model, n_experts, top_k, d_ff, n_shared, capacity,
                        ACT[act] if isinstance(act, str) else act,
                        DTYPE[dtype] if isinstance(dtype, str) else dtype,
-                       aux_coef)
+                       aux_coef,
+                       WQUANT[wquant] if not isinstance(wquant, int)
+                       else wquant)
 
 
 def problem_for(wl) -> moe_problem:
     """The C problem struct of a :class:`synth.Workload`."""
     return problem(wl.T, wl.d_model, wl.n_experts, wl.top_k, wl.d_ff,
                    n_shared=wl.n_shared, capacity=wl.capacity, act=wl.act,
-                   dtype=wl.dtype, aux_coef=wl.aux_coef)
+                   dtype=wl.dtype, aux_coef=wl.aux_coef,
+                   wquant=getattr(wl, "wquant", None))
 
 
 def expert_weights(w: dict) -> moe_expert_weights:
     """C weights struct from a dict of device tensors keyed like the
-    layer's weights (w1/w2/b1/b2 or w_gate/w_up/w_down, shared_*)."""
+    layer's weights (w1/w2/b1/b2 or w_gate/w_up/w_down, shared_*).  For
+    4-bit weights the matrices hold codes and ``<name>_q`` their
+    (scale, offset) pairs."""
     get = lambda *names: next((_ptr(w[n]) for n in names
                                if w.get(n) is not None), None)
+    q = lambda *names: get(*[n + "_q" for n in names])
     return moe_expert_weights(
         get("w1", "w_gate"), get("w_up"), get("w2", "w_down"), get("b1"),
         get("b2"), get("shared_w1", "shared_gate"), get("shared_up"),
-        get("shared_w2", "shared_down"), get("shared_b1"), get("shared_b2"))
+        get("shared_w2", "shared_down"), get("shared_b1"), get("shared_b2"),
+        q("w1", "w_gate"), q("w_up"), q("w2", "w_down"),
+        q("shared_w1", "shared_gate"), q("shared_up"),
+        q("shared_w2", "shared_down"))
 
 
 # ---------------------------------------------------------------------------
@@ -237,6 +254,42 @@ def moe_layer_forward(p, x, w_router, router_bias, select_bias, weights, out,
                                   _stream(stream)), "moe_layer_forward")
 
 
+def moe_quantize_int4(w, codes, qparams, stream=None):
+    """4-bit codes of a bf16 matrix (or stack of matrices) ``w`` whose last
+    axis is the input dimension K: ``codes`` uint8 [..., K/2], ``qparams``
+    float32 [..., K/128, 2]."""
+    K = w.shape[-1]
+    rows = w.numel() // K if K else 0
+    _check(_lib.moe_quantize_int4(_ptr(w), rows, K, _ptr(codes),
+                                  _ptr(qparams), _stream(stream)),
+           "moe_quantize_int4")
+
+
+QUANT_MATRICES = ("w1", "w2", "w_gate", "w_up", "w_down", "shared_w1",
+                  "shared_w2", "shared_gate", "shared_up", "shared_down")
+
+
+def quantize_weights(inp: dict, stream=None) -> dict:
+    """A copy of a weights dict with every expert matrix replaced by its
+    4-bit codes (same key) and (scale, offset) pairs (key + ``_q``), made
+    on the device by :func:`moe_quantize_int4`.  Biases and the router stay
+    as they are."""
+    out = dict(inp)
+    for n in QUANT_MATRICES:
+        w = inp.get(n)
+        if w is None:
+            continue
+        K = w.shape[-1]
+        codes = torch.empty(*w.shape[:-1], K // 2, dtype=torch.uint8,
+                            device=w.device)
+        qp = torch.empty(*w.shape[:-1], K // MOE_Q4_GROUP, 2,
+                         dtype=torch.float32, device=w.device)
+        moe_quantize_int4(w, codes, qp, stream)
+        out[n] = codes
+        out[n + "_q"] = qp
+    return out
+
+
 # ---------------------------------------------------------------------------
 # convenience: allocate outputs and run the whole layer
 # ---------------------------------------------------------------------------
@@ -277,7 +330,14 @@ def flops_and_bytes(wl, counts, kept_total) -> tuple:
     rows = kept_total + wl.n_shared * wl.T
     flops = 2 * rows * per_expert + 2 * wl.T * d * E
     touched = sum(1 for c in counts if c > 0) + wl.n_shared
-    byts = (touched * (per_expert + bias) * esz + 2 * wl.T * d * esz
+    if getattr(wl, "wquant", None) == "int4":
+        # codes (half a byte per weight) plus a float32 (scale, offset) per
+        # group of 128 weights
+        w_bytes = per_expert // 2 + (per_expert // MOE_Q4_GROUP) * 8 \
+            + bias * esz
+    else:
+        w_bytes = (per_expert + bias) * esz
+    byts = (touched * w_bytes + 2 * wl.T * d * esz
             + E * d * 4 + (E * 4 if wl.zipf_s > 0 else 0)
             + (E * 4 if wl.select_bias_std > 0 else 0))
     return flops, byts
@@ -285,4 +345,5 @@ def flops_and_bytes(wl, counts, kept_total) -> tuple:
 
 __all__ = [n for n in dir() if n.startswith("moe_")] + [
     "problem", "problem_for", "expert_weights", "workspace", "layer_forward",
+    "quantize_weights", "QUANT_MATRICES",
     "flops_and_bytes", "MoEError", "synth", "library_path", "EXPORTS"]

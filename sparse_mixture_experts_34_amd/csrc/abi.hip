@@ -72,6 +72,12 @@ int32_t check_problem(const moe_problem* p) {
   if (p->dtype != MOE_DTYPE_F32 && p->dtype != MOE_DTYPE_BF16)
     return MOE_EINVAL;
   if (!isfinite(p->aux_coef)) return MOE_EINVAL;
+  if (p->wquant != MOE_WQUANT_NONE && p->wquant != MOE_WQUANT_INT4)
+    return MOE_EINVAL;
+  if (p->wquant == MOE_WQUANT_INT4 &&
+      (p->dtype != MOE_DTYPE_BF16 || p->d_model % MOE_Q4_GROUP != 0 ||
+       p->d_ff % MOE_Q4_GROUP != 0))
+    return MOE_ENOTSUP;
   const long long rows = (long long)p->T * p->top_k + (long long)p->n_shared * p->T;
   if (rows >= (1LL << 31)) return MOE_ENOTSUP;
   return MOE_OK;
@@ -100,6 +106,15 @@ int32_t check_weights(const moe_problem* p, const moe_expert_weights* w) {
     if (p->n_shared && (!w->shared_w1 || !w->shared_w2 || !w->shared_b1 ||
                         !w->shared_b2 || w->shared_w_up))
       return MOE_EINVAL;
+  }
+  if (p->wquant == MOE_WQUANT_INT4) {
+    // every quantised matrix needs its (scale, offset) pairs
+    if (!w->w1_q || !w->w2_q) return MOE_EINVAL;
+    if (p->act == MOE_ACT_SWIGLU && !w->w_up_q) return MOE_EINVAL;
+    if (p->n_shared) {
+      if (!w->shared_w1_q || !w->shared_w2_q) return MOE_EINVAL;
+      if (p->act == MOE_ACT_SWIGLU && !w->shared_w_up_q) return MOE_EINVAL;
+    }
   }
   return MOE_OK;
 }
@@ -137,6 +152,13 @@ FfnArgs ffn_args(const moe_problem* p, const void* x, const int32_t* perm,
   a.sw2 = w->shared_w2;
   a.sb1 = w->shared_b1;
   a.sb2 = w->shared_b2;
+  a.wquant = p->wquant;
+  a.w1q = w->w1_q;
+  a.w_upq = w->w_up_q;
+  a.w2q = w->w2_q;
+  a.sw1q = w->shared_w1_q;
+  a.sw_upq = w->shared_w_up_q;
+  a.sw2q = w->shared_w2_q;
   a.h = h;
   a.y = y;
   return a;
@@ -341,6 +363,17 @@ int32_t moe_layer_forward(const moe_problem* p, const void* x,
   MOE_TRY(launch_combine(p->dtype, x, y, a.slot_of, gate, out, p->T,
                          p->d_model, p->top_k, p->n_shared, stream));
   return MOE_OK;
+}
+
+int32_t moe_quantize_int4(const void* w, int64_t rows, int32_t K,
+                          void* codes, float* qparams, hipStream_t stream) {
+  if (rows < 0) return MOE_EINVAL;
+  if (K <= 0 || K % MOE_Q4_GROUP != 0) return MOE_ENOTSUP;
+  if (rows > 0 && (!w || !codes || !qparams)) return MOE_EINVAL;
+  // one thread per code word: the grid (rows * K / 8 threads) must fit the
+  // 32-bit dispatch size
+  if ((long long)rows * (K / 8) >= (1LL << 32) - 256) return MOE_ENOTSUP;
+  return status_of(launch_quantize_int4(w, rows, K, codes, qparams, stream));
 }
 
 const char* moe_status_string(int32_t status) {

@@ -264,6 +264,236 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
 }
 
 // ===========================================================================
+// stream schedule, 4-bit weights
+// ===========================================================================
+// The stream schedule's work split (16*CG columns per workgroup, 4 waves
+// splitting K) with one K step per quantisation group of 128 weights.  Lane
+// (col, kq) takes weights kq*32 .. kq*32+31 of the group in its row: 16
+// code bytes, i.e. four words, each word one 16x16x32 MFMA B operand.  A
+// word becomes eight bf16 with one shift and one and-or per pair: the bits
+// 0x4300 | q are exactly the bf16 number 128 + q, so the MFMAs sum
+// x * (128 + q) over the group, and one more MFMA per 32 weights against
+// bf16 ones gives the group's sum of x.  Then
+//   sum x * (lo + q*s) = s * sum x*(128 + q) + (lo - 128*s) * sum x
+// folds the group's scale and offset in after its MFMAs.  The A operand
+// takes the same weights in natural order (lane kq: kq*32 + 8h + 0..7 for
+// MFMA h), matching the code word layout (even weights in the low
+// half-words, odd weights in the high half-words).
+template <int MODE>
+__device__ __forceinline__ void group_weights_q4(
+    const FfnArgs& a, int g, bool shared, int N, int K, const uint8_t*& c0,
+    const uint8_t*& c1, const float*& q0, const float*& q1,
+    const void*& bias) {
+  const size_t cmat = (size_t)N * (K / 2);              // code bytes
+  const size_t qmat = (size_t)N * (K / Q4_GROUP) * 2;   // floats
+  c1 = nullptr;
+  q1 = nullptr;
+  if (MODE == DOWN) {
+    c0 = shared ? (const uint8_t*)a.sw2 : (const uint8_t*)a.w2 + (size_t)g * cmat;
+    q0 = shared ? a.sw2q : a.w2q + (size_t)g * qmat;
+    bias = shared ? a.sb2
+                  : (a.b2 ? (const char*)a.b2 + (size_t)g * N * 2 : nullptr);
+  } else {
+    c0 = shared ? (const uint8_t*)a.sw1 : (const uint8_t*)a.w1 + (size_t)g * cmat;
+    q0 = shared ? a.sw1q : a.w1q + (size_t)g * qmat;
+    if (MODE == UP_SWIGLU) {
+      c1 = shared ? (const uint8_t*)a.sw_up
+                  : (const uint8_t*)a.w_up + (size_t)g * cmat;
+      q1 = shared ? a.sw_upq : a.w_upq + (size_t)g * qmat;
+      bias = nullptr;
+    } else {
+      bias = shared ? a.sb1 : (const char*)a.b1 + (size_t)g * N * 2;
+    }
+  }
+}
+
+template <int NMAT, int RT, int CG>
+struct Q4Buf {
+  u32x4 code[NMAT][CG];   // 32 codes of one weight row, four words
+  float2 qp[NMAT][CG];    // that row's (scale, offset) for the group
+  u32x4 a[RT][4];         // 32 bf16 of one token row per row tile
+};
+
+__device__ __forceinline__ bf16x8 q4_operand(uint32_t word) {
+  V16 r;
+  r.u[0] = 0x43004300u | (word & 0x000F000Fu);
+  r.u[1] = 0x43004300u | ((word >> 4) & 0x000F000Fu);
+  r.u[2] = 0x43004300u | ((word >> 8) & 0x000F000Fu);
+  r.u[3] = 0x43004300u | ((word >> 12) & 0x000F000Fu);
+  return r.h;
+}
+
+template <int MODE, int RT, int CG, int PF>
+__global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_q4_kernel(FfnArgs a) {
+  constexpr int NMAT = MODE == UP_SWIGLU ? 2 : 1;
+  __shared__ f32x4 red[ST_WAVES - 1][NMAT * CG * RT][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = blockIdx.y;
+  const Group gr = group_of(g, a.offsets, a.E, a.T, a.k);
+  if (gr.rows <= 0) return;                 // uniform over the workgroup
+  const int N = MODE == DOWN ? a.d : a.d_ff;
+  const int K = MODE == DOWN ? a.d_ff : a.d;
+  const int n0 = blockIdx.x * 16 * CG;
+  if (n0 >= N) return;                      // uniform over the workgroup
+  const uint8_t* cm[2];
+  const float* qm[2];
+  const void* biasv;
+  group_weights_q4<MODE>(a, g, gr.shared, N, K, cm[0], cm[1], qm[0], qm[1],
+                         biasv);
+
+  const int col = lane & 15;   // B: weight row n0+16c+col; A: token row
+  const int kq = lane >> 4;    // 32-weight quarter of the group
+  const int ngroups = K / Q4_GROUP;
+  const int s_beg = wave * ngroups / ST_WAVES;
+  const int my_steps = (wave + 1) * ngroups / ST_WAVES - s_beg;
+  const uint8_t* crow[NMAT][CG];
+  const float2* qrow[NMAT][CG];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int c = 0; c < CG; ++c) {
+      const int n = min(n0 + 16 * c + col, N - 1);
+      crow[m][c] = cm[m] + (size_t)n * (K / 2) + (size_t)s_beg * (Q4_GROUP / 2) + kq * 16;
+      qrow[m][c] = (const float2*)qm[m] + (size_t)n * ngroups + s_beg;
+    }
+  V16 ones;
+  ones.u = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+
+  for (int rg = 0; rg < gr.rows; rg += RT * 16) {
+    const int ntile = min(RT, (gr.rows - rg + 15) >> 4);
+    const bf16* arow[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const int i = min(rg + t * 16 + col, gr.rows - 1);
+      arow[t] = a_row<MODE, bf16>(a, gr, i, K) + s_beg * Q4_GROUP + kq * 32;
+    }
+    f32x4 acc[NMAT][CG][RT];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int c = 0; c < CG; ++c)
+#pragma unroll
+        for (int t = 0; t < RT; ++t) acc[m][c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    Q4Buf<NMAT, RT, CG> buf[PF];
+    auto load = [&](Q4Buf<NMAT, RT, CG>& b, int s) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int c = 0; c < CG; ++c) {
+          b.code[m][c] = ldg16(crow[m][c] + (size_t)s * (Q4_GROUP / 2));
+          b.qp[m][c] = qrow[m][c][s];
+        }
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        if (t < ntile) {
+#pragma unroll
+          for (int h = 0; h < 4; ++h) b.a[t][h] = ldg16(arow[t] + s * Q4_GROUP + h * 8);
+        }
+      }
+    };
+    auto compute = [&](const Q4Buf<NMAT, RT, CG>& b) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        if (t < ntile) {
+          f32x4 xs = f32x4{0.f, 0.f, 0.f, 0.f};
+          f32x4 pg[NMAT][CG];
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int c = 0; c < CG; ++c) pg[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            V16 av;
+            av.u = b.a[t][h];
+            xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av.h, ones.h, xs, 0, 0, 0);
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+              for (int c = 0; c < CG; ++c)
+                pg[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    av.h, q4_operand(b.code[m][c][h]), pg[m][c], 0, 0, 0);
+          }
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int c = 0; c < CG; ++c) {
+              const float sc = b.qp[m][c].x;
+              const float cl = b.qp[m][c].y - 128.0f * sc;
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                acc[m][c][t][r] += sc * pg[m][c][r] + cl * xs[r];
+            }
+        }
+      }
+    };
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+      if (p < my_steps) load(buf[p], p);
+    for (int s0 = 0; s0 < my_steps; s0 += PF) {
+#pragma unroll
+      for (int p = 0; p < PF; ++p) {
+        const int st = s0 + p;
+        if (st < my_steps) {
+          compute(buf[p]);
+          if (st + PF < my_steps) load(buf[p], st + PF);
+        }
+      }
+    }
+
+    // K-split reduction: waves 1..3 park their sums, wave 0 adds in order
+    if (wave > 0) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int c = 0; c < CG; ++c)
+#pragma unroll
+          for (int t = 0; t < RT; ++t)
+            red[wave - 1][(m * CG + c) * RT + t][lane] = acc[m][c][t];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 0; w < ST_WAVES - 1; ++w)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int c = 0; c < CG; ++c)
+#pragma unroll
+            for (int t = 0; t < RT; ++t)
+              acc[m][c][t] += red[w][(m * CG + c) * RT + t][lane];
+      // epilogue: lane holds column n0+16c+col, rows rg + 16t + 4*kq + r
+      bf16* outp = (bf16*)(MODE == DOWN ? a.y : a.h);
+#pragma unroll
+      for (int c = 0; c < CG; ++c) {
+        const int n = n0 + 16 * c + col;
+        if (n >= N) continue;
+        float bias = 0.f;
+        if (MODE != UP_SWIGLU && biasv) bias = (float)((const bf16*)biasv)[n];
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          if (t < ntile) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int i = rg + t * 16 + kq * 4 + r;
+              if (i < gr.rows) {
+                float v;
+                if (MODE == UP_SWIGLU)
+                  v = silu(acc[0][c][t][r]) * acc[NMAT - 1][c][t][r];
+                else if (MODE == UP_GELU) v = gelu_erf(acc[0][c][t][r] + bias);
+                else v = acc[0][c][t][r] + bias;
+                outp[(size_t)(gr.out0 + i) * N + n] = (bf16)v;
+              }
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();   // red is reused by the next row group
+  }
+}
+
+// ===========================================================================
 // tiled schedule (bf16)
 // ===========================================================================
 // Workgroup tile BM x 256 (BM = 128 or 256) over BK = 64 slices of K, eight
@@ -778,8 +1008,32 @@ Plan plan_of(const FfnArgs& a) {
 }
 }  // namespace
 
+// 4-bit weights: the weight-streaming schedule at every batch size (a
+// decode-path format; larger batches stay correct, re-streaming the
+// weights once per 32 rows of an expert).
+template <int MODE>
+hipError_t launch_q4(const FfnArgs& a, hipStream_t s) {
+  const int N = MODE == DOWN ? a.d : a.d_ff;
+  const int G = a.E + a.n_shared;
+  const int cg = (long long)((N + 31) / 32) * G >= 512 ? 2 : 1;
+  dim3 grid((N + 16 * cg - 1) / (16 * cg), G);
+  const bool rt1 = a.T <= 16;   // a token picks an expert at most once
+  if (cg == 2) {
+    if (rt1) ffn_stream_q4_kernel<MODE, 1, 2, 3><<<grid, ST_WAVES * 64, 0, s>>>(a);
+    else ffn_stream_q4_kernel<MODE, 2, 2, 2><<<grid, ST_WAVES * 64, 0, s>>>(a);
+  } else {
+    if (rt1) ffn_stream_q4_kernel<MODE, 1, 1, 3><<<grid, ST_WAVES * 64, 0, s>>>(a);
+    else ffn_stream_q4_kernel<MODE, 2, 1, 2><<<grid, ST_WAVES * 64, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_expert_up(const FfnArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
+  if (a.wquant) {
+    if (a.act == 1) return launch_q4<UP_SWIGLU>(a, s);
+    return launch_q4<UP_GELU>(a, s);
+  }
   const Plan p = plan_of(a);
   if (a.act == 1) return launch_mode<UP_SWIGLU>(a, s, p.sched, p.rt, p.max_tiles);
   return launch_mode<UP_GELU>(a, s, p.sched, p.rt, p.max_tiles);
@@ -787,6 +1041,7 @@ hipError_t launch_expert_up(const FfnArgs& a, hipStream_t s) {
 
 hipError_t launch_expert_down(const FfnArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
+  if (a.wquant) return launch_q4<DOWN>(a, s);
   const Plan p = plan_of(a);
   return launch_mode<DOWN>(a, s, p.sched, p.rt, p.max_tiles);
 }

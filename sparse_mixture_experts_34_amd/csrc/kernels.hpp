@@ -85,9 +85,18 @@ struct FfnArgs {
   const void *sw1, *sw_up, *sw2, *sb1, *sb2;
   void* h;   // [T*k + n_shared*T, d_ff] workspace
   void* y;   // [T*k + n_shared*T, d]
+  // 4-bit weights: wquant = 1, matrices hold codes, *q the (scale, offset)
+  // pairs per group of Q4_GROUP weights
+  int wquant;
+  const float *w1q, *w_upq, *w2q, *sw1q, *sw_upq, *sw2q;
 };
 hipError_t launch_expert_up(const FfnArgs& a, hipStream_t s);
 hipError_t launch_expert_down(const FfnArgs& a, hipStream_t s);
+
+// ---- 4-bit weights ---------------------------------------------------------
+constexpr int Q4_GROUP = 128;   // weights per (scale, offset) pair
+hipError_t launch_quantize_int4(const void* w, long long rows, int K,
+                                void* codes, float* qparams, hipStream_t s);
 
 // ---- combine ---------------------------------------------------------------
 hipError_t launch_combine(int dtype, const void* x, const void* y,

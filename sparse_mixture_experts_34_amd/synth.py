@@ -48,6 +48,7 @@ class Workload:
     zipf_s: float = 0.0               # router bias -s*ln(e+1) when > 0
     select_bias_std: float = 0.0      # > 0: DeepSeek-style selection bias
     seed_index: int = 0
+    wquant: str | None = None         # "int4": 4-bit expert weights
     notes: dict = field(default_factory=dict, compare=False, hash=False)
 
     @property
@@ -74,6 +75,12 @@ WORKLOADS = {
         "mixtral_decode", T=16, d_model=4096, n_experts=8, top_k=2,
         d_ff=14336, act="swiglu", dtype="bf16", capacity=0,
         router_std=0.02, seed_index=1),
+    # the decode layer above with its expert weights in 4 bits (same seed,
+    # so the same bf16 weights before quantisation)
+    "mixtral_decode_int4": Workload(
+        "mixtral_decode_int4", T=16, d_model=4096, n_experts=8, top_k=2,
+        d_ff=14336, act="swiglu", dtype="bf16", capacity=0,
+        router_std=0.02, seed_index=1, wquant="int4"),
     "mixtral_prefill": Workload(
         "mixtral_prefill", T=8192, d_model=4096, n_experts=8, top_k=2,
         d_ff=14336, act="swiglu", dtype="bf16", capacity=0,

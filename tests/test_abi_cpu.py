@@ -86,13 +86,17 @@ BAD = [
     (dict(act=7), moe.MOE_EINVAL),
     (dict(dtype=5), moe.MOE_EINVAL),
     (dict(aux_coef=float("nan")), moe.MOE_EINVAL),
+    (dict(wquant=5), moe.MOE_EINVAL),
+    (dict(wquant=1, dtype=0), moe.MOE_ENOTSUP),        # int4 needs bf16
+    (dict(wquant=1, d_model=192), moe.MOE_ENOTSUP),    # K % 128 != 0
+    (dict(wquant=1, d_ff=320), moe.MOE_ENOTSUP),
 ]
 
 
 def _prob(**kw):
     base = dict(T=16, d_model=128, n_experts=4, top_k=2, d_ff=256,
                 n_shared=0, capacity=0, act=moe.MOE_ACT_SWIGLU,
-                dtype=moe.MOE_DTYPE_BF16, aux_coef=0.01)
+                dtype=moe.MOE_DTYPE_BF16, aux_coef=0.01, wquant=0)
     base.update(kw)
     return binding.moe_problem(*[base[f] for f, _ in
                                  binding.moe_problem._fields_])
@@ -168,6 +172,45 @@ def test_weights_validation():
             moe.MOE_EINVAL
     assert lib.moe_expert_ffn(ctypes.byref(sw), f, f, f, None, f, f, big,
                               None) == moe.MOE_EINVAL
+
+
+def test_int4_weights_need_their_scales():
+    lib = binding._lib
+    big = 1 << 40
+    f = 0x1000
+    W = binding.moe_expert_weights
+    sw = _prob(wquant=1)
+    ge = _prob(wquant=1, act=moe.MOE_ACT_GELU, n_shared=1)
+    cases = [
+        (sw, W(f, f, f, None, None, None, None, None, None, None,
+               None, f, f)),                            # no w1_q
+        (sw, W(f, f, f, None, None, None, None, None, None, None,
+               f, None, f)),                            # no w_up_q
+        (sw, W(f, f, f, None, None, None, None, None, None, None,
+               f, f, None)),                            # no w2_q
+        (ge, W(f, None, f, f, f, f, None, f, f, f,
+               f, None, f, None, None, f)),             # no shared_w1_q
+    ]
+    for p, w in cases:
+        assert lib.moe_expert_ffn(ctypes.byref(p), f, f, f, ctypes.byref(w),
+                                  f, f, big, None) == moe.MOE_EINVAL
+        assert lib.moe_expert_up(ctypes.byref(p), f, f, f, ctypes.byref(w),
+                                 f, None) == moe.MOE_EINVAL
+
+
+def test_quantize_int4_validation():
+    lib = binding._lib
+    f = 0x1000
+    assert lib.moe_quantize_int4(f, -1, 128, f, f, None) == moe.MOE_EINVAL
+    assert lib.moe_quantize_int4(f, 4, 64, f, f, None) == moe.MOE_ENOTSUP
+    assert lib.moe_quantize_int4(f, 4, 0, f, f, None) == moe.MOE_ENOTSUP
+    assert lib.moe_quantize_int4(None, 4, 128, f, f, None) == moe.MOE_EINVAL
+    assert lib.moe_quantize_int4(f, 4, 128, None, f, None) == moe.MOE_EINVAL
+    assert lib.moe_quantize_int4(f, 4, 128, f, None, None) == moe.MOE_EINVAL
+    assert lib.moe_quantize_int4(f, 1 << 40, 128, f, f, None) == \
+        moe.MOE_ENOTSUP
+    # nothing to do: OK without touching any pointer or the device
+    assert lib.moe_quantize_int4(None, 0, 128, None, None, None) == moe.MOE_OK
 
 
 def test_workspace_too_small_or_misaligned():
