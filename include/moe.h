@@ -122,11 +122,11 @@ typedef struct moe_problem {
  *   in shared_w1 / shared_w_up / shared_w2 / shared_b1 / shared_b2.
  *
  * With wquant = MOE_WQUANT_INT4 the matrices w1, w_up, w2 (and the shared
- * ones) hold 4-bit codes as written by moe_quantize_int4 (uint8
- * [rows, K/2] for a [rows, K] matrix, stacked over experts), and *_q point
- * to their float32 [rows, K/128, 2] (scale, offset) pairs; the weight is
- * offset + code * scale.  Biases stay in the problem dtype.  The *_q
- * pointers are ignored (may be NULL) without quantisation.
+ * ones) hold 4-bit codes as written by moe_quantize_int4 for the stacked
+ * [E*N, K] matrix (E*N*K/2 bytes), and *_q point to their (scale, offset)
+ * pairs (E*N*(K/128)*2 float32), in that function's tiled order; the
+ * weight is offset + code * scale.  Biases stay in the problem dtype.  The
+ * *_q pointers are ignored (may be NULL) without quantisation.
  */
 typedef struct moe_expert_weights {
   const void* w1;
@@ -290,18 +290,28 @@ int32_t moe_layer_forward(const moe_problem* p, const void* x,
  * Group-wise 4-bit round-to-nearest quantisation of a bf16 weight matrix
  * ([LBS] Production Considerations, Quantization for MoE: 4-bit expert
  * weights cut Mixtral 8x7B's weights from about 93 GB to about 26 GB).
- *   w        [rows, K] bf16 input (K a positive multiple of 128).
- *   codes    [rows, K/2] uint8 output.  Per group of 128 consecutive
- *            weights of a row: lo = min, hi = max, scale = (hi - lo) / 15,
+ *   w        [rows, K] bf16 input; rows a multiple of 16 (stacked expert
+ *            matrices [E, N, K] count as E*N rows), K a positive multiple
+ *            of 128.
+ *   codes    rows*K/2 bytes output.  Per group of 128 consecutive weights
+ *            of a row: lo = min, hi = max, scale = (hi - lo) / 15,
  *            code = rint((w - lo) / scale) clamped to 0..15, ties to even,
  *            in float32 with correctly rounded division; a constant group
- *            gets scale 0 and code 0.  Eight consecutive weights k0..k7
- *            share one little-endian 32-bit word: nibble i holds k_(2i)
- *            for i < 4 and k_(2(i-4)+1) for i >= 4.
- *   qparams  [rows, K/128, 2] float32 output: (scale, lo) per group.
+ *            gets scale 0 and code 0.  The weight is lo + code * scale.
+ *            Storage (the GEMM's operand order): one 1024-byte tile per 16
+ *            rows x one group, tile (r/16, g) at ((r/16)*(K/128) + g)*1024;
+ *            in a tile, 16-byte slot m = r%16 + 16*kq holds row r's
+ *            weights kq*32 .. kq*32+31 of the group as four little-endian
+ *            32-bit words (word h: weights kq*32 + 8h + 0..7); in a word of
+ *            eight consecutive weights k0..k7, nibble i holds k_(2i) for
+ *            i < 4 and k_(2(i-4)+1) for i >= 4.
+ *   qparams  rows*(K/128)*2 float32 output: one 128-byte tile per 16 rows x
+ *            one group, at ((r/16)*(K/128) + g)*16 + r%16 the pair
+ *            (scale, lo) of row r.
  * rows may be 0.  Returns MOE_EINVAL for null pointers or rows < 0,
- * MOE_ENOTSUP when K is not a positive multiple of 128 or rows * K / 8
- * reaches 2^32 (split larger matrices by rows).
+ * MOE_ENOTSUP when K is not a positive multiple of 128, rows is not a
+ * multiple of 16, or rows * K / 8 reaches 2^32 (split larger matrices by
+ * rows).
  */
 int32_t moe_quantize_int4(const void* w, int64_t rows, int32_t K,
                           void* codes, float* qparams, hipStream_t stream);

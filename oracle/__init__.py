@@ -39,5 +39,6 @@ from .moe import (  # noqa: F401
     dequantize_int4,
     pack_int4,
     unpack_int4,
+    pack_qparams,
     int4_bytes,
 )

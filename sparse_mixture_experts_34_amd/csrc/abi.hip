@@ -368,7 +368,7 @@ int32_t moe_layer_forward(const moe_problem* p, const void* x,
 int32_t moe_quantize_int4(const void* w, int64_t rows, int32_t K,
                           void* codes, float* qparams, hipStream_t stream) {
   if (rows < 0) return MOE_EINVAL;
-  if (K <= 0 || K % MOE_Q4_GROUP != 0) return MOE_ENOTSUP;
+  if (K <= 0 || K % MOE_Q4_GROUP != 0 || rows % 16 != 0) return MOE_ENOTSUP;
   if (rows > 0 && (!w || !codes || !qparams)) return MOE_EINVAL;
   // one thread per code word: the grid (rows * K / 8 threads) must fit the
   // 32-bit dispatch size

@@ -269,7 +269,10 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
 // The stream schedule's work split (16*CG columns per workgroup, 4 waves
 // splitting K) with one K step per quantisation group of 128 weights.  Lane
 // (col, kq) takes weights kq*32 .. kq*32+31 of the group in its row: 16
-// code bytes, i.e. four words, each word one 16x16x32 MFMA B operand.  A
+// code bytes, i.e. four words, each word one 16x16x32 MFMA B operand.  The
+// codes are stored tiled in exactly this lane order (1024 bytes per 16 rows
+// x group), so a wave reads a tile with one fully coalesced load, and the
+// 16 rows' (scale, offset) pairs with one 128-byte line.  A
 // word becomes eight bf16 with one shift and one and-or per pair: the bits
 // 0x4300 | q are exactly the bf16 number 128 + q, so the MFMAs sum
 // x * (128 + q) over the group, and one more MFMA per 32 weights against
@@ -352,9 +355,12 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_q4_kernel(FfnArgs a)
   for (int m = 0; m < NMAT; ++m)
 #pragma unroll
     for (int c = 0; c < CG; ++c) {
-      const int n = min(n0 + 16 * c + col, N - 1);
-      crow[m][c] = cm[m] + (size_t)n * (K / 2) + (size_t)s_beg * (Q4_GROUP / 2) + kq * 16;
-      qrow[m][c] = (const float2*)qm[m] + (size_t)n * ngroups + s_beg;
+      // 16-row block of column group c (a partial last group re-reads the
+      // last block and stores nothing for it)
+      const int nb = min((n0 + 16 * c) >> 4, N / 16 - 1);
+      const size_t tile = (size_t)nb * ngroups + s_beg;
+      crow[m][c] = cm[m] + tile * 1024 + lane * 16;
+      qrow[m][c] = (const float2*)qm[m] + tile * 16 + col;
     }
   V16 ones;
   ones.u = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
@@ -381,8 +387,8 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_q4_kernel(FfnArgs a)
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int c = 0; c < CG; ++c) {
-          b.code[m][c] = ldg16(crow[m][c] + (size_t)s * (Q4_GROUP / 2));
-          b.qp[m][c] = qrow[m][c][s];
+          b.code[m][c] = ldg16(crow[m][c] + (size_t)s * 1024);
+          b.qp[m][c] = qrow[m][c][s * 16];
         }
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
@@ -1019,7 +1025,7 @@ hipError_t launch_q4(const FfnArgs& a, hipStream_t s) {
   dim3 grid((N + 16 * cg - 1) / (16 * cg), G);
   const bool rt1 = a.T <= 16;   // a token picks an expert at most once
   if (cg == 2) {
-    if (rt1) ffn_stream_q4_kernel<MODE, 1, 2, 3><<<grid, ST_WAVES * 64, 0, s>>>(a);
+    if (rt1) ffn_stream_q4_kernel<MODE, 1, 2, 2><<<grid, ST_WAVES * 64, 0, s>>>(a);
     else ffn_stream_q4_kernel<MODE, 2, 2, 2><<<grid, ST_WAVES * 64, 0, s>>>(a);
   } else {
     if (rt1) ffn_stream_q4_kernel<MODE, 1, 1, 3><<<grid, ST_WAVES * 64, 0, s>>>(a);

@@ -12,7 +12,11 @@
 //
 // Word layout: nibble i holds weight 2i for i < 4 and weight 2(i-4)+1 for
 // i >= 4, so a word turns into bf16 MFMA operand pairs (even weight low,
-// odd weight high) with one shift and one mask per pair.
+// odd weight high) with one shift and one mask per pair.  Words are stored
+// in the GEMM's operand order: a 1024-byte tile per 16 rows x one group,
+// slot m = row%16 + 16*kq holding weights kq*32..kq*32+31 of the group as
+// words h = 0..3, so one wave reads a tile with one contiguous load; the
+// (scale, offset) pairs of the 16 rows of a group share a 128-byte tile.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -62,10 +66,13 @@ __global__ __launch_bounds__(256) void quantize_int4_kernel(
     const int nib = (i & 1) ? 4 + (i >> 1) : (i >> 1);
     word |= (uint32_t)q << (4 * nib);
   }
-  codes[(size_t)row * (K / 8) + (size_t)gi * QW + j] = word;
+  const size_t tile = (size_t)(row >> 4) * gpr + gi;
+  const int slot = (int)(row & 15) + 16 * (j >> 2);
+  codes[tile * 256 + slot * 4 + (j & 3)] = word;
   if (j == 0) {
-    qparams[2 * g] = s;
-    qparams[2 * g + 1] = lo;
+    const size_t qi = (tile * 16 + (size_t)(row & 15)) * 2;
+    qparams[qi] = s;
+    qparams[qi + 1] = lo;
   }
 }
 

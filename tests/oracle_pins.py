@@ -552,11 +552,28 @@ def pin_int4_constant_group():
 
 def pin_int4_packing_hand_example():
     g = _golden("int4_format.json")
-    packed = oracle.pack_int4(np.array([g["codes"]], np.uint8))
-    assert packed.tolist() == [g["packed_bytes"]]
+    for ex in g["tile_examples"]:
+        rows = 32
+        q = np.zeros((rows, ex["K"]), np.uint8)
+        q[ex["row"], ex["k0"]:ex["k0"] + 8] = g["codes"]
+        b = oracle.pack_int4(q).reshape(-1)
+        nz = np.nonzero(b)[0].tolist()
+        o = ex["byte_offset"]
+        assert nz == list(range(o, o + 4)), (ex, nz)
+        assert b[o:o + 4].tolist() == g["packed_bytes"]
+    qe = g["qparams_example"]
+    sc = np.zeros((32, qe["K"] // 128), np.float32)
+    off = np.zeros_like(sc)
+    sc[qe["row"], qe["group"]] = 3.0
+    off[qe["row"], qe["group"]] = -7.0
+    flat = oracle.pack_qparams(sc, off).reshape(-1)
+    assert np.nonzero(flat)[0].tolist() == [qe["float_index"],
+                                            qe["float_index"] + 1]
+    assert flat[qe["float_index"]] == 3.0
+    assert flat[qe["float_index"] + 1] == -7.0
     rng = _rng(43)
-    q = rng.integers(0, 16, (5, 256)).astype(np.uint8)
-    assert (oracle.unpack_int4(oracle.pack_int4(q), 256) == q).all()
+    q = rng.integers(0, 16, (48, 384)).astype(np.uint8)
+    assert (oracle.unpack_int4(oracle.pack_int4(q), 48, 384) == q).all()
 
 
 def pin_int4_footprint_matches_page():

@@ -202,11 +202,12 @@ def test_quantize_int4_validation():
     lib = binding._lib
     f = 0x1000
     assert lib.moe_quantize_int4(f, -1, 128, f, f, None) == moe.MOE_EINVAL
-    assert lib.moe_quantize_int4(f, 4, 64, f, f, None) == moe.MOE_ENOTSUP
-    assert lib.moe_quantize_int4(f, 4, 0, f, f, None) == moe.MOE_ENOTSUP
-    assert lib.moe_quantize_int4(None, 4, 128, f, f, None) == moe.MOE_EINVAL
-    assert lib.moe_quantize_int4(f, 4, 128, None, f, None) == moe.MOE_EINVAL
-    assert lib.moe_quantize_int4(f, 4, 128, f, None, None) == moe.MOE_EINVAL
+    assert lib.moe_quantize_int4(f, 16, 64, f, f, None) == moe.MOE_ENOTSUP
+    assert lib.moe_quantize_int4(f, 16, 0, f, f, None) == moe.MOE_ENOTSUP
+    assert lib.moe_quantize_int4(f, 4, 128, f, f, None) == moe.MOE_ENOTSUP
+    assert lib.moe_quantize_int4(None, 16, 128, f, f, None) == moe.MOE_EINVAL
+    assert lib.moe_quantize_int4(f, 16, 128, None, f, None) == moe.MOE_EINVAL
+    assert lib.moe_quantize_int4(f, 16, 128, f, None, None) == moe.MOE_EINVAL
     assert lib.moe_quantize_int4(f, 1 << 40, 128, f, f, None) == \
         moe.MOE_ENOTSUP
     # nothing to do: OK without touching any pointer or the device

@@ -32,16 +32,17 @@ def gpu_quantize(w):
 
 
 def oracle_quantize(w2d):
+    """Stored code bytes and (scale, offset) floats, both flat, in the
+    library's tiled order."""
     q, s, o = oracle.quantize_int4(w2d)
-    return oracle.pack_int4(q), s, o
+    return (oracle.pack_int4(q).reshape(-1),
+            oracle.pack_qparams(s, o).reshape(-1))
 
 
 def assert_same_quant(codes, qp, w_host):
-    c_o, s_o, o_o = oracle_quantize(w_host)
-    assert (host(codes).reshape(c_o.shape) == c_o).all()
-    qh = host(qp).reshape(s_o.shape + (2,))
-    assert (qh[..., 0].view(np.uint32) == s_o.view(np.uint32)).all()
-    assert (qh[..., 1].view(np.uint32) == o_o.view(np.uint32)).all()
+    c_o, q_o = oracle_quantize(w_host)
+    assert (host(codes).reshape(-1) == c_o).all()
+    assert (host(qp).reshape(-1).view(np.uint32) == q_o.view(np.uint32)).all()
 
 
 def _test_matrix(rows, K, seed):
@@ -56,15 +57,17 @@ def _test_matrix(rows, K, seed):
     return w.to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("rows,K", [(1, 128), (7, 384), (33, 1024),
-                                    (64, 4096), (3, 14336)])
+@pytest.mark.parametrize("rows,K", [(16, 128), (32, 384), (48, 1024),
+                                    (64, 4096), (16, 14336)])
 def test_quantize_bit_exact(rows, K):
     w = _test_matrix(rows, K, seed=rows * 7 + K)
     codes, qp = gpu_quantize(w.cuda())
     assert_same_quant(codes, qp, w.float().numpy())
 
 
-def test_quantize_full_size_sampled_rows():
+def test_quantize_full_size_sampled_blocks():
+    # whole 16-row blocks (the storage tiles cover 16 rows) sampled from
+    # the stacked full-size matrices
     wl = synth.WORKLOADS["mixtral_decode"]
     inp = make(wl, margin=False)
     rng = np.random.default_rng(5)
@@ -72,15 +75,17 @@ def test_quantize_full_size_sampled_rows():
         w = inp[name]
         codes, qp = gpu_quantize(w)
         K = w.shape[-1]
-        flat_w = w.reshape(-1, K)
-        rows = np.unique(np.concatenate([[0, flat_w.shape[0] - 1],
-                                         rng.choice(flat_w.shape[0], 64,
-                                                    replace=False)]))
-        ri = torch.as_tensor(rows, device=w.device)
-        assert_same_quant(codes.reshape(-1, K // 2)[ri],
-                          qp.reshape(-1, K // 128, 2)[ri],
-                          host(flat_w[ri]))
-        log(f"  {name}: {len(rows)} sampled rows bit-exact")
+        G = K // 128
+        nblk = w.numel() // K // 16
+        blocks = np.unique(np.concatenate([[0, nblk - 1],
+                                           rng.choice(nblk, 12,
+                                                      replace=False)]))
+        bi = torch.as_tensor(blocks, device=w.device)
+        c_blk = codes.reshape(nblk, G * 1024)[bi]
+        q_blk = qp.reshape(nblk, G * 32)[bi]
+        w_rows = host(w.reshape(nblk, 16, K)[bi]).reshape(-1, K)
+        assert_same_quant(c_blk, q_blk, w_rows)
+        log(f"  {name}: {len(blocks)} sampled 16-row blocks bit-exact")
     del inp
     torch.cuda.empty_cache()
 

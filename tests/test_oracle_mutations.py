@@ -245,12 +245,26 @@ def m_q4_dequant_no_offset(mp):
     _patch(mp, "dequantize_int4", dequantize_int4)
 
 
-def m_q4_pack_natural_order(mp):
+def m_q4_pack_untiled(mp):
+    # the right words, stored row by row instead of in MFMA tiles
     def pack_int4(q):
-        q = np.asarray(q, np.uint8)
+        q = np.asarray(q, np.uint32)
         rows, K = q.shape
-        return (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+        k8 = q.reshape(rows, K // 8, 8)
+        word = np.zeros((rows, K // 8), np.uint32)
+        for i in range(4):
+            word |= k8[:, :, 2 * i] << np.uint32(4 * i)
+            word |= k8[:, :, 2 * i + 1] << np.uint32(16 + 4 * i)
+        return word.astype("<u4").view(np.uint8).reshape(rows, K // 2)
     _patch(mp, "pack_int4", pack_int4)
+
+
+def m_q4_qparams_row_major(mp):
+    def pack_qparams(scale, offset):
+        return np.stack([np.asarray(scale, np.float32),
+                         np.asarray(offset, np.float32)], axis=-1)
+    _patch(mp, "pack_qparams", pack_qparams)
+
 
 MUTATIONS = [m_no_renormalise, m_tie_to_higher_index, m_bias_in_gates,
              m_capacity_by_slot, m_keep_last, m_renormalise_survivors,
@@ -258,7 +272,8 @@ MUTATIONS = [m_no_renormalise, m_tie_to_higher_index, m_bias_in_gates,
              m_swap_gate_up, m_aux_post_capacity, m_aux_no_E,
              m_capacity_ceil, m_softmax_no_shift, m_no_shared,
              m_token_from_assignment_by_E, m_q4_floor, m_q4_sixteen_steps,
-             m_q4_dequant_no_offset, m_q4_pack_natural_order]
+             m_q4_dequant_no_offset, m_q4_pack_untiled,
+             m_q4_qparams_row_major]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=[m.__name__ for m in
