@@ -27,6 +27,8 @@ from .moe import (  # noqa: F401
     gelu,
     silu,
     softmax,
+    sigmoid,
+    update_select_bias,
     route,
     topk_margin,
     dispatch,

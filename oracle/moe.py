@@ -82,6 +82,19 @@ def softmax(logits):
 # Step 1: route
 # ---------------------------------------------------------------------------
 
+def sigmoid(z):
+    """Logistic sigmoid 1 / (1 + e^-z), the per-expert scoring function
+    ([FA] "The knobs": per-expert sigmoid scoring as the alternative to a
+    softmax over all experts).  Float64."""
+    z = np.asarray(z, F64)
+    out = np.empty_like(z)
+    pos = z >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-z[pos]))
+    ez = np.exp(z[~pos])
+    out[~pos] = ez / (1.0 + ez)
+    return out
+
+
 def _logits64(x, w_router, router_bias=None):
     l = np.asarray(x, F64) @ np.asarray(w_router, F64).T
     if router_bias is not None:
@@ -89,8 +102,9 @@ def _logits64(x, w_router, router_bias=None):
     return l
 
 
-def route(x, w_router, k, router_bias=None, select_bias=None):
-    """Router linear, softmax, top-k and renormalised gates.
+def route(x, w_router, k, router_bias=None, select_bias=None,
+          scoring="softmax", renormalize=True):
+    """Router linear, scoring, top-k and (renormalised) gates.
 
     * logits = x . W_r^T (+ router bias): one linear layer from the hidden
       state to E scores ([RC] "How a sparse MoE layer works"; [LBS]
@@ -107,31 +121,61 @@ def route(x, w_router, k, router_bias=None, select_bias=None):
     * gate[t, j] = probs[t, idx[t, j]] / sum over the k chosen probs
       ([RC]; [LBS] "Gating Mechanism"; [GN] "The router"; [FA] "Concept").
 
+    Variants ([FA] "The knobs": scoring by a softmax over all experts or a
+    per-expert sigmoid, and whether the chosen gates are renormalised to
+    sum to 1):
+    * ``scoring="sigmoid"``: scores = sigmoid(logits) per expert.  Without
+      a selection bias the key is the logit (the same order, sigmoid being
+      monotone); with one, the bias is added to the float32 score, the
+      scale DeepSeek-V3's routing scores live on ([GN] "DeepSeek-V3").
+      ``probs`` (the P of the aux loss) are each token's scores divided by
+      their sum over all experts, so they sum to 1 as softmax probs do.
+    * ``renormalize=False``: gate[t, j] is the chosen score itself
+      (softmax prob or sigmoid score), not divided by the chosen sum.
+
     Returns a dict: logits (float32 [T,E]), keys (float32 [T,E]),
-    idx (int64 [T,k]), gate (float64 [T,k]), probs (float64 [T,E]).
+    idx (int64 [T,k]), gate (float64 [T,k]), probs (float64 [T,E]),
+    scores (float64 [T,E]).
     """
     x = np.asarray(x)
     T = x.shape[0]
     E = np.asarray(w_router).shape[0]
     if not 1 <= k <= E:
         raise ValueError("route: need 1 <= k <= E")
+    if scoring not in ("softmax", "sigmoid"):
+        raise ValueError("route: scoring is softmax or sigmoid")
     logits = _logits64(x, w_router, router_bias).astype(np.float32)
-    keys = logits.copy()
-    if select_bias is not None:
-        keys = (keys + np.asarray(select_bias, np.float32)).astype(np.float32)
-    probs = softmax(logits)
+    if scoring == "softmax":
+        scores = softmax(logits)
+        probs = scores
+        keys = logits.copy()
+        if select_bias is not None:
+            keys = (keys + np.asarray(select_bias, np.float32)).astype(
+                np.float32)
+    else:
+        scores = sigmoid(logits)
+        probs = scores / scores.sum(axis=1, keepdims=True) if T else scores
+        if select_bias is None:
+            keys = logits.copy()
+        else:
+            keys = (scores.astype(np.float32) +
+                    np.asarray(select_bias, np.float32)).astype(np.float32)
     idx = np.zeros((T, k), np.int64)
     for t in range(T):
         # sort by key descending, then by expert index ascending
         order = sorted(range(E), key=lambda e: (-float(keys[t, e]), e))
         idx[t] = order[:k]
-    chosen = np.take_along_axis(probs, idx, axis=1)
-    gate = chosen / chosen.sum(axis=1, keepdims=True) if T else chosen
+    chosen = np.take_along_axis(scores, idx, axis=1)
+    if renormalize and T:
+        gate = chosen / chosen.sum(axis=1, keepdims=True)
+    else:
+        gate = chosen
     return {"logits": logits, "keys": keys, "idx": idx, "gate": gate,
-            "probs": probs}
+            "probs": probs, "scores": scores}
 
 
-def topk_margin(x, w_router, k, router_bias=None, select_bias=None):
+def topk_margin(x, w_router, k, router_bias=None, select_bias=None,
+                scoring="softmax"):
     """Smallest gap between consecutive sorted selection keys around the
     top-k boundary, per token, in float64 (no float32 rounding).
 
@@ -143,6 +187,8 @@ def topk_margin(x, w_router, k, router_bias=None, select_bias=None):
     """
     keys = _logits64(x, w_router, router_bias)
     if select_bias is not None:
+        if scoring == "sigmoid":
+            keys = sigmoid(keys)
         keys = keys + np.asarray(select_bias, F64)
     E = keys.shape[1]
     s = -np.sort(-keys, axis=1)
@@ -339,7 +385,8 @@ def aux_loss(counts, probs, alpha):
 
 def layer_forward(x, w_router, weights, *, k, cap, act, n_shared=0,
                   alpha=0.01, router_bias=None, select_bias=None,
-                  residual=True, tokens=None):
+                  residual=True, tokens=None, scoring="softmax",
+                  renormalize=True):
     """Route, dispatch, expert FFNs, combine and aux loss, in that order.
 
     With ``tokens`` the routing, dispatch and aux loss still cover every
@@ -350,7 +397,7 @@ def layer_forward(x, w_router, weights, *, k, cap, act, n_shared=0,
     x = np.asarray(x)
     T = x.shape[0]
     E = np.asarray(w_router).shape[0]
-    r = route(x, w_router, k, router_bias, select_bias)
+    r = route(x, w_router, k, router_bias, select_bias, scoring, renormalize)
     dsp = dispatch(r["idx"], E, cap)
     y = expert_ffn(x, dsp["perm"], dsp["offsets"], weights, act, k,
                    n_shared, tokens)
@@ -363,6 +410,22 @@ def layer_forward(x, w_router, weights, *, k, cap, act, n_shared=0,
                 "prob_mean": r["probs"].mean(axis=0) if T else
                 np.zeros(E, F64)})
     return res
+
+
+def update_select_bias(select_bias, counts, gamma):
+    """One step of the auxiliary-loss-free balancing of [GN] "DeepSeek-V3":
+    the selection bias of an over-loaded expert goes down and that of an
+    under-loaded expert goes up.  The page gives no step rule; the plain
+    reading kept here moves every bias by a fixed gamma towards balance:
+    b_e <- b_e + gamma * sign(mean count - count_e), where count_e are the
+    pre-capacity assignments of the step and the mean is sum(counts) / E.
+    The sign is decided exactly (sum(counts) - E * count_e in integers);
+    the update is one float32 addition."""
+    c = np.asarray(counts, np.int64)
+    E = c.shape[0]
+    sgn = np.sign(c.sum() - E * c).astype(np.float32)
+    b = np.asarray(select_bias, np.float32)
+    return (b + np.float32(gamma) * sgn).astype(np.float32)
 
 
 # ---------------------------------------------------------------------------

@@ -482,6 +482,114 @@ def pin_param_counts():
 
 
 # ---------------------------------------------------------------------------
+# Routing variants: scoring function, gate normalisation, bias update
+# ---------------------------------------------------------------------------
+
+def pin_sigmoid_scalar():
+    z = np.linspace(-60.0, 60.0, 1201)
+    assert np.allclose(oracle.sigmoid(z), scipy.special.expit(z), rtol=1e-14,
+                       atol=0)
+
+
+def _route_inputs(seed, T=64, d=32, E=8):
+    rng = _rng(seed)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    wr = (rng.standard_normal((E, d)) * 0.3).astype(np.float32)
+    return rng, x, wr
+
+
+def pin_route_raw_softmax_gates():
+    # without renormalisation a gate is the chosen softmax probability
+    _, x, wr = _route_inputs(51)
+    for k in (1, 2, 3):
+        r = oracle.route(x, wr, k, renormalize=False)
+        p = scipy.special.softmax(r["logits"].astype(np.float64), axis=1)
+        assert np.allclose(r["gate"], np.take_along_axis(p, r["idx"], 1),
+                           rtol=1e-12, atol=0)
+        assert (oracle.route(x, wr, k)["idx"] == r["idx"]).all()
+        if k == 1:   # Switch top-1: the gate is the largest probability
+            assert np.allclose(r["gate"][:, 0], p.max(axis=1), rtol=1e-12)
+        assert (r["gate"].sum(axis=1) < 1.0).all()
+
+
+def pin_route_sigmoid_scoring():
+    rng, x, wr = _route_inputs(52)
+    E, k = wr.shape[0], 3
+    rs = oracle.route(x, wr, k, scoring="sigmoid")
+    # sigmoid is monotone: the same choice as softmax scoring
+    assert (rs["idx"] == oracle.route(x, wr, k)["idx"]).all()
+    s = scipy.special.expit(rs["logits"].astype(np.float64))
+    ch = np.take_along_axis(s, rs["idx"], 1)
+    assert np.allclose(rs["gate"].sum(axis=1), 1.0, rtol=1e-12)
+    assert np.allclose(rs["gate"] * ch.sum(1, keepdims=True), ch, rtol=1e-12)
+    raw = oracle.route(x, wr, k, scoring="sigmoid", renormalize=False)
+    assert np.allclose(raw["gate"], ch, rtol=1e-12)
+    # P rows: the scores scaled to sum to 1
+    assert np.allclose(rs["probs"].sum(axis=1), 1.0, rtol=1e-12)
+    assert np.allclose(rs["probs"] * s.sum(1, keepdims=True), s, rtol=1e-12)
+    # a selection bias lives on the score scale: the choice is the stable
+    # top-k of float32(expit) + bias; gates stay the unbiased scores
+    b = rng.uniform(-0.3, 0.3, E).astype(np.float32)
+    rb = oracle.route(x, wr, k, select_bias=b, scoring="sigmoid")
+    key = (s.astype(np.float32) + b).astype(np.float32)
+    order = np.argsort(-key, axis=1, kind="stable")[:, :k]
+    assert (rb["idx"] == order).all()
+    by_logit = np.argsort(-(rs["logits"] + b), axis=1, kind="stable")[:, :k]
+    assert (by_logit != order).any()          # the two readings differ here
+    chb = np.take_along_axis(s, rb["idx"], 1)
+    assert np.allclose(rb["gate"], chb / chb.sum(1, keepdims=True),
+                       rtol=1e-12)
+
+
+def pin_sigmoid_all_tied_closed_form():
+    # x = 0: every logit 0, every score 1/2: raw gates 1/2, renormalised
+    # gates 1/k, P = 1/E, aux = alpha * k (ties to the lower indices)
+    E, k, T, d, alpha = 6, 2, 10, 16, 0.01
+    x = np.zeros((T, d), np.float32)
+    wr = _rng(53).standard_normal((E, d)).astype(np.float32)
+    raw = oracle.route(x, wr, k, scoring="sigmoid", renormalize=False)
+    assert (raw["gate"] == 0.5).all()
+    assert (raw["idx"] == np.arange(k)).all()
+    w = _swiglu_weights(_rng(54), E, d, 8)
+    o = oracle.layer_forward(x, wr, w, k=k, cap=0, act="swiglu", alpha=alpha,
+                             scoring="sigmoid")
+    assert np.allclose(o["gate"], 1.0 / k)
+    assert np.allclose(o["prob_mean"], 1.0 / E)
+    assert abs(o["aux"] - alpha * k) <= 1e-15
+
+
+def pin_layer_sigmoid_vs_brute_force():
+    # k = E with sigmoid scores: the dense mixture weighted by s / sum(s);
+    # raw gates weight by s itself
+    rng = _rng(55)
+    T, d, E, f = 12, 16, 4, 24
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    wr = (rng.standard_normal((E, d)) * 0.5).astype(np.float32)
+    w = _swiglu_weights(rng, E, d, f)
+    for renorm in (True, False):
+        o = oracle.layer_forward(x, wr, w, k=E, cap=0, act="swiglu",
+                                 scoring="sigmoid", renormalize=renorm)
+        s = scipy.special.expit(o["logits"].astype(np.float64))
+        g = np.take_along_axis(s, o["idx"], 1)
+        if renorm:
+            g = g / g.sum(1, keepdims=True)
+        ref = brute_force_dense(x, o["idx"], g, o["slot_of"], "swiglu", w, E,
+                                E)
+        assert _rel(o["out"], ref) < 1e-12
+
+
+def pin_bias_update_hand_counted():
+    for c in _golden("bias_update_hand_counted.json")["cases"]:
+        b = oracle.update_select_bias(np.array(c["bias"], np.float32),
+                                      c["counts"], c["gamma"])
+        assert b.dtype == np.float32
+        assert np.allclose(b, np.array(c["expected"], np.float32), rtol=0,
+                           atol=1e-7)
+        moved = np.sign(b.astype(np.float64) - np.array(c["bias"], np.float32))
+        assert moved.tolist() == c["signs"]
+
+
+# ---------------------------------------------------------------------------
 # 4-bit expert weights
 # ---------------------------------------------------------------------------
 
