@@ -74,6 +74,9 @@ extern "C" {
 #define MOE_DTYPE_F32 0
 #define MOE_DTYPE_BF16 1
 
+#define MOE_SCORING_SOFTMAX 0 /* softmax over all experts                */
+#define MOE_SCORING_SIGMOID 1 /* per-expert sigmoid                      */
+
 #define MOE_WQUANT_NONE 0 /* expert weights in the problem dtype          */
 #define MOE_WQUANT_INT4 1 /* expert weights as 4-bit codes, see below     */
 #define MOE_Q4_GROUP 128  /* weights per (scale, offset) pair             */
@@ -97,6 +100,15 @@ extern "C" {
  *              weights ([LBS] Production Considerations, Quantization for
  *              MoE); INT4 requires dtype BF16 and d_model, d_ff multiples
  *              of 128.  Zero-initialised structs get NONE.
+ *   scoring    MOE_SCORING_SOFTMAX (default) or MOE_SCORING_SIGMOID
+ *              ([FA] The knobs: softmax over all experts versus a
+ *              per-expert sigmoid).  With sigmoid scores a selection bias
+ *              is added to the float32 score (not the logit); without one
+ *              the choice is on the logit (the same order).  The P of the
+ *              aux loss is then each token's scores scaled to sum to 1.
+ *   raw_gates  0 (default): the chosen scores are renormalised to sum to 1;
+ *              1: a gate is the chosen score itself ([FA] The knobs,
+ *              norm_topk_prob).
  */
 typedef struct moe_problem {
   int32_t T;
@@ -110,6 +122,8 @@ typedef struct moe_problem {
   int32_t dtype;
   float aux_coef;
   int32_t wquant;
+  int32_t scoring;
+  int32_t raw_gates;
 } moe_problem;
 
 /*
@@ -315,6 +329,25 @@ int32_t moe_layer_forward(const moe_problem* p, const void* x,
  */
 int32_t moe_quantize_int4(const void* w, int64_t rows, int32_t K,
                           void* codes, float* qparams, hipStream_t stream);
+
+/*
+ * One step of auxiliary-loss-free balancing ([GN] DeepSeek-V3: the selection
+ * bias of an over-loaded expert decreases, that of an under-loaded expert
+ * increases, adjusted during training):
+ *   select_bias[e] += gamma * sign(mean count - counts[e])
+ * with mean count = sum(counts) / E; the sign is decided exactly in integer
+ * arithmetic (sum(counts) - E * counts[e]), the update is one float32
+ * addition.
+ *   counts       [E] int32 input: pre-capacity assignments per expert, as
+ *                written by moe_dispatch.
+ *   select_bias  [E] float32, updated in place.
+ *   gamma        bias update speed (finite).
+ * Only n_experts of `p` is read.  Returns MOE_EINVAL for a bad problem,
+ * null pointers or a non-finite gamma.
+ */
+int32_t moe_update_select_bias(const moe_problem* p, const int32_t* counts,
+                               float* select_bias, float gamma,
+                               hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char* moe_status_string(int32_t status);

@@ -27,6 +27,8 @@ MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_ACT_GELU, MOE_ACT_SWIGLU = 0, 1
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 MOE_WQUANT_NONE, MOE_WQUANT_INT4 = 0, 1
+MOE_SCORING_SOFTMAX, MOE_SCORING_SIGMOID = 0, 1
+SCORING = {"softmax": MOE_SCORING_SOFTMAX, "sigmoid": MOE_SCORING_SIGMOID}
 MOE_Q4_GROUP = 128
 WQUANT = {None: MOE_WQUANT_NONE, "none": MOE_WQUANT_NONE,
           "int4": MOE_WQUANT_INT4}
@@ -47,7 +49,8 @@ class moe_problem(ctypes.Structure):
                 ("d_ff", ctypes.c_int32), ("n_shared", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("act", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("aux_coef", ctypes.c_float),
-                ("wquant", ctypes.c_int32)]
+                ("wquant", ctypes.c_int32), ("scoring", ctypes.c_int32),
+                ("raw_gates", ctypes.c_int32)]
 
 
 class moe_expert_weights(ctypes.Structure):
@@ -76,6 +79,7 @@ _SIGS = {
     "moe_layer_forward": (_I32, [_P, _V, _V, _V, _V, _W, _V, _V, _V, _V, _V,
                                  _V, _SZ, _V]),
     "moe_quantize_int4": (_I32, [_V, ctypes.c_int64, _I32, _V, _V, _V]),
+    "moe_update_select_bias": (_I32, [_P, _V, _V, ctypes.c_float, _V]),
     "moe_status_string": (ctypes.c_char_p, [_I32]),
 }
 EXPORTS = tuple(_SIGS)
@@ -128,13 +132,16 @@ def _check(status, where):
 
 def problem(T, d_model, n_experts, top_k, d_ff, *, n_shared=0, capacity=0,
             act="swiglu", dtype="bf16", aux_coef=0.01,
-            wquant=None) -> moe_problem:
+            wquant=None, scoring="softmax",
+            raw_gates=False) -> moe_problem:
     return moe_problem(T, d_model, n_experts, top_k, d_ff, n_shared, capacity,
                        ACT[act] if isinstance(act, str) else act,
                        DTYPE[dtype] if isinstance(dtype, str) else dtype,
                        aux_coef,
                        WQUANT[wquant] if not isinstance(wquant, int)
-                       else wquant)
+                       else wquant,
+                       SCORING[scoring] if isinstance(scoring, str)
+                       else scoring, int(raw_gates))
 
 
 def problem_for(wl) -> moe_problem:
@@ -142,7 +149,9 @@ def problem_for(wl) -> moe_problem:
     return problem(wl.T, wl.d_model, wl.n_experts, wl.top_k, wl.d_ff,
                    n_shared=wl.n_shared, capacity=wl.capacity, act=wl.act,
                    dtype=wl.dtype, aux_coef=wl.aux_coef,
-                   wquant=getattr(wl, "wquant", None))
+                   wquant=getattr(wl, "wquant", None),
+                   scoring=getattr(wl, "scoring", "softmax"),
+                   raw_gates=getattr(wl, "raw_gates", False))
 
 
 def expert_weights(w: dict) -> moe_expert_weights:
@@ -263,6 +272,13 @@ def moe_quantize_int4(w, codes, qparams, stream=None):
     _check(_lib.moe_quantize_int4(_ptr(w), rows, K, _ptr(codes),
                                   _ptr(qparams), _stream(stream)),
            "moe_quantize_int4")
+
+
+def moe_update_select_bias(p, counts, select_bias, gamma, stream=None):
+    _check(_lib.moe_update_select_bias(ctypes.byref(p), _ptr(counts),
+                                       _ptr(select_bias), gamma,
+                                       _stream(stream)),
+           "moe_update_select_bias")
 
 
 QUANT_MATRICES = ("w1", "w2", "w_gate", "w_up", "w_down", "shared_w1",

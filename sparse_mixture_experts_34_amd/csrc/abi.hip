@@ -74,6 +74,9 @@ int32_t check_problem(const moe_problem* p) {
   if (!isfinite(p->aux_coef)) return MOE_EINVAL;
   if (p->wquant != MOE_WQUANT_NONE && p->wquant != MOE_WQUANT_INT4)
     return MOE_EINVAL;
+  if (p->scoring != MOE_SCORING_SOFTMAX && p->scoring != MOE_SCORING_SIGMOID)
+    return MOE_EINVAL;
+  if (p->raw_gates != 0 && p->raw_gates != 1) return MOE_EINVAL;
   if (p->wquant == MOE_WQUANT_INT4 &&
       (p->dtype != MOE_DTYPE_BF16 || p->d_model % MOE_Q4_GROUP != 0 ||
        p->d_ff % MOE_Q4_GROUP != 0))
@@ -208,7 +211,8 @@ int32_t moe_route(const moe_problem* p, const void* x, const float* w_router,
                                        stream));
   MOE_TRY(launch_route_select_from(part, L.ksplit, router_bias, select_bias,
                                    logits, topk_idx, topk_gate, rpart, p->T,
-                                   p->n_experts, p->top_k, stream));
+                                   p->n_experts, p->top_k, p->scoring,
+                                   p->raw_gates, stream));
   MOE_TRY(launch_prob_mean(rpart, prob_mean, L.nrb, p->T, p->n_experts,
                            stream));
   return MOE_OK;
@@ -336,7 +340,8 @@ int32_t moe_layer_forward(const moe_problem* p, const void* x,
                                        stream));
   MOE_TRY(launch_route_select_from(part, L.ksplit, router_bias, select_bias,
                                    nullptr, idx, gate, rpart, p->T,
-                                   p->n_experts, p->top_k, stream));
+                                   p->n_experts, p->top_k, p->scoring,
+                                   p->raw_gates, stream));
   DispatchArgs a;
   a.idx = idx;
   a.prob_mean_in = nullptr;
@@ -374,6 +379,16 @@ int32_t moe_quantize_int4(const void* w, int64_t rows, int32_t K,
   // 32-bit dispatch size
   if ((long long)rows * (K / 8) >= (1LL << 32) - 256) return MOE_ENOTSUP;
   return status_of(launch_quantize_int4(w, rows, K, codes, qparams, stream));
+}
+
+int32_t moe_update_select_bias(const moe_problem* p, const int32_t* counts,
+                               float* select_bias, float gamma,
+                               hipStream_t stream) {
+  int32_t st = check_problem(p);
+  if (st) return st;
+  if (!counts || !select_bias || !isfinite(gamma)) return MOE_EINVAL;
+  return status_of(launch_update_select_bias(counts, select_bias, gamma,
+                                             p->n_experts, stream));
 }
 
 const char* moe_status_string(int32_t status) {

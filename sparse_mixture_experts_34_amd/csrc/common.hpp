@@ -36,6 +36,11 @@ __device__ __forceinline__ float silu(float z) {
   return z / (1.0f + __expf(-z));
 }
 
+// Logistic sigmoid 1 / (1 + e^-z) (per-expert router scoring).
+__device__ __forceinline__ float sigmoid_f(float z) {
+  return 1.0f / (1.0f + __expf(-z));
+}
+
 // --- 16-byte vector type punning ----------------------------------------
 union V16 {
   u32x4 u;

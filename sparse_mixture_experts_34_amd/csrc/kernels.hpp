@@ -40,14 +40,18 @@ hipError_t launch_router_logits_partial(int dtype, const void* x,
                                         const float* wr, float* part, int T,
                                         int d, int E, int ksplit,
                                         hipStream_t s);
-// Sum the slices (+ router bias), softmax, top-k, gates, and per-block
+// Sum the slices (+ router bias), score (softmax, or sigmoid when
+// scoring = 1), top-k, gates (renormalised unless raw = 1), and per-block
 // probability partial sums [route_blocks(T), E].  logits may be null.
 hipError_t launch_route_select_from(const float* part, int ksplit,
                                     const float* router_bias,
                                     const float* select_bias, float* logits,
                                     int32_t* idx, float* gate,
                                     float* partials, int T, int E, int k,
-                                    hipStream_t s);
+                                    int scoring, int raw, hipStream_t s);
+// select_bias[e] += gamma * sign(mean count - counts[e]).
+hipError_t launch_update_select_bias(const int32_t* counts, float* bias,
+                                     float gamma, int E, hipStream_t s);
 // prob_mean[e] = sum_b partials[b,e] / T (fixed order).
 hipError_t launch_prob_mean(const float* partials, float* prob_mean, int nblk,
                             int T, int E, hipStream_t s);

@@ -198,7 +198,8 @@ __global__ __launch_bounds__(RS_WAVES * 64) void route_select_kernel(
     const float* __restrict__ router_bias,
     const float* __restrict__ select_bias, float* __restrict__ logits_out,
     int32_t* __restrict__ idx_out, float* __restrict__ gate_out,
-    float* __restrict__ partials, int T, int E, int k, int tpw) {
+    float* __restrict__ partials, int T, int E, int k, int tpw, int scoring,
+    int raw) {
   __shared__ float psum_s[RS_WAVES][256];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -244,23 +245,37 @@ __global__ __launch_bounds__(RS_WAVES * 64) void route_select_kernel(
           if (s < ksplit) v += pv[cur][c][s];
         if (router_bias) v += router_bias[e];
         l[c] = v;
-        key[c] = select_bias ? v + select_bias[e] : v;
+        // sigmoid scores with a selection bias: the bias is on the score
+        // scale; otherwise the logit orders the choice
+        key[c] = select_bias ? (scoring ? sigmoid_f(v) : v) + select_bias[e]
+                             : v;
         if (logits_out) logits_out[(size_t)t * E + e] = v;
       }
     }
-    float m = -INFINITY;
-#pragma unroll
-    for (int c = 0; c < MAXC; ++c) m = fmaxf(m, l[c]);
-    m = wave_max(m);
+    // per-token scores: softmax probs, or sigmoid scores; P accumulates
+    // the scores scaled to sum to 1
+    float m = -INFINITY, inv;
     float ex[MAXC], se = 0.f;
+    if (!scoring) {
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-      const int e = lane + 64 * c;
-      ex[c] = (e < E) ? __expf(l[c] - m) : 0.f;
-      se += ex[c];
+      for (int c = 0; c < MAXC; ++c) m = fmaxf(m, l[c]);
+      m = wave_max(m);
+#pragma unroll
+      for (int c = 0; c < MAXC; ++c) {
+        const int e = lane + 64 * c;
+        ex[c] = (e < E) ? __expf(l[c] - m) : 0.f;
+        se += ex[c];
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < MAXC; ++c) {
+        const int e = lane + 64 * c;
+        ex[c] = (e < E) ? sigmoid_f(l[c]) : 0.f;
+        se += ex[c];
+      }
     }
     se = wave_sum(se);
-    const float inv = 1.0f / se;
+    inv = 1.0f / se;
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) psum[c] += ex[c] * inv;
 
@@ -305,14 +320,32 @@ __global__ __launch_bounds__(RS_WAVES * 64) void route_select_kernel(
         my_l = bl;
       }
     }
-    // gates: chosen probabilities over their sum, i.e. a softmax over the
-    // chosen logits (the shared normaliser cancels)
-    const float mc = wave_max(lane < k ? my_l : -INFINITY);
-    const float ej = lane < k ? __expf(my_l - mc) : 0.f;
-    const float sj = wave_sum(ej);
+    // gates.  Softmax, renormalised: chosen probabilities over their sum,
+    // i.e. a softmax over the chosen logits (the shared normaliser
+    // cancels).  Softmax, raw: the chosen probability.  Sigmoid: the chosen
+    // score, over the chosen scores' sum when renormalised.
+    float g;
+    if (!scoring) {
+      if (!raw) {
+        const float mc = wave_max(lane < k ? my_l : -INFINITY);
+        const float ej = lane < k ? __expf(my_l - mc) : 0.f;
+        const float sj = wave_sum(ej);
+        g = ej / sj;
+      } else {
+        g = __expf(my_l - m) * inv;
+      }
+    } else {
+      const float sc = lane < k ? sigmoid_f(my_l) : 0.f;
+      if (!raw) {
+        const float sj = wave_sum(sc);
+        g = sc / sj;
+      } else {
+        g = sc;
+      }
+    }
     if (lane < k) {
       idx_out[(size_t)t * k + lane] = my_idx;
-      gate_out[(size_t)t * k + lane] = ej / sj;
+      gate_out[(size_t)t * k + lane] = g;
     }
   }
   // per-block probability partial sums, waves added in order 0..3
@@ -385,13 +418,13 @@ hipError_t launch_route_select_from(const float* part, int ksplit,
                                     const float* select_bias, float* logits,
                                     int32_t* idx, float* gate,
                                     float* partials, int T, int E, int k,
-                                    hipStream_t s) {
+                                    int scoring, int raw, hipStream_t s) {
   const int tpw = route_tpw(T);
   const dim3 grid(route_blocks(T)), block(RS_WAVES * 64);
 #define MOE_SELECT(C, KS, PF)                                                 \
   route_select_kernel<C, KS, PF><<<grid, block, 0, s>>>(                      \
       part, ksplit, router_bias, select_bias, logits, idx, gate, partials, T, \
-      E, k, tpw)
+      E, k, tpw, scoring, raw)
   const int mc = (E + 63) / 64;
   if (tpw > 1) {   // several tokens per wave: K split <= 2, prefetch
     if (mc == 1) MOE_SELECT(1, 2, true);
@@ -409,6 +442,32 @@ hipError_t launch_route_select_from(const float* part, int ksplit,
 hipError_t launch_prob_mean(const float* partials, float* prob_mean, int nblk,
                             int T, int E, hipStream_t s) {
   prob_mean_kernel<<<1, 256, 0, s>>>(partials, prob_mean, nblk, T, E);
+  return hipGetLastError();
+}
+
+namespace {
+// select_bias[e] += gamma * sign(sum(counts) - E * counts[e]) (exact sign)
+__global__ void update_select_bias_kernel(const int32_t* __restrict__ counts,
+                                          float* __restrict__ bias,
+                                          float gamma, int E) {
+  __shared__ long long total_s;
+  if (threadIdx.x == 0) {
+    long long tot = 0;
+    for (int e = 0; e < E; ++e) tot += counts[e];
+    total_s = tot;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const long long d = total_s - (long long)E * counts[e];
+    const float sg = d > 0 ? 1.0f : (d < 0 ? -1.0f : 0.0f);
+    bias[e] = bias[e] + gamma * sg;
+  }
+}
+}  // namespace
+
+hipError_t launch_update_select_bias(const int32_t* counts, float* bias,
+                                     float gamma, int E, hipStream_t s) {
+  update_select_bias_kernel<<<1, 256, 0, s>>>(counts, bias, gamma, E);
   return hipGetLastError();
 }
 

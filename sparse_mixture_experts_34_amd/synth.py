@@ -49,6 +49,8 @@ class Workload:
     select_bias_std: float = 0.0      # > 0: DeepSeek-style selection bias
     seed_index: int = 0
     wquant: str | None = None         # "int4": 4-bit expert weights
+    scoring: str = "softmax"          # router scores: softmax | sigmoid
+    raw_gates: bool = False           # gates without renormalisation
     notes: dict = field(default_factory=dict, compare=False, hash=False)
 
     @property
@@ -160,9 +162,9 @@ def make_inputs(wl: Workload, device="cpu", seed: int | None = None,
     are drawn as float32 normals and rounded (RNE) to the workload dtype;
     the router weight and the biases on the router stay float32.
 
-    ``margin_fn(x64, w_router64, k, router_bias64, select_bias64)`` may
-    return a per-token top-k margin; tokens at or below ``min_margin`` get
-    their x row redrawn from a per-(token, attempt) generator.  The number
+    ``margin_fn(x64, w_router64, k, router_bias64, select_bias64, scoring)``
+    may return a per-token top-k margin; tokens at or below ``min_margin``
+    get their x row redrawn from a per-(token, attempt) generator.  The number
     of redraws is returned under ``"redraws"``.
     """
     seed = wl.seed() if seed is None else seed
@@ -218,7 +220,7 @@ def _redraw_close_tokens(inp, wl, seed, dev, margin_fn, min_margin,
     rb = _host64(inp["router_bias"])
     sb = _host64(inp["select_bias"])
     x = inp["x"]
-    bad = np.nonzero(margin_fn(_host64(x), wr, wl.top_k, rb, sb)
+    bad = np.nonzero(margin_fn(_host64(x), wr, wl.top_k, rb, sb, wl.scoring)
                      <= min_margin)[0]
     for t in bad:
         t = int(t)
@@ -226,7 +228,8 @@ def _redraw_close_tokens(inp, wl, seed, dev, margin_fn, min_margin,
             g = torch.Generator(device=dev)
             g.manual_seed(_row_seed(seed, t, attempt))
             row = _randn((1, wl.d_model), g, dev, 1.0, wl.torch_dtype)
-            m = margin_fn(_host64(row), wr, wl.top_k, rb, sb)[0]
+            m = margin_fn(_host64(row), wr, wl.top_k, rb, sb,
+                          wl.scoring)[0]
             inp["redraws"] += 1
             if m > min_margin:
                 x[t] = row[0]

@@ -54,7 +54,8 @@ def oracle_route(inp, wl):
                         None if inp["router_bias"] is None
                         else host(inp["router_bias"]),
                         None if inp["select_bias"] is None
-                        else host(inp["select_bias"]))
+                        else host(inp["select_bias"]),
+                        scoring=wl.scoring, renormalize=not wl.raw_gates)
 
 
 def gpu_route(inp, wl, ws=None):
@@ -179,4 +180,4 @@ def oracle_layer(inp, wl, tokens=None, lazy=False):
         else host(inp["router_bias"]),
         select_bias=None if inp["select_bias"] is None
         else host(inp["select_bias"]),
-        tokens=tokens)
+        tokens=tokens, scoring=wl.scoring, renormalize=not wl.raw_gates)

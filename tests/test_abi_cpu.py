@@ -90,13 +90,16 @@ BAD = [
     (dict(wquant=1, dtype=0), moe.MOE_ENOTSUP),        # int4 needs bf16
     (dict(wquant=1, d_model=192), moe.MOE_ENOTSUP),    # K % 128 != 0
     (dict(wquant=1, d_ff=320), moe.MOE_ENOTSUP),
+    (dict(scoring=2), moe.MOE_EINVAL),
+    (dict(raw_gates=3), moe.MOE_EINVAL),
 ]
 
 
 def _prob(**kw):
     base = dict(T=16, d_model=128, n_experts=4, top_k=2, d_ff=256,
                 n_shared=0, capacity=0, act=moe.MOE_ACT_SWIGLU,
-                dtype=moe.MOE_DTYPE_BF16, aux_coef=0.01, wquant=0)
+                dtype=moe.MOE_DTYPE_BF16, aux_coef=0.01, wquant=0,
+                scoring=0, raw_gates=0)
     base.update(kw)
     return binding.moe_problem(*[base[f] for f, _ in
                                  binding.moe_problem._fields_])
@@ -212,6 +215,20 @@ def test_quantize_int4_validation():
         moe.MOE_ENOTSUP
     # nothing to do: OK without touching any pointer or the device
     assert lib.moe_quantize_int4(None, 0, 128, None, None, None) == moe.MOE_OK
+
+
+def test_update_select_bias_validation():
+    lib = binding._lib
+    f = 0x1000
+    p = ctypes.byref(_prob())
+    assert lib.moe_update_select_bias(p, None, f, 0.001, None) == \
+        moe.MOE_EINVAL
+    assert lib.moe_update_select_bias(p, f, None, 0.001, None) == \
+        moe.MOE_EINVAL
+    assert lib.moe_update_select_bias(p, f, f, float("inf"), None) == \
+        moe.MOE_EINVAL
+    assert lib.moe_update_select_bias(None, f, f, 0.001, None) == \
+        moe.MOE_EINVAL
 
 
 def test_workspace_too_small_or_misaligned():

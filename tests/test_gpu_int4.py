@@ -128,7 +128,8 @@ def oracle_q4_layer(inp, wl, tokens=None):
         host(inp["x"]), host(inp["w_router"]), w, k=wl.top_k,
         cap=wl.capacity, act=wl.act, n_shared=wl.n_shared,
         alpha=wl.aux_coef, router_bias=None if rb is None else host(rb),
-        select_bias=None if sb is None else host(sb), tokens=tokens)
+        select_bias=None if sb is None else host(sb), tokens=tokens,
+        scoring=wl.scoring, renormalize=not wl.raw_gates)
 
 
 SMALL_Q4 = [
