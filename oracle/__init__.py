@@ -32,6 +32,8 @@ from .moe import (  # noqa: F401
     route,
     topk_margin,
     dispatch,
+    philox4x32,
+    dispatch_reassign,
     expert_ffn,
     combine,
     aux_loss,

@@ -244,6 +244,126 @@ def dispatch(idx, E, cap):
 
 
 # ---------------------------------------------------------------------------
+# Overflow by random reassignment
+# ---------------------------------------------------------------------------
+
+_PHILOX_M = (0xD2511F53, 0xCD9E8D57)
+_PHILOX_W = (0x9E3779B9, 0xBB67AE85)
+_U32 = 0xFFFFFFFF
+
+
+def philox4x32(ctr, key, rounds=10):
+    """The Philox4x32-10 counter-based generator (Salmon, Moraes, Dror and
+    Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011): a round
+    multiplies words 0 and 2 of the 128-bit counter by two fixed 32-bit
+    multipliers and mixes the high and low halves of the products with
+    words 1 and 3 and the 64-bit key; the key advances by two Weyl
+    constants between rounds.  Returns the four 32-bit output words."""
+    c = [int(v) & _U32 for v in ctr]
+    k = [int(v) & _U32 for v in key]
+    for r in range(rounds):
+        if r:
+            k = [(k[0] + _PHILOX_W[0]) & _U32, (k[1] + _PHILOX_W[1]) & _U32]
+        p0 = _PHILOX_M[0] * c[0]
+        p1 = _PHILOX_M[1] * c[2]
+        c = [(p1 >> 32) ^ c[1] ^ k[0], p1 & _U32,
+             (p0 >> 32) ^ c[3] ^ k[1], p0 & _U32]
+    return c
+
+
+def _reassign_candidates(spare, mine):
+    """Experts with a free slot that the token does not already use, in
+    ascending index."""
+    return [e for e in range(len(spare)) if spare[e] > 0 and e not in mine]
+
+
+def _pick_slot(x, cand, spare):
+    """The expert holding free slot r = floor(x * total / 2^32) when the
+    candidates' free slots are laid out in ascending expert order."""
+    r = (x * sum(spare[e] for e in cand)) >> 32
+    for e in cand:
+        if r < spare[e]:
+            return e
+        r -= spare[e]
+    raise AssertionError("unreachable: r < total")
+
+
+def _reassigned_gate(scores_t, orig_idx_t, e, renormalize):
+    """The new expert's score under the token's own normaliser."""
+    norm = scores_t[orig_idx_t].sum() if renormalize else 1.0
+    return scores_t[e] / norm
+
+
+def dispatch_reassign(idx, scores, gate, E, cap, seed, renormalize=True):
+    """Capacity dispatch with overflow reassigned at random ([LBS] "Token
+    Dropping and Overflow Handling", random reassignment: an overflow token
+    goes to a randomly chosen expert slot that still has room, weighted by
+    that expert's router probability).
+
+    Plain reading of the steps the page leaves open:
+    * first the capacity cut of :func:`dispatch` (first ``cap`` per expert
+      in token order kept); spare[e] = cap - kept[e];
+    * the dropped assignments a = t*k + j are visited in ascending a; each
+      draws one 32-bit word x = philox4x32((a, 0, 0, 0), (seed low 32 bits,
+      seed high 32 bits))[0] and picks a free slot uniformly: with the
+      candidate experts (spare > 0 and not already one of token t's
+      experts) in ascending index, r = floor(x * total / 2^32) over
+      total = sum of their spare slots selects the expert whose slot range
+      holds r; that expert's spare drops by one.  With no candidate the
+      assignment stays dropped;
+    * the new gate is the reassigned expert's score (softmax probability
+      or sigmoid score) under the token's own normaliser: divided by the
+      sum of the scores of its originally chosen experts when gates are
+      renormalised, as is;
+    * each expert's rows are its kept assignments in token order followed
+      by its reassigned ones in the order they were placed.
+    counts (for the aux loss) stay the routing decisions before the cut.
+
+    Returns the :func:`dispatch` dict plus ``idx`` and ``gate`` (updated
+    copies) and ``n_reassigned``."""
+    idx = np.asarray(idx, np.int64)
+    T, k = idx.shape
+    base = dispatch(idx, E, cap)
+    new_idx = idx.copy()
+    new_gate = np.array(gate, np.float64, copy=True)
+    extra = [[] for _ in range(E)]
+    if cap > 0:
+        scores = np.asarray(scores, np.float64)
+        spare = [cap - int(base["kept"][e]) for e in range(E)]
+        key = (int(seed) & _U32, (int(seed) >> 32) & _U32)
+        for a in range(T * k):
+            if base["slot_of"][a] >= 0:
+                continue
+            t, j = divmod(a, k)
+            cand = _reassign_candidates(spare,
+                                        set(int(e) for e in new_idx[t]))
+            if not cand:
+                continue
+            e = _pick_slot(philox4x32((a, 0, 0, 0), key)[0], cand, spare)
+            spare[e] -= 1
+            new_idx[t, j] = e
+            new_gate[t, j] = _reassigned_gate(scores[t], idx[t], e,
+                                              renormalize)
+            extra[e].append(a)
+    kept = np.array([base["kept"][e] + len(extra[e]) for e in range(E)],
+                    np.int64)
+    offsets = np.zeros(E + 1, np.int64)
+    offsets[1:] = np.cumsum(kept)
+    perm = []
+    slot_of = np.full(T * k, -1, np.int64)
+    for e in range(E):
+        rows = list(base["perm"][base["offsets"][e]:base["offsets"][e + 1]])
+        for a in rows + extra[e]:
+            slot_of[a] = len(perm)
+            perm.append(int(a))
+    return {"counts": base["counts"], "kept": kept, "offsets": offsets,
+            "perm": np.asarray(perm, np.int64), "slot_of": slot_of,
+            "n_dropped": int(T * k - offsets[E]), "idx": new_idx,
+            "gate": new_gate,
+            "n_reassigned": int(sum(len(x) for x in extra))}
+
+
+# ---------------------------------------------------------------------------
 # Steps 3-4: expert FFNs over each expert's kept rows
 # ---------------------------------------------------------------------------
 
@@ -386,7 +506,7 @@ def aux_loss(counts, probs, alpha):
 def layer_forward(x, w_router, weights, *, k, cap, act, n_shared=0,
                   alpha=0.01, router_bias=None, select_bias=None,
                   residual=True, tokens=None, scoring="softmax",
-                  renormalize=True):
+                  renormalize=True, reassign_seed=None):
     """Route, dispatch, expert FFNs, combine and aux loss, in that order.
 
     With ``tokens`` the routing, dispatch and aux loss still cover every
@@ -398,7 +518,13 @@ def layer_forward(x, w_router, weights, *, k, cap, act, n_shared=0,
     T = x.shape[0]
     E = np.asarray(w_router).shape[0]
     r = route(x, w_router, k, router_bias, select_bias, scoring, renormalize)
-    dsp = dispatch(r["idx"], E, cap)
+    if reassign_seed is None:
+        dsp = dispatch(r["idx"], E, cap)
+    else:
+        dsp = dispatch_reassign(r["idx"], r["scores"], r["gate"], E, cap,
+                                reassign_seed, renormalize)
+        r = dict(r)
+        r["idx"], r["gate"] = dsp.pop("idx"), dsp.pop("gate")
     y = expert_ffn(x, dsp["perm"], dsp["offsets"], weights, act, k,
                    n_shared, tokens)
     out = combine(x if residual else None, y, dsp["slot_of"], r["gate"], k,

@@ -590,6 +590,111 @@ def pin_bias_update_hand_counted():
 
 
 # ---------------------------------------------------------------------------
+# Overflow by random reassignment
+# ---------------------------------------------------------------------------
+
+def pin_philox_known_answers():
+    for v in _golden("philox4x32_kat.json")["vectors"]:
+        h = lambda xs: [int(x, 16) for x in xs]
+        assert oracle.philox4x32(h(v["ctr"]), h(v["key"])) == h(v["out"])
+
+
+def pin_reassign_hand_counted():
+    for c in _golden("reassign_hand_counted.json")["cases"]:
+        idx = np.array(c["idx"])
+        T, k = idx.shape
+        E = c["E"]
+        rng = _rng(61)
+        sc = rng.uniform(0.1, 1.0, (T, E))
+        g = np.take_along_axis(sc, idx, 1)
+        g = g / g.sum(1, keepdims=True)
+        for seed in (0, 7, 2 ** 40 + 3):     # forced choices: any seed
+            r = oracle.dispatch_reassign(idx, sc, g, E, c["capacity"], seed)
+            assert r["idx"].tolist() == c["new_idx"], (c["name"], r["idx"])
+            for key in ("kept", "offsets", "perm", "slot_of"):
+                assert r[key].tolist() == c[key], (c["name"], key)
+            assert r["n_dropped"] == c["n_dropped"]
+            assert r["n_reassigned"] == c["n_reassigned"]
+            # a reassigned slot's gate: the new expert's score over the
+            # token's original normaliser
+            moved = np.argwhere(np.array(c["new_idx"]) != idx)
+            for t, j in moved:
+                e = c["new_idx"][t][j]
+                want = sc[t, e] / sc[t, idx[t]].sum()
+                assert abs(r["gate"][t, j] - want) < 1e-15
+
+
+def pin_reassign_invariants():
+    rng = _rng(62)
+    for trial in range(20):
+        T, E = int(rng.integers(5, 60)), int(rng.integers(2, 9))
+        k = int(rng.integers(1, min(E, 3) + 1))
+        cap = int(rng.integers(1, max(2, T * k // E + 2)))
+        logits = rng.standard_normal((T, E)) * 2 + np.log(
+            np.arange(1, E + 1))[::-1]
+        idx = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+        sc = oracle.softmax(logits)
+        g = np.take_along_axis(sc, idx, 1)
+        r = oracle.dispatch_reassign(idx, sc, g / g.sum(1, keepdims=True), E,
+                                     cap, seed=trial)
+        base = oracle.dispatch(idx, E, cap)
+        assert (r["counts"] == base["counts"]).all()
+        assert (r["kept"] <= cap).all()
+        assert r["kept"].sum() == base["kept"].sum() + r["n_reassigned"]
+        for t in range(T):                       # experts stay distinct
+            assert len(set(r["idx"][t].tolist())) == k
+        # kept rows keep their place in token order at the front of each
+        # group; perm and slot_of agree
+        for e in range(E):
+            rows = r["perm"][r["offsets"][e]:r["offsets"][e + 1]]
+            n0 = base["kept"][e]
+            assert rows[:n0].tolist() == base["perm"][
+                base["offsets"][e]:base["offsets"][e + 1]].tolist()
+            assert all(r["idx"].reshape(-1)[a] == e for a in rows)
+        for p_, a in enumerate(r["perm"]):
+            assert r["slot_of"][a] == p_
+        # nothing left that could have moved: every still-dropped slot's
+        # token already owns every expert with room
+        spare = cap - r["kept"]
+        for a in np.nonzero(r["slot_of"] < 0)[0]:
+            t = a // k
+            free = set(np.nonzero(spare > 0)[0].tolist())
+            assert free <= set(r["idx"][t].tolist())
+
+
+def pin_reassign_slot_weighting():
+    # one overflow assignment, two candidate experts with 1 and 3 free
+    # slots: chosen with probability 1/4 and 3/4 over seeds
+    idx = np.array([[0], [0], [0], [1]])   # cap 2: t2 overflows expert 0
+    E, cap = 3, 2                          # spare: e1 1, e2 2
+    sc = np.full((4, E), 1.0 / E)
+    g = np.ones((4, 1))
+    hits = np.zeros(E)
+    n = 4000
+    for seed in range(n):
+        r = oracle.dispatch_reassign(idx, sc, g, E, cap, seed)
+        hits[r["idx"][2, 0]] += 1
+    assert hits[0] == 0
+    p1 = hits[1] / n                                # expected 1/3
+    assert abs(p1 - 1.0 / 3) < 4 * math.sqrt((1 / 3) * (2 / 3) / n)
+
+
+def pin_layer_reassign_vs_brute_force():
+    rng = _rng(63)
+    T, d, E, k, f = 40, 16, 4, 2, 24
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    wr = rng.standard_normal((E, d)).astype(np.float32)
+    rb = np.array([3.0, 0.0, 0.0, 0.0], np.float32)   # expert 0 overflows
+    w = _swiglu_weights(rng, E, d, f)
+    o = oracle.layer_forward(x, wr, w, k=k, cap=24, act="swiglu",
+                             router_bias=rb, reassign_seed=99)
+    assert o["n_reassigned"] > 0
+    ref = brute_force_dense(x, o["idx"], o["gate"], o["slot_of"], "swiglu",
+                            w, E, k)
+    assert _rel(o["out"], ref) < 1e-12
+
+
+# ---------------------------------------------------------------------------
 # 4-bit expert weights
 # ---------------------------------------------------------------------------
 

@@ -311,6 +311,43 @@ def m_bias_update_wrong_sign(mp):
     _patch(mp, "update_select_bias", update_select_bias)
 
 
+def m_reassign_own_expert_allowed(mp):
+    mp.setattr(om, "_reassign_candidates",
+               lambda spare, mine: [e for e in range(len(spare))
+                                    if spare[e] > 0])
+
+
+def m_reassign_uniform_over_experts(mp):
+    def pick(x, cand, spare):
+        return cand[(x * len(cand)) >> 32]
+    mp.setattr(om, "_pick_slot", pick)
+
+
+def m_reassign_gate_unnormalised(mp):
+    mp.setattr(om, "_reassigned_gate",
+               lambda scores_t, orig_idx_t, e, renormalize: scores_t[e])
+
+
+def m_philox_swapped_products(mp):
+    _ph = om.philox4x32
+
+    def philox4x32(ctr, key, rounds=10):
+        c = [int(v) & 0xFFFFFFFF for v in ctr]
+        k = [int(v) & 0xFFFFFFFF for v in key]
+        for r in range(rounds):
+            if r:
+                k = [(k[0] + 0x9E3779B9) & 0xFFFFFFFF,
+                     (k[1] + 0xBB67AE85) & 0xFFFFFFFF]
+            p0 = 0xD2511F53 * c[0]
+            p1 = 0xCD9E8D57 * c[2]
+            # high halves mixed with the wrong words
+            c = [(p0 >> 32) ^ c[1] ^ k[0], p1 & 0xFFFFFFFF,
+                 (p1 >> 32) ^ c[3] ^ k[1], p0 & 0xFFFFFFFF]
+        return c
+    _patch(mp, "philox4x32", philox4x32)
+    del _ph
+
+
 MUTATIONS = [m_no_renormalise, m_tie_to_higher_index, m_bias_in_gates,
              m_capacity_by_slot, m_keep_last, m_renormalise_survivors,
              m_transposed_w2, m_drop_bias_b2, m_gelu_tanh, m_silu_is_sigmoid,
@@ -320,7 +357,9 @@ MUTATIONS = [m_no_renormalise, m_tie_to_higher_index, m_bias_in_gates,
              m_q4_dequant_no_offset, m_q4_pack_untiled,
              m_q4_qparams_row_major, m_sigmoid_bias_on_logits,
              m_raw_gates_renormalised, m_sigmoid_probs_unnormalised,
-             m_bias_update_wrong_sign]
+             m_bias_update_wrong_sign, m_reassign_own_expert_allowed,
+             m_reassign_uniform_over_experts, m_reassign_gate_unnormalised,
+             m_philox_swapped_products]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=[m.__name__ for m in
