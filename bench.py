@@ -38,6 +38,7 @@ METRIC = ("MoE layer fwd tokens/s + % of bf16 MFMA / HBM roofline "
 CPU_SAMPLE = {"mixtral_decode": 16, "mixtral_decode_int4": 2,
               "mixtral_prefill": 48,
               "switch_top1_cf1": 256, "switch_top1_cf125": 256,
+              "switch_top1_cf1_reassign": 256,
               "deepseek_v3": 12, "tiny_gelu_f32": 64}
 
 
@@ -160,7 +161,9 @@ def main():
     t_roof = max(F / PEAK_BF16, B / PEAK_HBM)
 
     # ---- kernel pass: the same layer as its C-ABI steps, HIP events ------
-    logits = None
+    reassign = wl.overflow == "reassign" and wl.capacity > 0
+    logits = (torch.empty(T, E, dtype=torch.float32, device=dev)
+              if reassign else None)
     idx = torch.empty(T, k, dtype=torch.int32, device=dev)
     gate = torch.empty(T, k, dtype=torch.float32, device=dev)
     pm = torch.empty(E, dtype=torch.float32, device=dev)
@@ -178,7 +181,12 @@ def main():
         moe.moe_route(p, inp["x"], inp["w_router"], inp["router_bias"],
                       inp["select_bias"], logits, idx, gate, pm, ws)
         ev[1].record()
-        moe.moe_dispatch(p, idx, pm, counts, offs, perm, slot, nd, aux, ws)
+        if reassign:
+            moe.moe_dispatch_reassign(p, idx, gate, logits, pm, counts, offs,
+                                      perm, slot, nd, aux, ws)
+        else:
+            moe.moe_dispatch(p, idx, pm, counts, offs, perm, slot, nd, aux,
+                             ws)
         ev[2].record()
         moe.moe_expert_up(p, inp["x"], perm, offs, W, h)
         ev[3].record()
@@ -265,7 +273,9 @@ def main():
                    "n_experts": E, "top_k": k, "d_ff": f, "act": wl.act,
                    "capacity": wl.capacity, "n_shared": wl.n_shared,
                    "expert_weights": "int4 (group 128, fp32 scale/offset)"
-                   if q4 else wl.dtype},
+                   if q4 else wl.dtype,
+                   "scoring": wl.scoring, "raw_gates": wl.raw_gates,
+                   "overflow": wl.overflow},
         "roofline": roof,
         "layer_roofline": {
             "flops": F, "bytes": B, "t_roof_us": round(t_roof * 1e6, 2),
@@ -332,11 +342,18 @@ def cpu_baseline(wl, inp, n_tokens=None, gpu_idx=None):
     x, wr = hx(inp["x"]), hx(inp["w_router"])
     rb, sb = hx(inp["router_bias"]), hx(inp["select_bias"])
     # route once (untimed) to find the experts the sample needs
-    r = oracle.route(x, wr, wl.top_k, rb, sb)
-    need = sorted(set(int(e) for e in r["idx"][tokens].ravel()))
+    renorm = not wl.raw_gates
+    reseed = wl.overflow_seed if wl.overflow == "reassign" else None
+    r = oracle.route(x, wr, wl.top_k, rb, sb, wl.scoring, renorm)
+    ridx = r["idx"]
+    if reseed is not None and wl.capacity > 0:
+        ridx = oracle.dispatch_reassign(r["idx"], r["scores"], r["gate"],
+                                        wl.n_experts, wl.capacity, reseed,
+                                        renorm)["idx"]
+    need = sorted(set(int(e) for e in ridx[tokens].ravel()))
     flips = None
     if gpu_idx is not None:
-        flips = int((np.asarray(gpu_idx) != r["idx"]).any(axis=1).sum())
+        flips = int((np.asarray(gpu_idx) != ridx).any(axis=1).sum())
     names = (["w1", "b1", "w2", "b2"] if wl.act == "gelu"
              else ["w_gate", "w_up", "w_down"])
     w = {}
@@ -361,7 +378,9 @@ def cpu_baseline(wl, inp, n_tokens=None, gpu_idx=None):
     t0 = time.perf_counter()
     oracle.layer_forward(x, wr, w, k=wl.top_k, cap=wl.capacity, act=wl.act,
                          n_shared=wl.n_shared, alpha=wl.aux_coef,
-                         router_bias=rb, select_bias=sb, tokens=tokens)
+                         router_bias=rb, select_bias=sb, tokens=tokens,
+                         scoring=wl.scoring, renormalize=renorm,
+                         reassign_seed=reseed)
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()
                    if i.get("internal_api") in ("openblas", "mkl", "blis")]

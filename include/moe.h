@@ -77,6 +77,9 @@ extern "C" {
 #define MOE_SCORING_SOFTMAX 0 /* softmax over all experts                */
 #define MOE_SCORING_SIGMOID 1 /* per-expert sigmoid                      */
 
+#define MOE_OVERFLOW_DROP 0     /* overflow assignments are dropped      */
+#define MOE_OVERFLOW_REASSIGN 1 /* reassigned to free slots at random    */
+
 #define MOE_WQUANT_NONE 0 /* expert weights in the problem dtype          */
 #define MOE_WQUANT_INT4 1 /* expert weights as 4-bit codes, see below     */
 #define MOE_Q4_GROUP 128  /* weights per (scale, offset) pair             */
@@ -109,6 +112,23 @@ extern "C" {
  *   raw_gates  0 (default): the chosen scores are renormalised to sum to 1;
  *              1: a gate is the chosen score itself ([FA] The knobs,
  *              norm_topk_prob).
+ *   overflow   MOE_OVERFLOW_DROP (default) or MOE_OVERFLOW_REASSIGN
+ *              ([LBS] Token Dropping and Overflow Handling, random
+ *              reassignment): after the capacity cut the dropped
+ *              assignments a = t*k + j are visited in ascending a; each
+ *              draws x = Philox4x32-10 word 0 of counter (a, 0, 0, 0) under
+ *              key (overflow_seed low, high 32 bits) and takes free slot
+ *              r = floor(x * total / 2^32) of the candidate experts (a free
+ *              slot and not already one of token t's experts; ascending
+ *              index, each contributing its free slots), or stays dropped
+ *              when there is none.  Its gate becomes the new expert's
+ *              score under the token's normaliser (divided by the sum of
+ *              its originally chosen scores unless raw_gates).  An expert's
+ *              rows are its kept assignments in token order, then its
+ *              reassigned ones in ascending a.  Counts (and the aux loss)
+ *              keep the routing decisions.  Used by moe_layer_forward and
+ *              moe_dispatch_reassign; moe_dispatch rejects it.
+ *   overflow_seed  64-bit key of the reassignment draws.
  */
 typedef struct moe_problem {
   int32_t T;
@@ -124,6 +144,8 @@ typedef struct moe_problem {
   int32_t wquant;
   int32_t scoring;
   int32_t raw_gates;
+  int32_t overflow;
+  uint64_t overflow_seed;
 } moe_problem;
 
 /*
@@ -223,6 +245,30 @@ int32_t moe_dispatch(const moe_problem* p, const int32_t* topk_idx,
                      int32_t* offsets, int32_t* perm, int32_t* slot_of,
                      int32_t* n_dropped, float* aux_loss, void* ws,
                      size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Step 2 with overflow reassignment (p->overflow = MOE_OVERFLOW_REASSIGN,
+ * see moe_problem): the outputs of moe_dispatch, where kept and offsets
+ * include the reassigned rows, plus in-place updates of the routing of the
+ * reassigned slots.
+ *   topk_idx   [T, k] int32 in/out: a reassigned slot gets its new expert.
+ *   topk_gate  [T, k] float32 in/out: a reassigned slot gets its new gate.
+ *   logits     [T, E] float32 input: the router logits moe_route wrote
+ *              (the new gates need the token's scores).
+ *   prob_mean, counts, offsets, perm, slot_of, n_dropped, aux_loss: as in
+ *              moe_dispatch (counts and aux from the routing decisions
+ *              before the cut and before reassignment).
+ * The draws are sequential in a (each takes a free slot), so this step
+ * runs in one wave per call; it costs about one microsecond per hundred
+ * overflow assignments.
+ */
+int32_t moe_dispatch_reassign(const moe_problem* p, int32_t* topk_idx,
+                              float* topk_gate, const float* logits,
+                              const float* prob_mean, int32_t* counts,
+                              int32_t* offsets, int32_t* perm,
+                              int32_t* slot_of, int32_t* n_dropped,
+                              float* aux_loss, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
 
 /*
  * Steps 3-4, expert FFNs over each expert's kept rows ([RC]; [GN]

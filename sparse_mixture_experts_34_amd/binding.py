@@ -28,6 +28,8 @@ MOE_ACT_GELU, MOE_ACT_SWIGLU = 0, 1
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 MOE_WQUANT_NONE, MOE_WQUANT_INT4 = 0, 1
 MOE_SCORING_SOFTMAX, MOE_SCORING_SIGMOID = 0, 1
+MOE_OVERFLOW_DROP, MOE_OVERFLOW_REASSIGN = 0, 1
+OVERFLOW = {"drop": MOE_OVERFLOW_DROP, "reassign": MOE_OVERFLOW_REASSIGN}
 SCORING = {"softmax": MOE_SCORING_SOFTMAX, "sigmoid": MOE_SCORING_SIGMOID}
 MOE_Q4_GROUP = 128
 WQUANT = {None: MOE_WQUANT_NONE, "none": MOE_WQUANT_NONE,
@@ -50,7 +52,8 @@ class moe_problem(ctypes.Structure):
                 ("capacity", ctypes.c_int32), ("act", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("aux_coef", ctypes.c_float),
                 ("wquant", ctypes.c_int32), ("scoring", ctypes.c_int32),
-                ("raw_gates", ctypes.c_int32)]
+                ("raw_gates", ctypes.c_int32), ("overflow", ctypes.c_int32),
+                ("overflow_seed", ctypes.c_uint64)]
 
 
 class moe_expert_weights(ctypes.Structure):
@@ -80,6 +83,8 @@ _SIGS = {
                                  _V, _SZ, _V]),
     "moe_quantize_int4": (_I32, [_V, ctypes.c_int64, _I32, _V, _V, _V]),
     "moe_update_select_bias": (_I32, [_P, _V, _V, ctypes.c_float, _V]),
+    "moe_dispatch_reassign": (_I32, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V,
+                                     _V, _V, _SZ, _V]),
     "moe_status_string": (ctypes.c_char_p, [_I32]),
 }
 EXPORTS = tuple(_SIGS)
@@ -133,7 +138,8 @@ def _check(status, where):
 def problem(T, d_model, n_experts, top_k, d_ff, *, n_shared=0, capacity=0,
             act="swiglu", dtype="bf16", aux_coef=0.01,
             wquant=None, scoring="softmax",
-            raw_gates=False) -> moe_problem:
+            raw_gates=False, overflow="drop",
+            overflow_seed=0) -> moe_problem:
     return moe_problem(T, d_model, n_experts, top_k, d_ff, n_shared, capacity,
                        ACT[act] if isinstance(act, str) else act,
                        DTYPE[dtype] if isinstance(dtype, str) else dtype,
@@ -141,7 +147,9 @@ def problem(T, d_model, n_experts, top_k, d_ff, *, n_shared=0, capacity=0,
                        WQUANT[wquant] if not isinstance(wquant, int)
                        else wquant,
                        SCORING[scoring] if isinstance(scoring, str)
-                       else scoring, int(raw_gates))
+                       else scoring, int(raw_gates),
+                       OVERFLOW[overflow] if isinstance(overflow, str)
+                       else overflow, int(overflow_seed))
 
 
 def problem_for(wl) -> moe_problem:
@@ -151,7 +159,9 @@ def problem_for(wl) -> moe_problem:
                    dtype=wl.dtype, aux_coef=wl.aux_coef,
                    wquant=getattr(wl, "wquant", None),
                    scoring=getattr(wl, "scoring", "softmax"),
-                   raw_gates=getattr(wl, "raw_gates", False))
+                   raw_gates=getattr(wl, "raw_gates", False),
+                   overflow=getattr(wl, "overflow", "drop"),
+                   overflow_seed=getattr(wl, "overflow_seed", 0))
 
 
 def expert_weights(w: dict) -> moe_expert_weights:
@@ -272,6 +282,17 @@ def moe_quantize_int4(w, codes, qparams, stream=None):
     _check(_lib.moe_quantize_int4(_ptr(w), rows, K, _ptr(codes),
                                   _ptr(qparams), _stream(stream)),
            "moe_quantize_int4")
+
+
+def moe_dispatch_reassign(p, topk_idx, topk_gate, logits, prob_mean, counts,
+                          offsets, perm, slot_of, n_dropped, aux_loss, ws,
+                          stream=None):
+    _check(_lib.moe_dispatch_reassign(
+        ctypes.byref(p), _ptr(topk_idx), _ptr(topk_gate), _ptr(logits),
+        _ptr(prob_mean), _ptr(counts), _ptr(offsets), _ptr(perm),
+        _ptr(slot_of), _ptr(n_dropped), _ptr(aux_loss), _ptr(ws),
+        ws.numel() if ws is not None else 0, _stream(stream)),
+        "moe_dispatch_reassign")
 
 
 def moe_update_select_bias(p, counts, select_bias, gamma, stream=None):

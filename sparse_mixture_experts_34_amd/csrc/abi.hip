@@ -24,7 +24,7 @@ struct Layout {
   int nrb;       // route blocks
   int nchunks;   // dispatch chunks
   size_t part, idx, gate, rpart, pmean, chunk, counts, offsets, perm, slot,
-      ndrop, aux, h, y, total;
+      ndrop, aux, h, y, logits, off0, rslot, newe, total;
 };
 
 Layout make_layout(const moe_problem& p) {
@@ -55,6 +55,12 @@ Layout make_layout(const moe_problem& p) {
   L.aux = take(4);
   L.h = take((size_t)rows * p.d_ff * esz);
   L.y = take((size_t)rows * p.d_model * esz);
+  // overflow reassignment: router logits, the cut's offsets, moved ranks
+  const bool re = p.overflow == MOE_OVERFLOW_REASSIGN;
+  L.logits = take(re ? (size_t)T * E * 4 : 0);
+  L.off0 = take(re ? (size_t)(E + 1) * 4 : 0);
+  L.rslot = take(re ? (size_t)T * k * 4 : 0);
+  L.newe = take(re ? (size_t)T * k * 4 : 0);
   L.total = off;
   return L;
 }
@@ -77,6 +83,8 @@ int32_t check_problem(const moe_problem* p) {
   if (p->scoring != MOE_SCORING_SOFTMAX && p->scoring != MOE_SCORING_SIGMOID)
     return MOE_EINVAL;
   if (p->raw_gates != 0 && p->raw_gates != 1) return MOE_EINVAL;
+  if (p->overflow != MOE_OVERFLOW_DROP && p->overflow != MOE_OVERFLOW_REASSIGN)
+    return MOE_EINVAL;
   if (p->wquant == MOE_WQUANT_INT4 &&
       (p->dtype != MOE_DTYPE_BF16 || p->d_model % MOE_Q4_GROUP != 0 ||
        p->d_ff % MOE_Q4_GROUP != 0))
@@ -225,6 +233,8 @@ int32_t moe_dispatch(const moe_problem* p, const int32_t* topk_idx,
                      size_t ws_bytes, hipStream_t stream) {
   int32_t st = check_problem(p);
   if (st) return st;
+  // reassignment needs the gates and logits: moe_dispatch_reassign
+  if (p->overflow != MOE_OVERFLOW_DROP) return MOE_EINVAL;
   if (!counts || !offsets || !n_dropped) return MOE_EINVAL;
   if (p->T > 0 && (!topk_idx || !perm || !slot_of)) return MOE_EINVAL;
   if (aux_loss && !prob_mean) return MOE_EINVAL;
@@ -256,6 +266,89 @@ int32_t moe_dispatch(const moe_problem* p, const int32_t* topk_idx,
   a.capacity = p->capacity;
   a.aux_coef = p->aux_coef;
   return status_of(launch_dispatch(a, stream));
+}
+
+namespace {
+ReassignArgs reassign_args(const moe_problem* p, int32_t* idx, float* gate,
+                           const float* logits, const int32_t* off0,
+                           int32_t* offsets, int32_t* perm, int32_t* slot_of,
+                           int32_t* n_dropped, int32_t* rslot,
+                           int32_t* newe) {
+  ReassignArgs r;
+  r.idx = idx;
+  r.gate = gate;
+  r.logits = logits;
+  r.off0 = off0;
+  r.offsets = offsets;
+  r.perm = perm;
+  r.slot_of = slot_of;
+  r.n_dropped = n_dropped;
+  r.rslot = rslot;
+  r.newe = newe;
+  r.T = p->T;
+  r.E = p->n_experts;
+  r.k = p->top_k;
+  r.capacity = p->capacity;
+  r.scoring = p->scoring;
+  r.raw = p->raw_gates;
+  r.key0 = (uint32_t)(p->overflow_seed & 0xFFFFFFFFu);
+  r.key1 = (uint32_t)(p->overflow_seed >> 32);
+  return r;
+}
+}  // namespace
+
+int32_t moe_dispatch_reassign(const moe_problem* p, int32_t* topk_idx,
+                              float* topk_gate, const float* logits,
+                              const float* prob_mean, int32_t* counts,
+                              int32_t* offsets, int32_t* perm,
+                              int32_t* slot_of, int32_t* n_dropped,
+                              float* aux_loss, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  int32_t st = check_problem(p);
+  if (st) return st;
+  if (p->overflow != MOE_OVERFLOW_REASSIGN) return MOE_EINVAL;
+  if (!counts || !offsets || !n_dropped) return MOE_EINVAL;
+  if (p->T > 0 && (!topk_idx || !topk_gate || !logits || !perm || !slot_of))
+    return MOE_EINVAL;
+  if (aux_loss && !prob_mean) return MOE_EINVAL;
+  if ((st = check_ws(p, ws, ws_bytes))) return st;
+  if (p->T == 0) {
+    MOE_TRY(launch_fill_zero32(counts, p->n_experts, stream));
+    MOE_TRY(launch_fill_zero32(offsets, p->n_experts + 1, stream));
+    MOE_TRY(launch_fill_zero32(n_dropped, 1, stream));
+    if (aux_loss) MOE_TRY(launch_fill_zero32(aux_loss, 1, stream));
+    return MOE_OK;
+  }
+  const Layout L = make_layout(*p);
+  char* wsb = (char*)ws;
+  const bool cut = p->capacity > 0;
+  int32_t* off0 = cut ? (int32_t*)(wsb + L.off0) : offsets;
+  DispatchArgs a;
+  a.idx = topk_idx;
+  a.prob_mean_in = prob_mean;
+  a.partials = nullptr;
+  a.n_partials = 0;
+  a.prob_mean_out = nullptr;
+  a.counts = counts;
+  a.offsets = off0;
+  a.perm = perm;
+  a.slot_of = slot_of;
+  a.n_dropped = n_dropped;
+  a.aux = aux_loss;
+  a.chunk_ws = (int32_t*)(wsb + L.chunk);
+  a.T = p->T;
+  a.E = p->n_experts;
+  a.k = p->top_k;
+  a.capacity = p->capacity;
+  a.aux_coef = p->aux_coef;
+  MOE_TRY(launch_dispatch(a, stream));
+  if (cut)
+    MOE_TRY(launch_reassign(
+        reassign_args(p, topk_idx, topk_gate, logits, off0, offsets, perm,
+                      slot_of, n_dropped, (int32_t*)(wsb + L.rslot),
+                      (int32_t*)(wsb + L.newe)),
+        stream));
+  return MOE_OK;
 }
 
 int32_t moe_expert_ffn(const moe_problem* p, const void* x,
@@ -338,8 +431,11 @@ int32_t moe_layer_forward(const moe_problem* p, const void* x,
   MOE_TRY(launch_router_logits_partial(p->dtype, x, w_router, part, p->T,
                                        p->d_model, p->n_experts, L.ksplit,
                                        stream));
+  const bool reassign =
+      p->overflow == MOE_OVERFLOW_REASSIGN && p->capacity > 0;
+  float* logits = reassign ? (float*)(wsb + L.logits) : nullptr;
   MOE_TRY(launch_route_select_from(part, L.ksplit, router_bias, select_bias,
-                                   nullptr, idx, gate, rpart, p->T,
+                                   logits, idx, gate, rpart, p->T,
                                    p->n_experts, p->top_k, p->scoring,
                                    p->raw_gates, stream));
   DispatchArgs a;
@@ -360,7 +456,16 @@ int32_t moe_layer_forward(const moe_problem* p, const void* x,
   a.k = p->top_k;
   a.capacity = p->capacity;
   a.aux_coef = p->aux_coef;
+  if (reassign) a.offsets = (int32_t*)(wsb + L.off0);
   MOE_TRY(launch_dispatch(a, stream));
+  if (reassign) {
+    a.offsets = (int32_t*)(wsb + L.offsets);
+    MOE_TRY(launch_reassign(
+        reassign_args(p, idx, gate, logits, (int32_t*)(wsb + L.off0),
+                      a.offsets, a.perm, a.slot_of, a.n_dropped,
+                      (int32_t*)(wsb + L.rslot), (int32_t*)(wsb + L.newe)),
+        stream));
+  }
   void* y = wsb + L.y;
   FfnArgs f = ffn_args(p, x, a.perm, a.offsets, w, wsb + L.h, y);
   MOE_TRY(launch_expert_up(f, stream));

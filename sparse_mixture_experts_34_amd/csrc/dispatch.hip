@@ -255,6 +255,267 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(DispatchArgs a,
                   a.slot_of, lane);
 }
 
+// ---------------------------------------------------------------------------
+// Overflow by random reassignment (letsbuildsolutions.com "How Mixture of
+// Experts Works", Token Dropping and Overflow Handling: overflow tokens go
+// to expert slots with room left, weighted by the new expert's router
+// probability).  Dropped assignments are visited in ascending id; each
+// takes a free slot drawn with Philox4x32-10, so the walk is sequential:
+// one wave, lanes = experts (4 per lane), the draws of a 64-assignment
+// chunk computed in parallel.
+// ---------------------------------------------------------------------------
+
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers:
+// As Easy as 1, 2, 3", SC 2011): word 0 of the output block.
+__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1,
+                                                 uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  return c0;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int rdlane(int v, int l) {
+  return __builtin_amdgcn_readlane(v, l);
+}
+
+// The sequential walk.  Lane l holds experts l + 64c (c < MAXC): their
+// free slots and the exclusive prefix of free slots over all experts in
+// ascending order, kept up to date by -1 past the chosen expert, so a pick
+// needs no scan: the token's own experts are taken out of the prefix with
+// a few scalar reads, and one ballot finds the expert holding slot r.
+// Writes the new expert (newe) and its rank among the expert's moved rows
+// (rslot) for every moved assignment, -1 elsewhere, then the offsets.
+// KK >= k: slots per token handled (unused ones hold expert -1).
+template <int MAXC, int KK>
+__global__ __launch_bounds__(64) void reassign_kernel(ReassignArgs a) {
+  const int lane = threadIdx.x;
+  const long long tk = (long long)a.T * a.k;
+  const int E = a.E, k = a.k;
+  int spare[MAXC], pre[MAXC], moved[MAXC];
+  int run = 0;
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int e = lane + 64 * c;
+    spare[c] = e < E ? a.capacity - (a.off0[e + 1] - a.off0[e]) : 0;
+    moved[c] = 0;
+    const int inc = wave_incl_scan(spare[c], lane);
+    pre[c] = run + inc - spare[c];
+    run += rdlane(inc, 63);
+  }
+  int total = run;                       // free slots left (uniform)
+  int cur_t = -1;
+  int cur_e[KK];
+#pragma unroll
+  for (int jj = 0; jj < KK; ++jj) cur_e[jj] = -1;
+
+  // per-lane view of assignment base + lane: dropped?, token, its experts
+  auto load = [&](long long base, bool& drop, int& tok, int* te) {
+    const long long aid = base + lane;
+    drop = false;
+    tok = (int)(aid / k);
+    if (aid < tk) {
+      const int ea = a.idx[aid];
+      drop = a.slot_of[aid] < 0 && (unsigned)ea < (unsigned)E;
+    }
+#pragma unroll
+    for (int jj = 0; jj < KK; ++jj)
+      te[jj] = (aid < tk && jj < k) ? a.idx[(size_t)tok * k + jj] : -1;
+  };
+  bool drop_n;
+  int tok_n, te_n[KK];
+  load(0, drop_n, tok_n, te_n);
+  for (long long base = 0; base < tk; base += 64) {
+    const bool drop = drop_n;
+    const int tok = tok_n;
+    int te[KK];
+#pragma unroll
+    for (int jj = 0; jj < KK; ++jj) te[jj] = te_n[jj];
+    if (base + 64 < tk) load(base + 64, drop_n, tok_n, te_n);   // prefetch
+    const long long aid = base + lane;
+    uint64_t mask = __ballot(drop);
+    int my_rank = -1, my_e = -1;
+    if (mask && total > 0) {
+      const uint32_t x = drop ? philox_word0((uint32_t)aid,
+                                             (uint32_t)(aid >> 32), 0u, 0u,
+                                             a.key0, a.key1)
+                              : 0u;
+      while (mask) {
+        const int b = __ffsll((unsigned long long)mask) - 1;
+        mask &= mask - 1;
+        // free slots of the token's own experts leave the candidate set.
+        // With one slot per token that expert is the one that overflowed,
+        // which has no free slot: nothing to exclude.
+        int sx[KK];
+        int excl = 0;
+        int j = 0;
+#pragma unroll
+        for (int jj = 0; jj < KK; ++jj) sx[jj] = 0;
+        if constexpr (KK > 1) {
+          const int t = rdlane(tok, b);
+          j = (int)((base + b) - (long long)t * k);
+          if (t != cur_t) {
+            cur_t = t;
+#pragma unroll
+            for (int jj = 0; jj < KK; ++jj) cur_e[jj] = rdlane(te[jj], b);
+          }
+#pragma unroll
+          for (int jj = 0; jj < KK; ++jj) {
+            const int e = cur_e[jj];
+            if ((unsigned)e < (unsigned)E) {
+              int v = 0;
+#pragma unroll
+              for (int c = 0; c < MAXC; ++c)
+                if ((e >> 6) == c) v = rdlane(spare[c], e & 63);
+              sx[jj] = v;
+              excl += v;
+            }
+          }
+        }
+        const int avail = total - excl;
+        if (avail <= 0) continue;        // stays dropped
+        const uint32_t xb = (uint32_t)rdlane((int)x, b);
+        const int r = (int)(((unsigned long long)xb * (unsigned)avail) >> 32);
+        int e_new = -1;
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+          const int e = lane + 64 * c;
+          int adj = pre[c];
+          bool mine = false;
+          if constexpr (KK > 1) {
+#pragma unroll
+            for (int jj = 0; jj < KK; ++jj) {
+              adj -= cur_e[jj] < e ? sx[jj] : 0;
+              mine |= cur_e[jj] == e;
+            }
+          }
+          const int w = (e < E && !mine) ? spare[c] : 0;
+          const uint64_t hit = __ballot(w > 0 && adj <= r && r < adj + w);
+          if (e_new < 0 && hit)
+            e_new = (__ffsll((unsigned long long)hit) - 1) + 64 * c;
+        }
+        const int owner = e_new & 63, c_sel = e_new >> 6;
+        int rank = 0;
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+          if (c == c_sel) rank = rdlane(moved[c], owner);
+          const int e = lane + 64 * c;
+          if (c == c_sel && lane == owner) {
+            moved[c] += 1;
+            spare[c] -= 1;
+          }
+          if (e > e_new) pre[c] -= 1;
+        }
+        total -= 1;
+        if constexpr (KK > 1) {
+#pragma unroll
+          for (int jj = 0; jj < KK; ++jj)
+            if (jj == j) cur_e[jj] = e_new;
+        }
+        if (lane == b) {
+          my_rank = rank;
+          my_e = e_new;
+        }
+      }
+    }
+    if (aid < tk) {
+      a.rslot[aid] = my_rank;
+      a.newe[aid] = my_e;
+    }
+  }
+  // offsets over the kept plus moved rows (ascending expert)
+  run = 0;
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int e = lane + 64 * c;
+    const int kept = e < E ? (a.off0[e + 1] - a.off0[e]) + moved[c] : 0;
+    const int inc = wave_incl_scan(kept, lane);
+    if (e < E) a.offsets[e] = run + inc - kept;
+    run += rdlane(inc, 63);
+  }
+  if (lane == 0) {
+    a.offsets[E] = run;
+    *a.n_dropped = (int32_t)(tk - run);
+  }
+}
+
+// New rows: an expert's kept assignments keep their order and shift by the
+// rows moved into earlier experts; its moved ones follow them.  A moved
+// slot's gate: the new expert's score under the token's normaliser (its
+// original choice; all experts for raw softmax gates).  idx still holds
+// the original choice here.
+__global__ void reassign_rebuild_kernel(ReassignArgs a) {
+  const long long tk = (long long)a.T * a.k;
+  const long long aid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (aid >= tk) return;
+  const int old = a.slot_of[aid];
+  const int rk = a.rslot[aid];
+  int ns = -1;
+  if (old >= 0) {
+    const int e = a.idx[aid];
+    ns = old + (a.offsets[e] - a.off0[e]);
+  } else if (rk >= 0) {
+    const int e = a.newe[aid];
+    ns = a.offsets[e] + (a.off0[e + 1] - a.off0[e]) + rk;
+    const int t = (int)(aid / a.k);
+    const float* lg = a.logits + (size_t)t * a.E;
+    const int32_t* oi = a.idx + (size_t)t * a.k;
+    float g;
+    if (!a.scoring) {
+      float m = -INFINITY, ssum = 0.f;
+      if (!a.raw) {
+        for (int jj = 0; jj < a.k; ++jj)
+          if ((unsigned)oi[jj] < (unsigned)a.E) m = fmaxf(m, lg[oi[jj]]);
+        for (int jj = 0; jj < a.k; ++jj)
+          if ((unsigned)oi[jj] < (unsigned)a.E) ssum += __expf(lg[oi[jj]] - m);
+      } else {
+        for (int x = 0; x < a.E; ++x) m = fmaxf(m, lg[x]);
+        for (int x = 0; x < a.E; ++x) ssum += __expf(lg[x] - m);
+      }
+      g = __expf(lg[e] - m) / ssum;
+    } else {
+      float ssum = 0.f;
+      if (!a.raw)
+        for (int jj = 0; jj < a.k; ++jj)
+          if ((unsigned)oi[jj] < (unsigned)a.E) ssum += sigmoid_f(lg[oi[jj]]);
+      g = sigmoid_f(lg[e]) / (a.raw ? 1.f : ssum);
+    }
+    a.gate[aid] = g;
+  }
+  a.slot_of[aid] = ns;
+  if (ns >= 0) a.perm[ns] = (int32_t)aid;
+  if (aid >= a.offsets[a.E]) a.perm[aid] = -1;
+}
+
+// The moved slots' new experts, after every gate was computed from the
+// original choice.
+__global__ void reassign_commit_kernel(ReassignArgs a) {
+  const long long tk = (long long)a.T * a.k;
+  const long long aid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (aid < tk && a.rslot[aid] >= 0) a.idx[aid] = a.newe[aid];
+}
+
 __global__ void fill_zero32_kernel(uint32_t* p, long long n) {
   long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
@@ -274,6 +535,26 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
                                                    a.chunk_ws);
   dispatch_scan_kernel<<<1, SCAN_THREADS, 0, s>>>(a, nchunks);
   dispatch_scatter_kernel<<<blocks, DW * 64, 0, s>>>(a, nchunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_reassign(const ReassignArgs& a, hipStream_t s) {
+  const long long tk = (long long)a.T * a.k;
+  if (tk == 0) return hipSuccess;
+#define MOE_REASSIGN(C)                                              \
+  do {                                                               \
+    if (a.k == 1) reassign_kernel<C, 1><<<1, 64, 0, s>>>(a);         \
+    else if (a.k == 2) reassign_kernel<C, 2><<<1, 64, 0, s>>>(a);    \
+    else if (a.k <= 4) reassign_kernel<C, 4><<<1, 64, 0, s>>>(a);    \
+    else reassign_kernel<C, 8><<<1, 64, 0, s>>>(a);                  \
+  } while (0)
+  if (a.E <= 64) MOE_REASSIGN(1);
+  else if (a.E <= 128) MOE_REASSIGN(2);
+  else MOE_REASSIGN(4);
+#undef MOE_REASSIGN
+  const unsigned blocks = (unsigned)((tk + 255) / 256);
+  reassign_rebuild_kernel<<<blocks, 256, 0, s>>>(a);
+  reassign_commit_kernel<<<blocks, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

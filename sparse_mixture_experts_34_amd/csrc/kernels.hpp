@@ -78,6 +78,24 @@ struct DispatchArgs {
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
 
+// Overflow reassignment after launch_dispatch (which wrote the cut's
+// offsets into off0 and slot_of with -1 for drops; perm is rewritten).
+struct ReassignArgs {
+  int32_t* idx;           // [T*k] in/out
+  float* gate;            // [T*k] in/out
+  const float* logits;    // [T, E]
+  const int32_t* off0;    // [E+1] offsets after the cut
+  int32_t* offsets;       // [E+1] out
+  int32_t* perm;          // [T*k] out
+  int32_t* slot_of;       // [T*k] in (after the cut) / out
+  int32_t* n_dropped;     // [1] out
+  int32_t* rslot;         // [T*k] workspace: rank among an expert's moved
+  int32_t* newe;          // [T*k] workspace: the moved slot's new expert
+  int T, E, k, capacity, scoring, raw;
+  uint32_t key0, key1;
+};
+hipError_t launch_reassign(const ReassignArgs& a, hipStream_t s);
+
 // ---- expert FFN ------------------------------------------------------------
 struct FfnArgs {
   int dtype, act;

@@ -51,6 +51,8 @@ class Workload:
     wquant: str | None = None         # "int4": 4-bit expert weights
     scoring: str = "softmax"          # router scores: softmax | sigmoid
     raw_gates: bool = False           # gates without renormalisation
+    overflow: str = "drop"            # drop | reassign (random free slot)
+    overflow_seed: int = 0            # key of the reassignment draws
     notes: dict = field(default_factory=dict, compare=False, hash=False)
 
     @property
@@ -95,6 +97,13 @@ WORKLOADS = {
         "switch_top1_cf125", T=16384, d_model=2048, n_experts=64, top_k=1,
         d_ff=8192, act="gelu", dtype="bf16", capacity=320, zipf_s=1.1,
         seed_index=3),
+    # the Switch layer at capacity factor 1.0 with overflow reassigned to
+    # free slots at random instead of dropped
+    "switch_top1_cf1_reassign": Workload(
+        "switch_top1_cf1_reassign", T=16384, d_model=2048, n_experts=64,
+        top_k=1, d_ff=8192, act="gelu", dtype="bf16", capacity=256,
+        zipf_s=1.1, seed_index=3, overflow="reassign",
+        overflow_seed=20261203),
     "deepseek_v3": Workload(
         "deepseek_v3", T=4096, d_model=7168, n_experts=256, top_k=8,
         d_ff=2048, act="swiglu", dtype="bf16", capacity=0, n_shared=1,

@@ -180,4 +180,6 @@ def oracle_layer(inp, wl, tokens=None, lazy=False):
         else host(inp["router_bias"]),
         select_bias=None if inp["select_bias"] is None
         else host(inp["select_bias"]),
-        tokens=tokens, scoring=wl.scoring, renormalize=not wl.raw_gates)
+        tokens=tokens, scoring=wl.scoring, renormalize=not wl.raw_gates,
+        reassign_seed=wl.overflow_seed if wl.overflow == "reassign"
+        else None)

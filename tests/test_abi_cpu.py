@@ -92,6 +92,7 @@ BAD = [
     (dict(wquant=1, d_ff=320), moe.MOE_ENOTSUP),
     (dict(scoring=2), moe.MOE_EINVAL),
     (dict(raw_gates=3), moe.MOE_EINVAL),
+    (dict(overflow=2), moe.MOE_EINVAL),
 ]
 
 
@@ -99,7 +100,7 @@ def _prob(**kw):
     base = dict(T=16, d_model=128, n_experts=4, top_k=2, d_ff=256,
                 n_shared=0, capacity=0, act=moe.MOE_ACT_SWIGLU,
                 dtype=moe.MOE_DTYPE_BF16, aux_coef=0.01, wquant=0,
-                scoring=0, raw_gates=0)
+                scoring=0, raw_gates=0, overflow=0, overflow_seed=0)
     base.update(kw)
     return binding.moe_problem(*[base[f] for f, _ in
                                  binding.moe_problem._fields_])
@@ -215,6 +216,60 @@ def test_quantize_int4_validation():
         moe.MOE_ENOTSUP
     # nothing to do: OK without touching any pointer or the device
     assert lib.moe_quantize_int4(None, 0, 128, None, None, None) == moe.MOE_OK
+
+
+def test_struct_layouts_match_the_header():
+    # compile the header with the host compiler and compare sizes/offsets
+    src = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "moe.h"
+int main(void) {
+  printf("%zu %zu %zu %zu\n", sizeof(moe_problem),
+         offsetof(moe_problem, overflow_seed), sizeof(moe_expert_weights),
+         offsetof(moe_expert_weights, shared_w2_q));
+  return 0;
+}
+"""
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        exe = os.path.join(d, "t")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I",
+                        os.path.join(ROOT, "include"), "-I",
+                        "/opt/rocm/include", c, "-o", exe], check=True,
+                       capture_output=True)
+        out = subprocess.run([exe], capture_output=True, text=True,
+                             check=True).stdout.split()
+    P, W = binding.moe_problem, binding.moe_expert_weights
+    assert [int(v) for v in out] == [ctypes.sizeof(P),
+                                      P.overflow_seed.offset,
+                                      ctypes.sizeof(W),
+                                      W.shared_w2_q.offset]
+
+
+def test_reassign_validation():
+    lib = binding._lib
+    f = 0x1000
+    big = 1 << 40
+    drop = ctypes.byref(_prob(capacity=4))
+    re = ctypes.byref(_prob(capacity=4, overflow=1, overflow_seed=5))
+    # moe_dispatch cannot reassign (no gates/logits); the reassign entry
+    # needs the reassign mode and its extra inputs
+    assert lib.moe_dispatch(re, f, f, f, f, f, f, f, f, f, big, None) == \
+        moe.MOE_EINVAL
+    assert lib.moe_dispatch_reassign(drop, f, f, f, f, f, f, f, f, f, f, f,
+                                     big, None) == moe.MOE_EINVAL
+    assert lib.moe_dispatch_reassign(re, f, None, f, f, f, f, f, f, f, f, f,
+                                     big, None) == moe.MOE_EINVAL
+    assert lib.moe_dispatch_reassign(re, f, f, None, f, f, f, f, f, f, f, f,
+                                     big, None) == moe.MOE_EINVAL
+    assert moe.moe_workspace_bytes(_prob(T=1024, capacity=4, overflow=1)) > \
+        moe.moe_workspace_bytes(_prob(T=1024, capacity=4))
+    need = moe.moe_workspace_bytes(_prob(capacity=4, overflow=1))
+    assert lib.moe_dispatch_reassign(re, f, f, f, f, f, f, f, f, f, f, f,
+                                     need - 1, None) == moe.MOE_EWORKSPACE
 
 
 def test_update_select_bias_validation():
