@@ -56,8 +56,10 @@ __device__ __forceinline__ void scatter_chunk(
     const int32_t* __restrict__ idx, long long tk, int c, int* base,
     const int32_t* offsets, int E, int32_t* __restrict__ perm,
     int32_t* __restrict__ slot_of, int lane) {
-  for (int r = 0; r < CH / 64; ++r) {
-    const long long a = (long long)c * CH + r * 64 + lane;
+  const long long c0 = (long long)c * CH;
+  const int rounds = (int)min((long long)(CH / 64), (tk - c0 + 63) / 64);
+  for (int r = 0; r < rounds; ++r) {
+    const long long a = c0 + r * 64 + lane;
     int e = a < tk ? idx[a] : -1;
     if ((unsigned)e >= (unsigned)E) e = -1;
     int before = 0;
@@ -86,8 +88,8 @@ __device__ __forceinline__ void scatter_chunk(
   }
   // perm rows past the kept total are set to -1
   const int total = offsets[E];
-  for (int r = 0; r < CH / 64; ++r) {
-    const long long p = (long long)c * CH + r * 64 + lane;
+  for (int r = 0; r < rounds; ++r) {
+    const long long p = c0 + r * 64 + lane;
     if (p < tk && p >= total) perm[p] = -1;
   }
 }
@@ -96,7 +98,8 @@ __device__ __forceinline__ void scatter_chunk(
 // chunk[c*E + e] holds per-chunk counts on entry and chunk base ranks on
 // exit.  Writes counts, offsets, n_dropped, prob mean and aux.
 //
-// Each expert gets TPE = NTHR / E (a power of two) threads: thread j scans a
+// Each expert gets TPE threads (a power of two, at most NTHR / E, no more
+// than the chunks and partial rows need): thread j scans a
 // contiguous range of chunks and sums an interleaved share of the
 // probability partial rows; the TPE pieces are combined in the fixed order
 // j = 0, 1, ... (deterministic).  red_* hold NTHR entries.
@@ -105,8 +108,12 @@ __device__ void scan_all(int* chunk, int nchunks, const DispatchArgs& a,
                          int32_t* offsets_out, int* red_i, float* red_f) {
   const int t = threadIdx.x;
   const int E = a.E;
+  // threads per expert: enough to split the chunk scan and the partial
+  // rows, at most NTHR / E (the pieces are combined serially)
+  const int n_part = a.partials ? a.n_partials : 0;
+  const int need = max(max(nchunks, (n_part + 15) / 16), 1);
   int tpe = 1;
-  while (tpe * 2 * E <= NTHR) tpe *= 2;
+  while (tpe < need && tpe * 2 * E <= NTHR) tpe *= 2;
   const int e = t / tpe, j = t % tpe;
   const bool act = e < E;
   // ---- per-chunk counts -> chunk base ranks, per-expert totals ----------
@@ -142,7 +149,7 @@ __device__ void scan_all(int* chunk, int nchunks, const DispatchArgs& a,
   __syncthreads();
   if (act && j == 0) red_i[e] = kept_e;
   __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
+  for (int o = 1; o < E; o <<= 1) {   // entries >= E stay 0
     int v = (t < 256 && t >= o) ? red_i[t - o] : 0;
     __syncthreads();
     if (t < 256) red_i[t] += v;
@@ -190,7 +197,9 @@ __device__ void scan_all(int* chunk, int nchunks, const DispatchArgs& a,
   __syncthreads();
   if (act && j == 0) red_f[e] = term;
   __syncthreads();
-  for (int o = 128; o >= 1; o >>= 1) {
+  int half = 1;
+  while (half * 2 < E) half *= 2;     // terms >= E are 0
+  for (int o = half; o >= 1; o >>= 1) {
     if (t < o) red_f[t] += red_f[t + o];
     __syncthreads();
   }
