@@ -541,7 +541,7 @@ constexpr int TL_WAVES = 8;
 // False for a workgroup with no tile.
 template <int NTHR>
 __device__ bool find_tile_n(const FfnArgs& a, int G, int BM, int NB,
-                            int* s_info) {
+                            int* s_info, int chunk = 0) {
   __shared__ int s_wsum[NTHR / 64];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
@@ -568,9 +568,15 @@ __device__ bool find_tile_n(const FfnArgs& a, int G, int BM, int NB,
   }
   incl += base;
   const int excl = incl - span;
-  const int per_xcd = (total + N_XCD - 1) / N_XCD;
   const int slot = blockIdx.x / N_XCD;
-  const int L = slot < per_xcd ? (blockIdx.x % N_XCD) * per_xcd + slot : total;
+  int L;
+  if (chunk > 0) {
+    // runs of `chunk` logical tiles dealt to the XCDs in turn
+    L = ((slot / chunk) * N_XCD + blockIdx.x % N_XCD) * chunk + slot % chunk;
+  } else {
+    const int per_xcd = (total + N_XCD - 1) / N_XCD;
+    L = slot < per_xcd ? (blockIdx.x % N_XCD) * per_xcd + slot : total;
+  }
   if (t < G && L >= excl && L < incl) {
     const int nt = span / NB;
     const int r = L - excl;
@@ -884,6 +890,283 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
 
 
 // ===========================================================================
+// panel schedule (bf16)
+// ===========================================================================
+// For experts with a few hundred rows each (many experts, moderate batch):
+// the layer is weight-bound there, so every weight byte should cross HBM
+// once.  A workgroup owns a panel of up to PN_BM rows of one group and 16*CG
+// weight rows per wave (256 per workgroup: SwiGLU 128 gate + the matching
+// 128 up rows, else 256 output columns), over the whole of K.  Each wave
+// streams its own weight rows from HBM straight into MFMA B registers
+// (16x16x32, PF-deep register ring, as in the stream schedule); the panel's
+// token rows (A) are read once per workgroup with ordinary loads, written to
+// a double-buffered, XOR-swizzled LDS slice and read by all eight waves.
+// Row tiles past the panel's rows issue no MFMAs and no loads, so a ragged
+// expert costs its own rows, not a full tile.  Every load is an ordinary
+// compiler-visible load, so the compiler's waits are exact: a wait for one
+// slice never waits for later weight loads.
+constexpr int PN_KSTEP = 64;     // K per step (two 16x16x32 MFMAs)
+#ifndef PN_BM_CFG
+#define PN_BM_CFG 256
+#endif
+#ifndef PN_L_CFG
+#define PN_L_CFG 1
+#endif
+#ifndef PN_W_CFG
+#define PN_W_CFG 8
+#endif
+#ifndef PN_NBG_CFG
+#define PN_NBG_CFG 2
+#endif
+constexpr int PN_BM = PN_BM_CFG;   // rows per panel
+constexpr int PN_L = PN_L_CFG;     // steps of lookahead
+constexpr int PN_W = PN_W_CFG;     // waves per workgroup
+constexpr int PN_NBG = PN_NBG_CFG; // 16-row weight groups per wave
+#ifndef PN_CHUNK
+#define PN_CHUNK 1
+#endif
+#ifndef PN_RA
+#define PN_RA 4
+#endif
+
+// LDS slice: BM rows of 128 bytes; 16-byte chunk c of row r sits at
+// position c ^ ((r >> 1) & 7), so that a 16-row MFMA operand read (one chunk
+// per row) spreads over all banks.
+__device__ __forceinline__ int pn_key(int r) { return (r >> 1) & 7; }
+
+// End of a step: this wave's LDS writes and reads are done, then meet the
+// other waves.  No vmcnt wait: loads for later steps stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+template <int NMAT, int CG>
+struct PanelB {
+  u32x4 b[NMAT][CG][2];
+};
+
+constexpr int pn_gcd(int x, int y) { return y == 0 ? x : pn_gcd(y, x % y); }
+constexpr int pn_lcm(int x, int y) { return x / pn_gcd(x, y) * y; }
+
+// BM rows per panel; L steps of lookahead for both operands: step s stores
+// A step s+1 into LDS and issues A step s+1+L and weight step s+1+L, so L
+// register sets of A and L+1 weight slots are live.  A and weight loads of
+// one step are issued together, A first: vector loads complete in order, so
+// a wait for A step s+1 also waits for weight step s, which step s needs
+// anyway, and for nothing later.
+// W waves per workgroup, NBG groups of 16 weight rows per wave (SwiGLU:
+// NBG/2 gate groups and the matching up groups).
+template <int MODE, int BM, int L, int W, int NBG>
+__global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
+                                                              int NB) {
+  constexpr int NMAT = MODE == UP_SWIGLU ? 2 : 1;
+  constexpr int CG = NBG / NMAT;                   // 16-column groups / wave
+  constexpr int MT = BM / 16;                      // 16-row tiles per panel
+  constexpr int COLS = W * 16 * CG;                // output columns / panel
+  constexpr int SL = BM * PN_KSTEP;                // elements per slice
+  constexpr int AI = BM * PN_KSTEP / 8 / (W * 64); // A loads / lane
+  constexpr int NSLOT = L + 1;                     // weight ring slots
+  static_assert(CG * NMAT == NBG && AI * W * 64 * 8 == SL, "shape");
+  __shared__ __attribute__((aligned(16))) bf16 S0[SL];
+  __shared__ __attribute__((aligned(16))) bf16 S1[SL];
+  __shared__ int s_info[3];
+
+  const int G = a.E + a.n_shared;
+  if (!find_tile_n<W * 64>(a, G, BM, NB, s_info, PN_CHUNK ? NB : 0)) return;
+  const int g = s_info[0], r0 = s_info[1], nb = s_info[2];
+  const Group gr = group_of(g, a.offsets, a.E, a.T, a.k);
+  const int N = MODE == DOWN ? a.d : a.d_ff;
+  const int K = MODE == DOWN ? a.d_ff : a.d;
+  const int nvalid = min(BM, gr.rows - r0);
+  const int ntile = (nvalid + 15) >> 4;
+  const void *w0v, *w1v, *biasv;
+  group_weights<MODE>(a, g, gr.shared, N, K, w0v, w1v, biasv);
+  const bf16* wm[2] = {(const bf16*)w0v, (const bf16*)w1v};
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, kq = lane >> 4;
+  const int nbase = nb * COLS;
+
+  // A loads: thread covers rows (i*512 + tid) / 8, chunk tid % 8 of each
+  // step (8 threads read one row's 128 bytes); 32-bit element offsets.
+  // Rows past the panel re-read its last row (one cached line per
+  // instruction): every load is unconditional, which keeps the compiler's
+  // wait counts exact across the loop.
+  const bf16* abase = (const bf16*)(MODE == DOWN ? a.h : a.x);
+  uint32_t ao[AI];
+  int lo[AI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int row = (i * W * 64 + tid) >> 3;
+    const int p = tid & 7;
+    const int ri = r0 + min(row, nvalid - 1);
+    const int arow_g = MODE == DOWN ? gr.out0 + ri
+                                    : (gr.shared ? ri : a.perm[gr.out0 + ri] / a.k);
+    ao[i] = (uint32_t)arow_g * (uint32_t)K + (uint32_t)(p << 3);
+    lo[i] = row * PN_KSTEP + ((p ^ pn_key(row)) << 3);
+  }
+  // B: wave column group c holds weight rows nbase + 16*(wave*CG + c) + col;
+  // lane kq takes k = kq*16 .. kq*16+15 of each 64-wide step.  A partial
+  // last block re-reads row N-1 and stores nothing for it.
+  const bf16* brow[NMAT][CG];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int c = 0; c < CG; ++c)
+      brow[m][c] = wm[m] + (size_t)min(nbase + 16 * (wave * CG + c) + col, N - 1) * K + kq * 16;
+  // MFMA A operand of row tile t, half h: row 16t + col, chunk 2kq + h; the
+  // swizzle key of row 16t + col is key(col) for every t.
+  const int aoff0 = col * PN_KSTEP + (((2 * kq) ^ pn_key(col)) << 3);
+  const int aoff1 = col * PN_KSTEP + (((2 * kq + 1) ^ pn_key(col)) << 3);
+
+  const int nk = K / PN_KSTEP;
+  u32x4 ar[L][AI];
+  // Loads past the last step re-read the last step (cached, never used).
+  auto loadA = [&](u32x4 (&r)[AI], int s) {
+    const int k0 = min(s, nk - 1) * PN_KSTEP;
+#pragma unroll
+    for (int i = 0; i < AI; ++i) r[i] = ldg16(abase + ao[i] + k0);
+  };
+  auto storeA = [&](const u32x4 (&r)[AI], bf16* S) {
+#pragma unroll
+    for (int i = 0; i < AI; ++i) *reinterpret_cast<u32x4*>(S + lo[i]) = r[i];
+  };
+  PanelB<NMAT, CG> ring[NSLOT];
+  auto loadB = [&](PanelB<NMAT, CG>& b, int s) {
+    const int k0 = min(s, nk - 1) * PN_KSTEP;
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int c = 0; c < CG; ++c) {
+        b.b[m][c][0] = ldg16(brow[m][c] + k0);
+        b.b[m][c][1] = ldg16(brow[m][c] + k0 + 8);
+      }
+  };
+  f32x4 acc[NMAT][CG][MT];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int c = 0; c < CG; ++c)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[m][c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // prologue in the loop's issue order: A step 0 into S0, then A step j
+  // (register set j % L) and weight step j for j = 1..L; weight step 0
+  // right after A step 0
+  loadA(ar[0], 0);
+  loadB(ring[0], 0);
+  storeA(ar[0], S0);
+#pragma unroll
+  for (int j = 1; j <= L; ++j) {
+    loadA(ar[j % L], j);
+    loadB(ring[j], j);
+  }
+  lds_barrier();
+
+  // The K loop for NT active row tiles (a compile-time count, so the loop
+  // body is straight-line code: the compiler pipelines the LDS operand reads
+  // with the MFMAs and its wait counts stay exact).  Tiles past the panel's
+  // rows up to NT hold copies of its last row; their sums are not stored.
+  auto kloop = [&](auto ntc) {
+    constexpr int NT = decltype(ntc)::value;
+    // MFMAs of one step: half h (k 8h..8h+7 of each lane's 16) outermost,
+    // so the two MFMAs into one accumulator are a tile sweep apart
+    auto compute = [&](const bf16* S, const PanelB<NMAT, CG>& b) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16* sa = S + (h ? aoff1 : aoff0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          V16 f;
+          f.u = *reinterpret_cast<const u32x4*>(sa + t * 16 * PN_KSTEP);
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int c = 0; c < CG; ++c) {
+              V16 bv;
+              bv.u = b.b[m][c][h];
+              acc[m][c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.h, bv.h, acc[m][c][t], 0, 0, 0);
+            }
+        }
+      }
+      // order: PN_RA operand reads ahead, then each tile's MFMAs followed
+      // by the next read (bounds the live operand registers)
+      constexpr int NM = NMAT * CG;
+      constexpr int RA = PN_RA < 2 * NT ? PN_RA : 2 * NT;
+      __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);   // DS reads
+#pragma unroll
+      for (int i = 0; i < 2 * NT - RA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);   // MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, RA * NM, 0);
+    };
+    // Step s (u = s mod U): reads slice s % 2 and weight slot s % (L+1);
+    // first writes A step s+1 (register set (s+1) % L) into the other
+    // slice, whose readers finished at the last barrier, and reloads that
+    // set with A step s+1+L; after the MFMAs refills its weight slot with
+    // step s+1+L.
+    auto step = [&](int s, int u) {
+      bf16* cur = (u & 1) ? S1 : S0;
+      bf16* nxt = (u & 1) ? S0 : S1;
+      storeA(ar[(u + 1) % L], nxt);
+      loadA(ar[(u + 1) % L], s + 1 + L);
+      compute(cur, ring[u % NSLOT]);
+      loadB(ring[u % NSLOT], s + 1 + L);
+      lds_barrier();
+    };
+    // whole trips of U steps (constant slice, set and slot indices), then
+    // the remaining steps
+    constexpr int U = pn_lcm(2, pn_lcm(L, NSLOT));
+    const int ntrip = nk / U;
+    for (int tr = 0; tr < ntrip; ++tr) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) step(tr * U + u, u);
+    }
+#pragma unroll
+    for (int u = 0; u < U - 1; ++u)
+      if (ntrip * U + u < nk) step(ntrip * U + u, u);
+  };
+  // two instances: panels filling at most half the tiles run the half-size
+  // loop (more instances overflow the register file)
+  static_assert(MT % 2 == 0, "half panel");
+  if (ntile > MT / 2) kloop(IntC<MT>{});
+  else kloop(IntC<MT / 2>{});
+
+  // epilogue: lane holds column n of group c and rows 16t + 4kq + r
+  bf16* outp = (bf16*)(MODE == DOWN ? a.y : a.h);
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    const int n = nbase + 16 * (wave * CG + c) + col;
+    if (n >= N) continue;
+    float bias = 0.f;
+    if (MODE != UP_SWIGLU && biasv) bias = (float)((const bf16*)biasv)[n];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      if (t < ntile) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * t + 4 * kq + r;
+          if (i < nvalid) {
+            float v;
+            if (MODE == UP_SWIGLU)
+              v = silu(acc[0][c][t][r]) * acc[NMAT - 1][c][t][r];
+            else if (MODE == UP_GELU) v = gelu_erf(acc[0][c][t][r] + bias);
+            else v = acc[0][c][t][r] + bias;
+            outp[(size_t)(gr.out0 + r0 + i) * N + n] = (bf16)v;
+          }
+        }
+      }
+    }
+  }
+}
+
+// ===========================================================================
 // float32 schedule
 // ===========================================================================
 // Linear row-tile id -> (group, first row); false past the last tile.
@@ -974,6 +1257,12 @@ hipError_t launch_mode(const FfnArgs& a, hipStream_t s, int sched, int rt,
     else
       ffn_tiled_kernel<MODE, 128, 32, 6, TL_WAVES>
           <<<(unsigned)tiles, TL_WAVES * 64, 0, s>>>(a, NB);
+  } else if (sched == 4) {
+    // max_tiles counts panels of PN_BM rows
+    constexpr int cols = PN_W * 16 * (MODE == UP_SWIGLU ? PN_NBG / 2 : PN_NBG);
+    const int NB = (N + cols - 1) / cols;
+    long long tiles = (long long)(max_tiles + N_XCD - 1) / N_XCD * N_XCD * NB;
+    ffn_panel_kernel<MODE, PN_BM, PN_L, PN_W, PN_NBG><<<(unsigned)tiles, PN_W * 64, 0, s>>>(a, NB);
   } else {
     dim3 grid(max_tiles, (N + F32_BN - 1) / F32_BN);
     ffn_f32_kernel<MODE><<<grid, 256, 0, s>>>(a);
@@ -985,11 +1274,12 @@ hipError_t launch_mode(const FfnArgs& a, hipStream_t s, int sched, int rt,
 
 // Schedule choice from shapes only (no device readback):
 //   f32 -> float32 kernel; bf16 with at most 64 assignments per expert on
-//   average -> stream; otherwise tiled.
+//   average -> stream; up to 256 -> panel; otherwise tiled.
 int ffn_schedule(int dtype, int T, int k, int E) {
   if (dtype != 1) return 2;
   const long long tk = (long long)T * k;
   if (tk <= 64LL * E) return 0;        // stream
+  if (tk <= 256LL * E) return 4;       // panel
   if (tk >= 1024LL * E) return 1;      // tiled, 256-row tiles
   return 3;                            // tiled, 128-row tiles
 }
@@ -1007,7 +1297,7 @@ Plan plan_of(const FfnArgs& a) {
     const int maxrows = a.T;   // a token picks an expert at most once
     p.rt = maxrows <= 16 ? 1 : (maxrows <= 32 ? 2 : 4);
   }
-  const int bm = p.sched == 1 ? 256 : (p.sched == 3 ? 128 : F32_BM);
+  const int bm = p.sched == 1 ? 256 : (p.sched == 4 ? PN_BM : (p.sched == 3 ? 128 : F32_BM));
   p.max_tiles = (int)((tk + bm - 1) / bm) + a.E +
                 (a.n_shared ? (a.T + bm - 1) / bm : 0);
   return p;

@@ -29,10 +29,10 @@ SMALL = [
     W("mixtral_s_stream_wide", T=24, d_model=1024, n_experts=8, top_k=2,
       d_ff=2048, act="swiglu", dtype="bf16", capacity=0, router_std=0.02,
       seed_index=25),
-    W("mixtral_s_tiled", T=700, d_model=256, n_experts=8, top_k=2,
+    W("mixtral_s_panel", T=700, d_model=256, n_experts=8, top_k=2,
       d_ff=384, act="swiglu", dtype="bf16", capacity=0, router_std=0.02,
       seed_index=12),
-    W("switch_s_tiled_drops", T=1500, d_model=128, n_experts=16, top_k=1,
+    W("switch_s_panel_drops", T=1500, d_model=128, n_experts=16, top_k=1,
       d_ff=320, act="gelu", dtype="bf16", capacity=93, zipf_s=1.1,
       seed_index=13),
     W("switch_s_stream_drops", T=600, d_model=128, n_experts=16, top_k=1,
@@ -41,7 +41,7 @@ SMALL = [
     W("deepseek_s_stream", T=300, d_model=192, n_experts=32, top_k=4,
       d_ff=128, act="swiglu", dtype="bf16", capacity=0, n_shared=1,
       select_bias_std=0.1, seed_index=15),
-    W("deepseek_s_tiled", T=700, d_model=192, n_experts=32, top_k=4,
+    W("deepseek_s_panel", T=700, d_model=192, n_experts=32, top_k=4,
       d_ff=128, act="swiglu", dtype="bf16", capacity=0, n_shared=1,
       select_bias_std=0.1, seed_index=16),
     W("gelu_shared_f32_drops", T=50, d_model=64, n_experts=3, top_k=2,
@@ -58,6 +58,17 @@ SMALL = [
     W("gelu_bf16_tiled_shared_drops", T=900, d_model=128, n_experts=4,
       top_k=2, d_ff=192, act="gelu", dtype="bf16", capacity=400, n_shared=1,
       seed_index=22),
+    # panels (64*E < T*k <= 256*E): experts and the shared expert spanning
+    # several 256-row panels, partial weight blocks, an odd K-step count
+    W("swiglu_panel_multi_shared", T=1000, d_model=192, n_experts=8,
+      top_k=2, d_ff=320, act="swiglu", dtype="bf16", capacity=0,
+      n_shared=1, router_std=0.02, seed_index=26),
+    W("gelu_panel_bias_drops", T=3000, d_model=256, n_experts=16, top_k=1,
+      d_ff=448, act="gelu", dtype="bf16", capacity=200, zipf_s=0.3,
+      seed_index=27),
+    # 128-row tiles (256*E < T*k < 1024*E) with SwiGLU
+    W("swiglu_tiled128", T=1500, d_model=128, n_experts=4, top_k=2,
+      d_ff=256, act="swiglu", dtype="bf16", capacity=0, seed_index=28),
     # 256-row tiles (T*k >= 1024*E), ragged M and partial N blocks
     W("swiglu_bm256", T=2200, d_model=128, n_experts=2, top_k=1, d_ff=384,
       act="swiglu", dtype="bf16", capacity=0, seed_index=23),
