@@ -930,8 +930,7 @@ constexpr int PN_NBG = PN_NBG_CFG; // 16-row weight groups per wave
 #endif
 
 // LDS slice: BM rows of 128 bytes; 16-byte chunk c of row r sits at
-// position c ^ ((r >> 1) & 7), so that a 16-row MFMA operand read (one chunk
-// per row) spreads over all banks.
+// position c ^ ((r >> 1) & 7).
 __device__ __forceinline__ int pn_key(int r) { return (r >> 1) & 7; }
 
 // End of a step: this wave's LDS writes and reads are done, then meet the
@@ -1011,19 +1010,22 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
     ao[i] = (uint32_t)arow_g * (uint32_t)K + (uint32_t)(p << 3);
     lo[i] = row * PN_KSTEP + ((p ^ pn_key(row)) << 3);
   }
-  // B: wave column group c holds weight rows nbase + 16*(wave*CG + c) + col;
-  // lane kq takes k = kq*16 .. kq*16+15 of each 64-wide step.  A partial
-  // last block re-reads row N-1 and stores nothing for it.
+  // B: wave column group c holds weight rows nbase + 16*(wave*CG + c) + col.
+  // MFMA h of a 64-wide step contracts k-chunk kq + 4h (8 elements) of lane
+  // group kq, for A and B alike: with this order the A operand reads of
+  // 16 rows x 4 chunks hit every LDS bank once (the order 2kq + h measured
+  // about three conflict cycles per read).  A partial last block re-reads
+  // row N-1 and stores nothing for it.
   const bf16* brow[NMAT][CG];
 #pragma unroll
   for (int m = 0; m < NMAT; ++m)
 #pragma unroll
     for (int c = 0; c < CG; ++c)
-      brow[m][c] = wm[m] + (size_t)min(nbase + 16 * (wave * CG + c) + col, N - 1) * K + kq * 16;
-  // MFMA A operand of row tile t, half h: row 16t + col, chunk 2kq + h; the
+      brow[m][c] = wm[m] + (size_t)min(nbase + 16 * (wave * CG + c) + col, N - 1) * K + kq * 8;
+  // MFMA A operand of row tile t, half h: row 16t + col, chunk kq + 4h; the
   // swizzle key of row 16t + col is key(col) for every t.
-  const int aoff0 = col * PN_KSTEP + (((2 * kq) ^ pn_key(col)) << 3);
-  const int aoff1 = col * PN_KSTEP + (((2 * kq + 1) ^ pn_key(col)) << 3);
+  const int aoff0 = col * PN_KSTEP + ((kq ^ pn_key(col)) << 3);
+  const int aoff1 = col * PN_KSTEP + (((kq + 4) ^ pn_key(col)) << 3);
 
   const int nk = K / PN_KSTEP;
   u32x4 ar[L][AI];
@@ -1045,7 +1047,7 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
 #pragma unroll
       for (int c = 0; c < CG; ++c) {
         b.b[m][c][0] = ldg16(brow[m][c] + k0);
-        b.b[m][c][1] = ldg16(brow[m][c] + k0 + 8);
+        b.b[m][c][1] = ldg16(brow[m][c] + k0 + 32);
       }
   };
   f32x4 acc[NMAT][CG][MT];
@@ -1074,8 +1076,8 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
   // rows up to NT hold copies of its last row; their sums are not stored.
   auto kloop = [&](auto ntc) {
     constexpr int NT = decltype(ntc)::value;
-    // MFMAs of one step: half h (k 8h..8h+7 of each lane's 16) outermost,
-    // so the two MFMAs into one accumulator are a tile sweep apart
+    // MFMAs of one step: half h outermost, so the two MFMAs into one
+    // accumulator are a tile sweep apart
     auto compute = [&](const bf16* S, const PanelB<NMAT, CG>& b) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
