@@ -1030,14 +1030,17 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
   const int nk = K / PN_KSTEP;
   u32x4 ar[L][AI];
   // Loads past the last step re-read the last step (cached, never used).
-  auto loadA = [&](u32x4 (&r)[AI], int s) {
+  // the first NA of this thread's A loads (rows below NA * W * 64 / 8)
+  auto loadA = [&](auto nac, u32x4 (&r)[AI], int s) {
+    constexpr int NA = decltype(nac)::value;
     const int k0 = min(s, nk - 1) * PN_KSTEP;
 #pragma unroll
-    for (int i = 0; i < AI; ++i) r[i] = ldg16(abase + ao[i] + k0);
+    for (int i = 0; i < NA; ++i) r[i] = ldg16(abase + ao[i] + k0);
   };
-  auto storeA = [&](const u32x4 (&r)[AI], bf16* S) {
+  auto storeA = [&](auto nac, const u32x4 (&r)[AI], bf16* S) {
+    constexpr int NA = decltype(nac)::value;
 #pragma unroll
-    for (int i = 0; i < AI; ++i) *reinterpret_cast<u32x4*>(S + lo[i]) = r[i];
+    for (int i = 0; i < NA; ++i) *reinterpret_cast<u32x4*>(S + lo[i]) = r[i];
   };
   PanelB<NMAT, CG> ring[NSLOT];
   auto loadB = [&](PanelB<NMAT, CG>& b, int s) {
@@ -1057,25 +1060,16 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
     for (int c = 0; c < CG; ++c)
 #pragma unroll
       for (int t = 0; t < MT; ++t) acc[m][c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // prologue in the loop's issue order: A step 0 into S0, then A step j
-  // (register set j % L) and weight step j for j = 1..L; weight step 0
-  // right after A step 0
-  loadA(ar[0], 0);
-  loadB(ring[0], 0);
-  storeA(ar[0], S0);
-#pragma unroll
-  for (int j = 1; j <= L; ++j) {
-    loadA(ar[j % L], j);
-    loadB(ring[j], j);
-  }
-  lds_barrier();
-
   // The K loop for NT active row tiles (a compile-time count, so the loop
   // body is straight-line code: the compiler pipelines the LDS operand reads
   // with the MFMAs and its wait counts stay exact).  Tiles past the panel's
   // rows up to NT hold copies of its last row; their sums are not stored.
   auto kloop = [&](auto ntc) {
     constexpr int NT = decltype(ntc)::value;
+    // A rows 0 .. NT*16-1 only: loads per thread
+    constexpr int NA = (NT * 16 * 8 + W * 64 - 1) / (W * 64);
+    static_assert(NA >= 1 && NA <= AI, "A loads");
+    const IntC<NA> na{};
     // MFMAs of one step: half h outermost, so the two MFMAs into one
     // accumulator are a tile sweep apart
     auto compute = [&](const bf16* S, const PanelB<NMAT, CG>& b) {
@@ -1116,12 +1110,24 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
     auto step = [&](int s, int u) {
       bf16* cur = (u & 1) ? S1 : S0;
       bf16* nxt = (u & 1) ? S0 : S1;
-      storeA(ar[(u + 1) % L], nxt);
-      loadA(ar[(u + 1) % L], s + 1 + L);
+      storeA(na, ar[(u + 1) % L], nxt);
+      loadA(na, ar[(u + 1) % L], s + 1 + L);
       compute(cur, ring[u % NSLOT]);
       loadB(ring[u % NSLOT], s + 1 + L);
       lds_barrier();
     };
+    // prologue in the loop's issue order: A step 0 into S0, then A step j
+    // (register set j % L) and weight step j for j = 1..L; weight step 0
+    // right after A step 0
+    loadA(na, ar[0], 0);
+    loadB(ring[0], 0);
+    storeA(na, ar[0], S0);
+#pragma unroll
+    for (int j = 1; j <= L; ++j) {
+      loadA(na, ar[j % L], j);
+      loadB(ring[j], j);
+    }
+    lds_barrier();
     // whole trips of U steps (constant slice, set and slot indices), then
     // the remaining steps
     constexpr int U = pn_lcm(2, pn_lcm(L, NSLOT));
