@@ -906,28 +906,14 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
 // compiler-visible load, so the compiler's waits are exact: a wait for one
 // slice never waits for later weight loads.
 constexpr int PN_KSTEP = 64;     // K per step (two 16x16x32 MFMAs)
-#ifndef PN_BM_CFG
-#define PN_BM_CFG 256
-#endif
-#ifndef PN_L_CFG
-#define PN_L_CFG 1
-#endif
-#ifndef PN_W_CFG
-#define PN_W_CFG 8
-#endif
-#ifndef PN_NBG_CFG
-#define PN_NBG_CFG 2
-#endif
-constexpr int PN_BM = PN_BM_CFG;   // rows per panel
-constexpr int PN_L = PN_L_CFG;     // steps of lookahead
-constexpr int PN_W = PN_W_CFG;     // waves per workgroup
-constexpr int PN_NBG = PN_NBG_CFG; // 16-row weight groups per wave
-#ifndef PN_CHUNK
-#define PN_CHUNK 1
-#endif
-#ifndef PN_RA
-#define PN_RA 4
-#endif
+// Panel configuration (measured on the DeepSeek-V3 and Switch workloads;
+// 192- and 128-row panels, two steps of lookahead, 4 waves x 64 weight rows
+// and two 4-wave workgroups per CU were all slower):
+constexpr int PN_BM = 256;    // rows per panel
+constexpr int PN_L = 1;       // steps of lookahead
+constexpr int PN_W = 8;       // waves per workgroup
+constexpr int PN_NBG = 2;     // 16-row weight groups per wave
+constexpr int PN_RA = 4;      // LDS operand reads issued ahead of the MFMAs
 
 // LDS slice: BM rows of 128 bytes; 16-byte chunk c of row r sits at
 // position c ^ ((r >> 1) & 7).
@@ -976,7 +962,7 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
   __shared__ int s_info[3];
 
   const int G = a.E + a.n_shared;
-  if (!find_tile_n<W * 64>(a, G, BM, NB, s_info, PN_CHUNK ? NB : 0)) return;
+  if (!find_tile_n<W * 64>(a, G, BM, NB, s_info, NB)) return;
   const int g = s_info[0], r0 = s_info[1], nb = s_info[2];
   const Group gr = group_of(g, a.offsets, a.E, a.T, a.k);
   const int N = MODE == DOWN ? a.d : a.d_ff;
