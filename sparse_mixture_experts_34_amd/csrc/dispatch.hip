@@ -334,6 +334,9 @@ __global__ __launch_bounds__(64) void reassign_kernel(ReassignArgs a) {
     run += rdlane(inc, 63);
   }
   int total = run;                       // free slots left (uniform)
+  int endv[MAXC];                        // inclusive prefix (one slot/token)
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) endv[c] = pre[c] + spare[c];
   int cur_t = -1;
   int cur_e[KK];
 #pragma unroll
@@ -365,7 +368,60 @@ __global__ __launch_bounds__(64) void reassign_kernel(ReassignArgs a) {
     const long long aid = base + lane;
     uint64_t mask = __ballot(drop);
     int my_rank = -1, my_e = -1;
-    if (mask && total > 0) {
+    if constexpr (KK == 1) {
+      // One slot per token: nothing to exclude, and every pick takes one
+      // free slot, so the j-th dropped lane of this chunk draws from
+      // total - j slots.  Its slot r is known before the walk; the walk
+      // only finds the expert holding slot r among the slots still free:
+      // the number of experts whose free slots end at or before r (end =
+      // inclusive prefix of free slots, kept up to date by -1 from the
+      // chosen expert on).
+      if (mask && total > 0) {
+        const uint32_t x = drop ? philox_word0((uint32_t)aid,
+                                               (uint32_t)(aid >> 32), 0u, 0u,
+                                               a.key0, a.key1)
+                                : 0u;
+        const int j = (int)__builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(mask >> 32),
+            __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+        const int av = total - j;
+        const int rl = (drop && av > 0)
+                           ? (int)(((unsigned long long)x * (unsigned)av) >> 32)
+                           : 0;
+        // every dropped lane gets a slot while slots last (av > 0)
+        const int npick = min(__popcll(mask), total);
+        for (int i = 0; i < npick; ++i) {
+          const int b = __ffsll((unsigned long long)mask) - 1;
+          mask &= mask - 1;
+          const int rb = rdlane(rl, b);
+          int e_new = 0;
+#pragma unroll
+          for (int c = 0; c < MAXC; ++c)
+            e_new += __popcll(__ballot(endv[c] <= rb));
+          // e_new < E: slot rb < total, the last expert's end
+          int rank;
+          if constexpr (MAXC == 1) {
+            rank = rdlane(moved[0], e_new);
+          } else {
+            rank = 0;
+#pragma unroll
+            for (int c = 0; c < MAXC; ++c)
+              if (c == (e_new >> 6)) rank = rdlane(moved[c], e_new & 63);
+          }
+#pragma unroll
+          for (int c = 0; c < MAXC; ++c) {
+            const int e = lane + 64 * c;
+            endv[c] -= e >= e_new ? 1 : 0;
+            moved[c] += e == e_new ? 1 : 0;
+          }
+          if (lane == b) {
+            my_e = e_new;
+            my_rank = rank;
+          }
+        }
+        total -= npick;
+      }
+    } else if (mask && total > 0) {
       const uint32_t x = drop ? philox_word0((uint32_t)aid,
                                              (uint32_t)(aid >> 32), 0u, 0u,
                                              a.key0, a.key1)
