@@ -75,16 +75,52 @@ __device__ __forceinline__ void split3(float v, bf16& hi, bf16& mid, bf16& lo) {
   lo = (bf16)r2;
 }
 
-// --- wave reductions (fixed butterfly order: deterministic) -------------
+// --- wave reductions ------------------------------------------------------
+// DPP lane moves (gfx9 controls): partner within a quad, then within 8 and
+// 16 lanes by mirroring, then row 0 -> 1 and 2 -> 3 (row_bcast:15) and
+// row 1 -> 2, 3 (row_bcast:31); lane 63 then holds the result, which is
+// read back to every lane.  Fixed order: deterministic.  Every lane of the
+// wave must be active.
+constexpr int DPP_QUAD_1032 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_2301 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_MIRROR = 0x140;
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_BCAST15 = 0x142;
+constexpr int DPP_ROW_BCAST31 = 0x143;
+
+// lane's value moved by CTRL (rows outside ROWMASK return `old`)
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWMASK, 0xf, false);
+}
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __builtin_bit_cast(
+      float, dpp_i<CTRL, ROWMASK>(__builtin_bit_cast(int, old),
+                                  __builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ float lane63(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
-  return v;
+  v = fmaxf(v, dpp_f<DPP_QUAD_1032>(v, v));
+  v = fmaxf(v, dpp_f<DPP_QUAD_2301>(v, v));
+  v = fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v, v));
+  v = fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v, v));
+  v = fmaxf(v, dpp_f<DPP_ROW_BCAST15, 0xa>(v, v));
+  v = fmaxf(v, dpp_f<DPP_ROW_BCAST31, 0xc>(v, v));
+  return lane63(v);
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
-  return v;
+  v += dpp_f<DPP_QUAD_1032>(0.f, v);
+  v += dpp_f<DPP_QUAD_2301>(0.f, v);
+  v += dpp_f<DPP_ROW_HALF_MIRROR>(0.f, v);
+  v += dpp_f<DPP_ROW_MIRROR>(0.f, v);
+  v += dpp_f<DPP_ROW_BCAST15, 0xa>(0.f, v);
+  v += dpp_f<DPP_ROW_BCAST31, 0xc>(0.f, v);
+  return lane63(v);
 }
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }

@@ -298,19 +298,30 @@ __global__ __launch_bounds__(RS_WAVES * 64) void route_select_kernel(
           bl = l[c];
         }
       }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        float ok = __shfl_xor(bk, o, 64);
-        int oi = __shfl_xor(bi, o, 64);
-        float ol = __shfl_xor(bl, o, 64);
-        bool better = (oi != 0x7fffffff) &&
-                      (bi == 0x7fffffff || ok > bk || (ok == bk && oi < bi));
+      // wave argmax on (key desc, index asc): a total order, so the DPP
+      // steps of the wave reductions give the same winner in any order
+      auto take = [&](float ok, int oi, float ol) {
+        const bool better = (oi != 0x7fffffff) &&
+                            (bi == 0x7fffffff || ok > bk || (ok == bk && oi < bi));
         if (better) {
           bk = ok;
           bi = oi;
           bl = ol;
         }
-      }
+      };
+#define MOE_ARGMAX_STEP(CTRL, RM)                                       \
+      take(dpp_f<CTRL, RM>(bk, bk), dpp_i<CTRL, RM>(bi, bi),           \
+           dpp_f<CTRL, RM>(bl, bl))
+      MOE_ARGMAX_STEP(DPP_QUAD_1032, 0xf);
+      MOE_ARGMAX_STEP(DPP_QUAD_2301, 0xf);
+      MOE_ARGMAX_STEP(DPP_ROW_HALF_MIRROR, 0xf);
+      MOE_ARGMAX_STEP(DPP_ROW_MIRROR, 0xf);
+      MOE_ARGMAX_STEP(DPP_ROW_BCAST15, 0xa);
+      MOE_ARGMAX_STEP(DPP_ROW_BCAST31, 0xc);
+#undef MOE_ARGMAX_STEP
+      bk = lane63(bk);
+      bi = __builtin_amdgcn_readlane(bi, 63);
+      bl = lane63(bl);
       // every lane now holds the same winner
 #pragma unroll
       for (int c = 0; c < MAXC; ++c)
