@@ -188,9 +188,9 @@ def main():
             moe.moe_dispatch(p, idx, pm, counts, offs, perm, slot, nd, aux,
                              ws)
         ev[2].record()
-        moe.moe_expert_up(p, inp["x"], perm, offs, W, h)
+        moe.moe_expert_up(p, inp["x"], perm, offs, W, h, ws)
         ev[3].record()
-        moe.moe_expert_down(p, h, offs, W, y)
+        moe.moe_expert_down(p, h, offs, W, y, ws)
         ev[4].record()
         moe.moe_combine(p, inp["x"], y, slot, gate, out2)
         ev[5].record()

@@ -295,21 +295,27 @@ int32_t moe_expert_ffn(const moe_problem* p, const void* x,
  * gelu(x . W1^T + b1).
  *   h   [T*k + n_shared*T, d_ff] output, problem dtype; rows
  *       [offsets[E], T*k) are not written.
+ *   ws  optional workspace (NULL with ws_bytes 0, or at least
+ *       moe_workspace_bytes): with it the large-batch GEMM may split its
+ *       last round of tiles along K (same results up to summation order);
+ *       only its split area is used.
  */
 int32_t moe_expert_up(const moe_problem* p, const void* x,
                       const int32_t* perm, const int32_t* offsets,
-                      const moe_expert_weights* w, void* h,
-                      hipStream_t stream);
+                      const moe_expert_weights* w, void* h, void* ws,
+                      size_t ws_bytes, hipStream_t stream);
 
 /*
  * Step 4 alone, the down projection: y[r] = h[r] . W2^T (+ b2 for GELU) for
  * the same rows as moe_expert_up.
  *   h   [T*k + n_shared*T, d_ff] input as written by moe_expert_up.
  *   y   [T*k + n_shared*T, d] output, problem dtype.
+ *   ws  optional workspace, as for moe_expert_up.
  */
 int32_t moe_expert_down(const moe_problem* p, const void* h,
                         const int32_t* offsets, const moe_expert_weights* w,
-                        void* y, hipStream_t stream);
+                        void* y, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
 
 /*
  * Step 5, combine ([RC]: weighted sum plus residual; [LBS] Token Dropping:

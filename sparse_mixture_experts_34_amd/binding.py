@@ -76,8 +76,8 @@ _SIGS = {
     "moe_dispatch": (_I32, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V, _SZ,
                             _V]),
     "moe_expert_ffn": (_I32, [_P, _V, _V, _V, _W, _V, _V, _SZ, _V]),
-    "moe_expert_up": (_I32, [_P, _V, _V, _V, _W, _V, _V]),
-    "moe_expert_down": (_I32, [_P, _V, _V, _W, _V, _V]),
+    "moe_expert_up": (_I32, [_P, _V, _V, _V, _W, _V, _V, _SZ, _V]),
+    "moe_expert_down": (_I32, [_P, _V, _V, _W, _V, _V, _SZ, _V]),
     "moe_combine": (_I32, [_P, _V, _V, _V, _V, _V, _V]),
     "moe_layer_forward": (_I32, [_P, _V, _V, _V, _V, _W, _V, _V, _V, _V, _V,
                                  _V, _SZ, _V]),
@@ -237,20 +237,22 @@ def moe_expert_ffn(p, x, perm, offsets, weights, y, ws, stream=None):
                                _stream(stream)), "moe_expert_ffn")
 
 
-def moe_expert_up(p, x, perm, offsets, weights, h, stream=None):
+def moe_expert_up(p, x, perm, offsets, weights, h, ws=None, stream=None):
     w = weights if isinstance(weights, moe_expert_weights) else \
         expert_weights(weights)
     _check(_lib.moe_expert_up(ctypes.byref(p), _ptr(x), _ptr(perm),
                               _ptr(offsets), ctypes.byref(w), _ptr(h),
+                              _ptr(ws), ws.numel() if ws is not None else 0,
                               _stream(stream)), "moe_expert_up")
 
 
-def moe_expert_down(p, h, offsets, weights, y, stream=None):
+def moe_expert_down(p, h, offsets, weights, y, ws=None, stream=None):
     w = weights if isinstance(weights, moe_expert_weights) else \
         expert_weights(weights)
     _check(_lib.moe_expert_down(ctypes.byref(p), _ptr(h), _ptr(offsets),
-                                ctypes.byref(w), _ptr(y), _stream(stream)),
-           "moe_expert_down")
+                                ctypes.byref(w), _ptr(y), _ptr(ws),
+                                ws.numel() if ws is not None else 0,
+                                _stream(stream)), "moe_expert_down")
 
 
 def moe_combine(p, x_residual, y, slot_of, topk_gate, out, stream=None):

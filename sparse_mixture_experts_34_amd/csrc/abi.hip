@@ -24,7 +24,9 @@ struct Layout {
   int nrb;       // route blocks
   int nchunks;   // dispatch chunks
   size_t part, idx, gate, rpart, pmean, chunk, counts, offsets, perm, slot,
-      ndrop, aux, h, y, logits, off0, rslot, newe, total;
+      ndrop, aux, h, y, logits, off0, rslot, newe, split_part, split_cnt,
+      total;
+  int split_cpx;   // CUs per XCD the split area holds (0: none)
 };
 
 Layout make_layout(const moe_problem& p) {
@@ -61,6 +63,13 @@ Layout make_layout(const moe_problem& p) {
   L.off0 = take(re ? (size_t)(E + 1) * 4 : 0);
   L.rslot = take(re ? (size_t)T * k * 4 : 0);
   L.newe = take(re ? (size_t)T * k * 4 : 0);
+  // tiled expert GEMMs (bf16 weights): one partial tile and one counter
+  // per CU for the K-split last round
+  const int sched = ffn_schedule(p.dtype, p.T, p.top_k, p.n_experts);
+  L.split_cpx = (p.wquant == MOE_WQUANT_NONE && (sched == 1 || sched == 3))
+                    ? device_cus() / 8 : 0;
+  L.split_part = take((size_t)8 * L.split_cpx * SPLIT_TILE_FLOATS * 4);
+  L.split_cnt = take((size_t)8 * L.split_cpx * 4);
   L.total = off;
   return L;
 }
@@ -172,7 +181,19 @@ FfnArgs ffn_args(const moe_problem* p, const void* x, const int32_t* perm,
   a.sw2q = w->shared_w2_q;
   a.h = h;
   a.y = y;
+  a.split_part = nullptr;
+  a.split_cnt = nullptr;
+  a.split_cpx = 0;
   return a;
+}
+
+// The K-split area of the workspace, when the layout has one.
+void with_split(FfnArgs& a, const Layout& L, char* ws) {
+  if (L.split_cpx > 0) {
+    a.split_part = (float*)(ws + L.split_part);
+    a.split_cnt = (int32_t*)(ws + L.split_cnt);
+    a.split_cpx = L.split_cpx;
+  }
 }
 
 }  // namespace
@@ -363,32 +384,38 @@ int32_t moe_expert_ffn(const moe_problem* p, const void* x,
   if (p->T == 0) return MOE_OK;
   const Layout L = make_layout(*p);
   FfnArgs a = ffn_args(p, x, perm, offsets, w, (char*)ws + L.h, y);
+  with_split(a, L, (char*)ws);
   MOE_TRY(launch_expert_up(a, stream));
   return status_of(launch_expert_down(a, stream));
 }
 
 int32_t moe_expert_up(const moe_problem* p, const void* x,
                       const int32_t* perm, const int32_t* offsets,
-                      const moe_expert_weights* w, void* h,
-                      hipStream_t stream) {
+                      const moe_expert_weights* w, void* h, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
   int32_t st = check_problem(p);
   if (st) return st;
   if ((st = check_weights(p, w))) return st;
   if (p->T > 0 && (!x || !perm || !offsets || !h)) return MOE_EINVAL;
+  if (ws && (st = check_ws(p, ws, ws_bytes))) return st;
   if (p->T == 0) return MOE_OK;
   FfnArgs a = ffn_args(p, x, perm, offsets, w, h, nullptr);
+  if (ws) with_split(a, make_layout(*p), (char*)ws);
   return status_of(launch_expert_up(a, stream));
 }
 
 int32_t moe_expert_down(const moe_problem* p, const void* h,
                         const int32_t* offsets, const moe_expert_weights* w,
-                        void* y, hipStream_t stream) {
+                        void* y, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
   int32_t st = check_problem(p);
   if (st) return st;
   if ((st = check_weights(p, w))) return st;
   if (p->T > 0 && (!h || !offsets || !y)) return MOE_EINVAL;
+  if (ws && (st = check_ws(p, ws, ws_bytes))) return st;
   if (p->T == 0) return MOE_OK;
   FfnArgs a = ffn_args(p, nullptr, nullptr, offsets, w, (void*)h, y);
+  if (ws) with_split(a, make_layout(*p), (char*)ws);
   return status_of(launch_expert_down(a, stream));
 }
 
@@ -468,6 +495,7 @@ int32_t moe_layer_forward(const moe_problem* p, const void* x,
   }
   void* y = wsb + L.y;
   FfnArgs f = ffn_args(p, x, a.perm, a.offsets, w, wsb + L.h, y);
+  with_split(f, L, wsb);
   MOE_TRY(launch_expert_up(f, stream));
   MOE_TRY(launch_expert_down(f, stream));
   MOE_TRY(launch_combine(p->dtype, x, y, a.slot_of, gate, out, p->T,

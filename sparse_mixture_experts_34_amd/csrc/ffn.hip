@@ -589,6 +589,84 @@ __device__ bool find_tile_n(const FfnArgs& a, int G, int BM, int NB,
   return s_info[1] >= 0;
 }
 
+// Tiled schedule with the last round split along K.  Logical tiles and the
+// XCD runs are those of find_tile_n (no chunking).  An XCD's run of n tiles
+// fills R = n / cpx whole rounds of its cpx CUs; the lo = n - R*cpx tiles
+// left over would leave most CUs idle in a last round, so each is cut into
+// s = min(cpx / lo, nk) K ranges (when s >= 2 and a split workspace is
+// given) and the pieces are spread over the CUs.  s_info: group, first row,
+// n-block, first and end K slice, split item (-1: whole tile), counter
+// index, pieces s.  False for a workgroup with no work.
+template <int NTHR>
+__device__ bool find_tile_split(const FfnArgs& a, int G, int BM, int NB,
+                                int nk, int* s_info) {
+  __shared__ int s_wsum[NTHR / 64];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  if (t == 0) s_info[1] = -1;
+  int span = 0;
+  if (t < G) {
+    const int rows = t < a.E ? a.offsets[t + 1] - a.offsets[t] : a.T;
+    span = ((rows + BM - 1) / BM) * NB;
+  }
+  int incl = span;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NTHR / 64; ++w) {
+    const int ws = s_wsum[w];
+    if (w < wave) base += ws;
+    total += ws;
+  }
+  incl += base;
+  const int excl = incl - span;
+  const int x = blockIdx.x % N_XCD, slot = blockIdx.x / N_XCD;
+  const int per = (total + N_XCD - 1) / N_XCD;
+  const int first = x * per;
+  const int n = max(0, min(per, total - first));
+  const int cpx = a.split_part ? a.split_cpx : 0;
+  const int R = cpx > 0 ? n / cpx : 0;
+  const int lo = n - R * cpx;
+  const int sp = (cpx > 0 && lo > 0) ? min(cpx / lo, nk) : 1;
+  int L = total, kb = 0, ke = nk, item = -1, ctr = 0;
+  if (sp < 2) {
+    if (slot < n) L = first + slot;
+  } else if (slot < R * cpx) {
+    L = first + slot;
+  } else {
+    const int q = slot - R * cpx;
+    if (q < lo * sp) {
+      const int tl = q / sp, c = q - tl * sp;
+      L = first + R * cpx + tl;
+      kb = c * nk / sp;
+      ke = (c + 1) * nk / sp;
+      item = x * cpx + q;
+      ctr = x * cpx + tl;
+    }
+  }
+  if (t < G && L >= excl && L < incl) {
+    const int nt = span / NB;
+    const int r = L - excl;
+    const int nb = r / nt;
+    s_info[0] = t;
+    s_info[1] = (r - nb * nt) * BM;
+    s_info[2] = nb;
+    s_info[3] = kb;
+    s_info[4] = ke;
+    s_info[5] = item;
+    s_info[6] = ctr;
+    s_info[7] = sp;
+  }
+  __syncthreads();
+  return s_info[1] >= 0;
+}
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
@@ -671,7 +749,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
   __shared__ __attribute__((aligned(16))) bf16 B3[NS > 3 ? SB : 8];
   __shared__ __attribute__((aligned(16))) bf16 B4[NS > 4 ? SB : 8];
   __shared__ __attribute__((aligned(16))) bf16 B5[NS > 5 ? SB : 8];
-  __shared__ int s_info[3];
+  __shared__ int s_info[9];
   // stage s's arrays (s is a constant after unrolling, so each access names
   // one distinct object)
   auto As = [&](int st) -> bf16* {
@@ -696,8 +774,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
   };
 
   const int G = a.E + a.n_shared;
-  if (!find_tile_n<TL_THREADS>(a, G, BM, NB, s_info)) return;
+  const int Kd = MODE == DOWN ? a.d_ff : a.d;
+  if (!find_tile_split<TL_THREADS>(a, G, BM, NB, Kd / BK, s_info)) return;
   const int g = s_info[0], r0 = s_info[1], nb = s_info[2];
+  const int kb = s_info[3], ke = s_info[4], item = s_info[5];
   const Group gr = group_of(g, a.offsets, a.E, a.T, a.k);
   const int N = MODE == DOWN ? a.d : a.d_ff;
   const int K = MODE == DOWN ? a.d_ff : a.d;
@@ -746,7 +826,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
     bo[i] = (uint32_t)wrow * (uint32_t)K + ((lp ^ Geo::key(row)) << 3);
   }
   auto issue = [&](int kt, bf16* Ad, bf16* Bd) {
-    const int k0 = kt * BK;
+    const int k0 = (kb + kt) * BK;
 #pragma unroll
     for (int i = 0; i < IA; ++i)
       dma16(abase_g + ao[i] + k0, Ad + (wave * IA + i) * Geo::RPI * BK);
@@ -763,7 +843,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int nk = K / BK;
+  const int nk = ke - kb;   // K slices of this piece
   // MFMA operand rows: A rows wm*WM + 32i + l31, B rows wn*64 + 32j + l31;
   // their swizzle key is key(l31) for every tile
   const int akey = Geo::key(l31);
@@ -832,6 +912,67 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
         else slice_barrier<0>();
       }
     }
+  }
+
+  // ---- a K piece of a split tile: park the partial sums; the last piece
+  // to arrive adds them all in piece order and stores the tile ----
+  if (item >= 0) {
+    static_assert(MT * NT * 16 * TL_THREADS <= SPLIT_TILE_FLOATS, "split tile");
+    const int ctr = s_info[6], sp = s_info[7];
+    // 16-byte partials: float4 (i, j, v4) of thread tid at
+    // ((i*NT + j)*4 + v4)*TL_THREADS + tid
+    f32x4* pp = reinterpret_cast<f32x4*>(a.split_part + (size_t)item * SPLIT_TILE_FLOATS);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4)
+          pp[((i * NT + j) * 4 + v4) * TL_THREADS + tid] =
+              f32x4{acc[i][j][4 * v4], acc[i][j][4 * v4 + 1],
+                    acc[i][j][4 * v4 + 2], acc[i][j][4 * v4 + 3]};
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_info[8] = atomicAdd(a.split_cnt + ctr, 1);
+    __syncthreads();
+    if (s_info[8] != sp - 1) return;   // uniform: another piece finishes it
+    __threadfence();
+    // pieces of a tile are consecutive items (tile tl of the XCD: items
+    // x*cpx + tl*sp + 0 .. sp-1); this one is piece pc.  Sum in piece
+    // order, one 32x32 accumulator tile at a time (its four loads per
+    // piece issued together).
+    const int pc = (item % a.split_cpx) % sp;
+    const f32x4* p0 = reinterpret_cast<const f32x4*>(
+        a.split_part + (size_t)(item - pc) * SPLIT_TILE_FLOATS);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        f32x4 sum[4];
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) sum[v4] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < sp; ++q) {
+          f32x4 pv[4];
+          if (q == pc) {
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4)
+              pv[v4] = f32x4{acc[i][j][4 * v4], acc[i][j][4 * v4 + 1],
+                             acc[i][j][4 * v4 + 2], acc[i][j][4 * v4 + 3]};
+          } else {
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4)
+              pv[v4] = p0[(size_t)q * (SPLIT_TILE_FLOATS / 4) +
+                          ((i * NT + j) * 4 + v4) * TL_THREADS + tid];
+          }
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) sum[v4] += pv[v4];
+        }
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * v4 + e] = sum[v4][e];
+      }
+    if (tid == 0) a.split_cnt[ctr] = 0;   // ready for the next launch
   }
 
   // ---- epilogue: activation, stage the bf16 tile in LDS, store rows ----
@@ -1240,11 +1381,18 @@ hipError_t launch_mode(const FfnArgs& a, hipStream_t s, int sched, int rt,
       else ffn_stream_kernel<MODE, 4, 1><<<grid, ST_WAVES * 64, 0, s>>>(a);
     }
   } else if (sched == 1 || sched == 3) {
-    // sched 1: BM = 256, sched 3: BM = 128; max_tiles counts m-tiles
+    // sched 1: BM = 256, sched 3: BM = 128; max_tiles counts m-tiles.  With
+    // a split workspace each XCD may need up to split_cpx more workgroups
+    // for the pieces of its last round; their counters start at zero.
     const int ncols = MODE == UP_SWIGLU ? TL_BN / 2 : TL_BN;
     const int NB = (N + ncols - 1) / ncols;
     long long tiles = (long long)max_tiles * NB;
     tiles = (tiles + N_XCD - 1) / N_XCD * N_XCD;
+    if (a.split_part) {
+      tiles += (long long)N_XCD * a.split_cpx;
+      const hipError_t e = launch_fill_zero32(a.split_cnt, (long long)N_XCD * a.split_cpx, s);
+      if (e != hipSuccess) return e;
+    }
     if (sched == 1)
       ffn_tiled_kernel<MODE, 256, 64, 2, TL_WAVES>
           <<<(unsigned)tiles, TL_WAVES * 64, 0, s>>>(a, NB);
@@ -1265,6 +1413,15 @@ hipError_t launch_mode(const FfnArgs& a, hipStream_t s, int sched, int rt,
 }
 
 }  // namespace
+
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    return 256;
+  return n;
+}
 
 // Schedule choice from shapes only (no device readback):
 //   f32 -> float32 kernel; bf16 with at most 64 assignments per expert on

@@ -111,7 +111,16 @@ struct FfnArgs {
   // pairs per group of Q4_GROUP weights
   int wquant;
   const float *w1q, *w_upq, *w2q, *sw1q, *sw_upq, *sw2q;
+  // tiled schedule, last round split along K (optional workspace): one
+  // partial tile of SPLIT_TILE_FLOATS floats and one counter per CU for
+  // split_cpx CUs per XCD; split_part == nullptr: no split
+  float* split_part;
+  int32_t* split_cnt;
+  int split_cpx;
 };
+constexpr int SPLIT_TILE_FLOATS = 256 * 256;
+// CUs of the current device (persistent and split grids)
+int device_cus();
 hipError_t launch_expert_up(const FfnArgs& a, hipStream_t s);
 hipError_t launch_expert_down(const FfnArgs& a, hipStream_t s);
 

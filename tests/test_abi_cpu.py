@@ -199,7 +199,7 @@ def test_int4_weights_need_their_scales():
         assert lib.moe_expert_ffn(ctypes.byref(p), f, f, f, ctypes.byref(w),
                                   f, f, big, None) == moe.MOE_EINVAL
         assert lib.moe_expert_up(ctypes.byref(p), f, f, f, ctypes.byref(w),
-                                 f, None) == moe.MOE_EINVAL
+                                 f, None, 0, None) == moe.MOE_EINVAL
 
 
 def test_quantize_int4_validation():

@@ -6,15 +6,19 @@ rows (one or two panels or 256-row tiles), with and without a shared expert,
 odd numbers of 64-wide K steps and partial weight blocks.  The schedule is
 chosen from T, k and E only (stream up to 64 assignments per expert on
 average, panel up to 256, tiled beyond), so each case fixes T*k/E and then
-places the counts freely (rows past offsets[E] are unused).  Outputs are
-compared by max |gpu - oracle| / max |oracle| over the computed rows (2e-2,
-bf16)."""
+places the counts freely (rows past offsets[E] are unused).  Each case runs
+through moe_expert_ffn (with workspace: the tiled schedules may split their
+last round along K) and through moe_expert_up + moe_expert_down (no
+workspace: never split).  Outputs are compared by max |gpu - oracle| /
+max |oracle| over the computed rows (2e-2, bf16)."""
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from gpu_helpers import TOL, gpu_expert_ffn, host, log
+import sparse_mixture_experts_34_amd as moe
 from sparse_mixture_experts_34_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -64,6 +68,39 @@ def _grouping(counts, T, k, seed):
     return np.asarray(perm, np.int32), offsets
 
 
+def _gpu_up_down(inp, perm, offsets, wl):
+    """moe_expert_up then moe_expert_down (no workspace)."""
+    p = moe.problem_for(wl)
+    dev = inp["x"].device
+    rows = wl.T * wl.top_k + wl.n_shared * wl.T
+    h = torch.full((rows, wl.d_ff), float("nan"), dtype=wl.torch_dtype,
+                   device=dev)
+    y = torch.full((rows, wl.d_model), float("nan"), dtype=wl.torch_dtype,
+                   device=dev)
+    pt = torch.full((max(wl.T * wl.top_k, 1),), -1, dtype=torch.int32,
+                    device=dev)
+    if perm.size:
+        pt[:perm.size] = torch.as_tensor(perm, device=dev)
+    ot = torch.as_tensor(offsets, device=dev)
+    moe.moe_expert_up(p, inp["x"], pt, ot, inp, h)
+    moe.moe_expert_down(p, h, ot, inp, y)
+    torch.cuda.synchronize()
+    return y
+
+
+def _errors(y, ref, offsets, counts, rows):
+    assert np.isfinite(y[rows]).all()
+    err = np.abs(y[rows] - ref[rows]).max() / np.abs(ref[rows]).max()
+    # per expert too, so a wrong small group cannot hide behind a big one
+    worst = 0.0
+    for e in range(len(counts)):
+        r = np.arange(offsets[e], offsets[e + 1])
+        if r.size:
+            worst = max(worst, np.abs(y[r] - ref[r]).max()
+                        / np.abs(ref[r]).max())
+    return err, worst
+
+
 @pytest.mark.parametrize("wl,counts", CASES, ids=[c[0].name for c in CASES])
 def test_expert_ffn_boundaries(wl, counts):
     log(f"ffn boundaries {wl.name}: counts {counts}")
@@ -77,14 +114,9 @@ def test_expert_ffn_boundaries(wl, counts):
     rows = np.arange(offsets[-1])
     if wl.n_shared:
         rows = np.concatenate([rows, T * k + np.arange(T)])
-    assert np.isfinite(y[rows]).all()
-    err = np.abs(y[rows] - ref[rows]).max() / np.abs(ref[rows]).max()
-    # per expert too, so a wrong small group cannot hide behind a big one
-    worst = 0.0
-    for e in range(len(counts)):
-        r = np.arange(offsets[e], offsets[e + 1])
-        if r.size:
-            worst = max(worst, np.abs(y[r] - ref[r]).max()
-                        / np.abs(ref[r]).max())
-    log(f"  rel err {err:.2e}, worst expert {worst:.2e}")
-    assert err <= TOL["bf16"] and worst <= TOL["bf16"]
+    err, worst = _errors(y, ref, offsets, counts, rows)
+    y2 = host(_gpu_up_down(inp, perm, offsets, wl)).astype(np.float64)
+    err2, worst2 = _errors(y2, ref, offsets, counts, rows)
+    log(f"  moe_expert_ffn rel err {err:.2e} (worst expert {worst:.2e}); "
+        f"up+down {err2:.2e} ({worst2:.2e})")
+    assert max(err, worst, err2, worst2) <= TOL["bf16"]
