@@ -18,17 +18,24 @@
 //   up    H[r, n]  = act(A[r,:] . W1[g, n, :]) (SwiGLU: silu(gate) * up)
 //   down  Y[r, n]  = H[r,:] . W2[g, n, :] (+ b2)
 //
-// Two bf16 schedules, picked on the host from the shapes only:
-//   stream  few rows per expert (decode): a workgroup owns 32 output
-//           columns, its waves split K, and each streams its weight rows
-//           once from HBM straight into MFMA B registers (16x16x32) with a
-//           3-deep register prefetch ring; the handful of token rows ride
-//           along as the A operand; partial sums meet in LDS.
-//   tiled   many rows per expert (prefill): 256- or 128-row by 256-column
-//           workgroup tiles, A and B loaded straight into XOR-swizzled LDS
-//           stages, 32x32x16 MFMAs, the activation fused into the epilogue,
-//           and the output tile staged through LDS for 16-byte row stores.
-// float32 problems use a plain float32 kernel (same grouping).
+// Three bf16 schedules, picked on the host from the shapes only (average
+// assignments per expert T*k/E):
+//   stream  up to 64 (decode): a workgroup owns 32 output columns, its
+//           waves split K, and each streams its weight rows once from HBM
+//           straight into MFMA B registers (16x16x32) with a 3-deep register
+//           prefetch ring; the handful of token rows ride along as the A
+//           operand; partial sums meet in LDS.
+//   panel   up to 256 (many experts, moderate batch): a workgroup owns up to
+//           256 rows of one expert and 256 weight rows over all of K; the
+//           weights stream once from HBM into MFMA B registers, the token
+//           rows are shared through LDS.
+//   tiled   more (prefill): 256- or 128-row by 256-column workgroup tiles,
+//           A and B loaded straight into XOR-swizzled LDS stages, 32x32x16
+//           MFMAs, the activation fused into the epilogue, the output tile
+//           staged through LDS for 16-byte row stores, and each XCD's last
+//           round of tiles split along K over its CUs.
+// 4-bit weights use the stream schedule at every batch size; float32
+// problems use a plain float32 kernel (same grouping).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -530,28 +537,23 @@ constexpr int N_XCD = 8;
 // bytes in flight per CU to cover HBM latency.
 constexpr int TL_WAVES = 8;
 
-// Workgroup -> (group, first row, n-block); whole workgroup of NTHR (>=
-// number of groups) threads.  Thread g takes group g's tile count
-// ceil(rows/BM) * NB; a workgroup prefix scan (wave shuffles, then wave
-// totals through LDS) gives each group's first logical tile and the total.
-// Logical tiles run group by group, n-block by n-block, m-tiles innermost.
-// Workgroups reach the 8 XCDs round-robin by id, so id p is mapped to the
-// logical tile (p % 8) * ceil(total / 8) + p / 8: each XCD gets a contiguous
-// run of the real tiles (the grid is an upper bound, a multiple of 8).
-// False for a workgroup with no tile.
+// Logical tiles run group by group, n-block by n-block, row tiles (m)
+// innermost; group g has ceil(rows/BM) * NB of them.  Whole workgroup of
+// NTHR (>= number of groups) threads: thread g < G gets its group's first
+// logical tile (excl) and end (incl) from a prefix scan (wave shuffles, then
+// wave totals through LDS); every thread gets the total.
 template <int NTHR>
-__device__ bool find_tile_n(const FfnArgs& a, int G, int BM, int NB,
-                            int* s_info, int chunk = 0) {
+__device__ void tile_scan(const FfnArgs& a, int G, int BM, int NB, int& excl,
+                          int& incl, int& total) {
   __shared__ int s_wsum[NTHR / 64];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  if (t == 0) s_info[1] = -1;
   int span = 0;
   if (t < G) {
     const int rows = t < a.E ? a.offsets[t + 1] - a.offsets[t] : a.T;
     span = ((rows + BM - 1) / BM) * NB;
   }
-  int incl = span;
+  incl = span;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int v = __shfl_up(incl, o, 64);
@@ -559,7 +561,8 @@ __device__ bool find_tile_n(const FfnArgs& a, int G, int BM, int NB,
   }
   if (lane == 63) s_wsum[wave] = incl;
   __syncthreads();
-  int base = 0, total = 0;
+  int base = 0;
+  total = 0;
 #pragma unroll
   for (int w = 0; w < NTHR / 64; ++w) {
     const int ws = s_wsum[w];
@@ -567,18 +570,16 @@ __device__ bool find_tile_n(const FfnArgs& a, int G, int BM, int NB,
     total += ws;
   }
   incl += base;
-  const int excl = incl - span;
-  const int slot = blockIdx.x / N_XCD;
-  int L;
-  if (chunk > 0) {
-    // runs of `chunk` logical tiles dealt to the XCDs in turn
-    L = ((slot / chunk) * N_XCD + blockIdx.x % N_XCD) * chunk + slot % chunk;
-  } else {
-    const int per_xcd = (total + N_XCD - 1) / N_XCD;
-    L = slot < per_xcd ? (blockIdx.x % N_XCD) * per_xcd + slot : total;
-  }
+  excl = incl - span;
+}
+
+// (group, first row, n-block) of logical tile L into s_info, by the thread
+// whose group holds it; false for L past the last tile.  Whole workgroup.
+__device__ __forceinline__ bool publish_tile(int G, int BM, int NB, int L,
+                                             int excl, int incl, int* s_info) {
+  const int t = threadIdx.x;
   if (t < G && L >= excl && L < incl) {
-    const int nt = span / NB;
+    const int nt = (incl - excl) / NB;
     const int r = L - excl;
     const int nb = r / nt;
     s_info[0] = t;
@@ -589,43 +590,37 @@ __device__ bool find_tile_n(const FfnArgs& a, int G, int BM, int NB,
   return s_info[1] >= 0;
 }
 
-// Tiled schedule with the last round split along K.  Logical tiles and the
-// XCD runs are those of find_tile_n (no chunking).  An XCD's run of n tiles
-// fills R = n / cpx whole rounds of its cpx CUs; the lo = n - R*cpx tiles
-// left over would leave most CUs idle in a last round, so each is cut into
-// s = min(cpx / lo, nk) K ranges (when s >= 2 and a split workspace is
-// given) and the pieces are spread over the CUs.  s_info: group, first row,
-// n-block, first and end K slice, split item (-1: whole tile), counter
-// index, pieces s.  False for a workgroup with no work.
+// Panel schedule: workgroups reach the 8 XCDs round-robin by id (slot =
+// id / 8 on XCD id % 8); runs of NB logical tiles (one panel's n-blocks,
+// which share its token rows) are dealt to the XCDs in turn, so XCD x's
+// slot j takes tile ((j / NB) * 8 + x) * NB + j % NB.  False for a
+// workgroup with no tile (the grid is an upper bound).
+template <int NTHR>
+__device__ bool find_panel_tile(const FfnArgs& a, int G, int BM, int NB,
+                                int* s_info) {
+  if (threadIdx.x == 0) s_info[1] = -1;
+  int excl, incl, total;
+  tile_scan<NTHR>(a, G, BM, NB, excl, incl, total);
+  const int slot = blockIdx.x / N_XCD;
+  const int L = ((slot / NB) * N_XCD + blockIdx.x % N_XCD) * NB + slot % NB;
+  return publish_tile(G, BM, NB, L, excl, incl, s_info);
+}
+
+// Tiled schedule: XCD x takes the contiguous run of ceil(total / 8)
+// logical tiles from x * ceil(total / 8), so its L2 serves the weight and
+// token slices neighbouring tiles share.  The run of n tiles fills
+// R = n / cpx whole rounds of the XCD's cpx CUs; the lo = n - R*cpx tiles
+// left over would leave most CUs idle in a last round, so (given a split
+// workspace, and when s = min(cpx / lo, nk) >= 2) each is cut into s K
+// ranges spread over the CUs.  s_info: group, first row, n-block, first and
+// end K slice, split item (-1: whole tile), counter index, pieces s.  False
+// for a workgroup with no work.
 template <int NTHR>
 __device__ bool find_tile_split(const FfnArgs& a, int G, int BM, int NB,
                                 int nk, int* s_info) {
-  __shared__ int s_wsum[NTHR / 64];
-  const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
-  if (t == 0) s_info[1] = -1;
-  int span = 0;
-  if (t < G) {
-    const int rows = t < a.E ? a.offsets[t + 1] - a.offsets[t] : a.T;
-    span = ((rows + BM - 1) / BM) * NB;
-  }
-  int incl = span;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += v;
-  }
-  if (lane == 63) s_wsum[wave] = incl;
-  __syncthreads();
-  int base = 0, total = 0;
-#pragma unroll
-  for (int w = 0; w < NTHR / 64; ++w) {
-    const int ws = s_wsum[w];
-    if (w < wave) base += ws;
-    total += ws;
-  }
-  incl += base;
-  const int excl = incl - span;
+  if (threadIdx.x == 0) s_info[1] = -1;
+  int excl, incl, total;
+  tile_scan<NTHR>(a, G, BM, NB, excl, incl, total);
   const int x = blockIdx.x % N_XCD, slot = blockIdx.x / N_XCD;
   const int per = (total + N_XCD - 1) / N_XCD;
   const int first = x * per;
@@ -650,21 +645,14 @@ __device__ bool find_tile_split(const FfnArgs& a, int G, int BM, int NB,
       ctr = x * cpx + tl;
     }
   }
-  if (t < G && L >= excl && L < incl) {
-    const int nt = span / NB;
-    const int r = L - excl;
-    const int nb = r / nt;
-    s_info[0] = t;
-    s_info[1] = (r - nb * nt) * BM;
-    s_info[2] = nb;
+  if (threadIdx.x == 0) {
     s_info[3] = kb;
     s_info[4] = ke;
     s_info[5] = item;
     s_info[6] = ctr;
     s_info[7] = sp;
   }
-  __syncthreads();
-  return s_info[1] >= 0;
+  return publish_tile(G, BM, NB, L, excl, incl, s_info);
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -1103,7 +1091,7 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
   __shared__ int s_info[3];
 
   const int G = a.E + a.n_shared;
-  if (!find_tile_n<W * 64>(a, G, BM, NB, s_info, NB)) return;
+  if (!find_panel_tile<W * 64>(a, G, BM, NB, s_info)) return;
   const int g = s_info[0], r0 = s_info[1], nb = s_info[2];
   const Group gr = group_of(g, a.offsets, a.E, a.T, a.k);
   const int N = MODE == DOWN ? a.d : a.d_ff;
