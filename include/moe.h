@@ -194,7 +194,11 @@ int32_t moe_capacity(int32_t T, int32_t top_k, int32_t n_experts,
 
 /*
  * Workspace bytes needed by every entry point below for problem `p`
- * (one size serves all of them).  Host-only; writes *bytes.
+ * (one size serves all of them).  Host-only; writes *bytes.  For batches
+ * large enough for the tiled expert GEMMs the size includes one float32
+ * partial tile (256 KiB) and one counter per compute unit of the current
+ * device (the K split of the last round of tiles), so query it with the
+ * device that will run the calls current.
  * Returns MOE_EINVAL / MOE_ENOTSUP for a problem the library rejects.
  */
 int32_t moe_workspace_bytes(const moe_problem* p, size_t* bytes);
