@@ -838,44 +838,74 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
   const int arow0 = (wm * WM + l31) * BK;
   const int brow0 = (wn * WN + l31) * BK;
   // Operands of substep ss+1 are read from LDS before the MFMAs of substep
-  // ss are issued, so LDS latency overlaps matrix work.
-  auto compute = [&](const bf16* Ab, const bf16* Bb) {
-    V16 av[2][MT], bv[2][NT];
-    auto fetch = [&](int ss, int set) {
-      const int pos = ((ss * 2 + q) ^ akey) << 3;
-      const bf16* ap = Ab + arow0 + pos;
-      const bf16* bp = Bb + brow0 + pos;
+  // ss are issued, so LDS latency overlaps matrix work.  Two register sets
+  // of operands, alternating by substep.
+  V16 av[2][MT], bv[2][NT];
+  auto fetch = [&](const bf16* Ab, const bf16* Bb, int ss, int set) {
+    const int pos = ((ss * 2 + q) ^ akey) << 3;
+    const bf16* ap = Ab + arow0 + pos;
+    const bf16* bp = Bb + brow0 + pos;
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
-        av[set][i].u = *reinterpret_cast<const u32x4*>(ap + i * 32 * BK);
+    for (int i = 0; i < MT; ++i)
+      av[set][i].u = *reinterpret_cast<const u32x4*>(ap + i * 32 * BK);
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      bv[set][j].u = *reinterpret_cast<const u32x4*>(bp + j * 32 * BK);
+  };
+  auto mfmas = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int j = 0; j < NT; ++j)
-        bv[set][j].u = *reinterpret_cast<const u32x4*>(bp + j * 32 * BK);
-    };
-    fetch(0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[set][i].h, bv[set][j].h, acc[i][j], 0, 0, 0);
+  };
+  // schedule: the next substep's LDS reads interleaved one by one with this
+  // substep's MFMAs
+  auto interleave = [&]() {
+#pragma unroll
+    for (int r = 0; r < MT + NT; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one DS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, MT * NT - (MT + NT), 0);
+  };
+  auto compute = [&](const bf16* Ab, const bf16* Bb) {
+    fetch(Ab, Bb, 0, 0);
 #pragma unroll
     for (int ss = 0; ss < Geo::SUB; ++ss) {
       const int cur = ss & 1;
-      if (ss + 1 < Geo::SUB) fetch(ss + 1, cur ^ 1);
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cur][i].h, bv[cur][j].h, acc[i][j], 0, 0, 0);
-      // schedule: the next substep's LDS reads interleaved one by one with
-      // this substep's MFMAs
-      if (ss + 1 < Geo::SUB) {
-#pragma unroll
-        for (int r = 0; r < MT + NT; ++r) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one DS read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, MT * NT - (MT + NT), 0);
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, MT * NT, 0);
-      }
+      if (ss + 1 < Geo::SUB) fetch(Ab, Bb, ss + 1, cur ^ 1);
+      mfmas(cur);
+      if (ss + 1 < Geo::SUB) interleave();
+      else __builtin_amdgcn_sched_group_barrier(0x008, MT * NT, 0);
     }
   };
+  // One slice in flight (two stages): the MFMAs of a slice's last substep
+  // are issued after the slice barrier, behind the next slice's first LDS
+  // reads, so the matrix cores work while those reads are in flight.  Their
+  // operands are in registers already (the barrier waited for the reads),
+  // so the stage they came from may be refilled meanwhile.  Before the first
+  // slice the deferred set holds zeros: its MFMAs add exact zeros.
+  constexpr int LS = (Geo::SUB - 1) & 1;   // register set of the last substep
+  auto compute_deferred = [&](const bf16* Ab, const bf16* Bb) {
+    fetch(Ab, Bb, 0, 0);
+    mfmas(LS);   // the previous slice's last substep
+    __builtin_amdgcn_sched_group_barrier(0x100, MT + NT, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, MT * NT, 0);
+#pragma unroll
+    for (int ss = 0; ss + 1 < Geo::SUB; ++ss) {
+      const int cur = ss & 1;
+      fetch(Ab, Bb, ss + 1, cur ^ 1);
+      mfmas(cur);
+      interleave();
+    }
+  };
+  if constexpr (D == 1) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) av[LS][i].u = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < NT; ++j) bv[LS][j].u = u32x4{0u, 0u, 0u, 0u};
+  }
 
   // prologue: slices 0..D-1 in flight, then wait for slice 0
 #pragma unroll
@@ -887,20 +917,31 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
   // reads stage k % NS; before it, slice k + D is issued into stage
   // (k + D) % NS, last read by slice k - 1 (one barrier ago).  After slice k
   // the wave waits until slice k + 1 has landed: all later slices may stay
-  // in flight.
+  // in flight.  With one slice in flight (two stages) the slice body has no
+  // branch: the last slice issues itself again into the idle stage (one
+  // redundant slice per tile), which lets the compiler schedule the loads,
+  // the first LDS reads and the MFMAs of a slice as one block.
   for (int kt = 0; kt < nk; kt += NS) {
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
       const int k = kt + u;
       if (k < nk) {
-        const bool more = k + D < nk;
-        if (more) issue(k + D, As((u + D) % NS), Bs((u + D) % NS));
-        compute(As(u), Bs(u));
-        if (more) slice_barrier<(D - 1) * PER>();
-        else slice_barrier<0>();
+        if constexpr (D == 1) {
+          issue(min(k + 1, nk - 1), As((u + 1) % NS), Bs((u + 1) % NS));
+          compute_deferred(As(u), Bs(u));
+          slice_barrier<0>();
+        } else {
+          const bool more = k + D < nk;
+          if (more) issue(k + D, As((u + D) % NS), Bs((u + D) % NS));
+          compute(As(u), Bs(u));
+          if (more) slice_barrier<(D - 1) * PER>();
+          else slice_barrier<0>();
+        }
       }
     }
   }
+
+  if constexpr (D == 1) mfmas(LS);   // the last slice's last substep
 
   // ---- a K piece of a split tile: park the partial sums; the last piece
   // to arrive adds them all in piece order and stores the tile ----
