@@ -66,7 +66,7 @@ Layout make_layout(const moe_problem& p) {
   // tiled expert GEMMs (bf16 weights): one partial tile and one counter
   // per CU for the K-split last round
   const int sched = ffn_schedule(p.dtype, p.T, p.top_k, p.n_experts);
-  L.split_cpx = (p.wquant == MOE_WQUANT_NONE && (sched == 1 || sched == 3))
+  L.split_cpx = (p.wquant == MOE_WQUANT_NONE && sched == 1)
                     ? device_cus() / 8 : 0;
   L.split_part = take((size_t)8 * L.split_cpx * SPLIT_TILE_FLOATS * 4);
   L.split_cnt = take((size_t)8 * L.split_cpx * 4);

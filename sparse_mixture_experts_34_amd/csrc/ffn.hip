@@ -29,7 +29,7 @@
 //           256 rows of one expert and 256 weight rows over all of K; the
 //           weights stream once from HBM into MFMA B registers, the token
 //           rows are shared through LDS.
-//   tiled   more (prefill): 256- or 128-row by 256-column workgroup tiles,
+//   tiled   more (prefill): 256-row by 256-column workgroup tiles,
 //           A and B loaded straight into XOR-swizzled LDS stages, 32x32x16
 //           MFMAs, the activation fused into the epilogue, the output tile
 //           staged through LDS for 16-byte row stores, and each XCD's last
@@ -509,9 +509,9 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_q4_kernel(FfnArgs a)
 // ===========================================================================
 // tiled schedule (bf16)
 // ===========================================================================
-// Workgroup tile BM x 256 (BM = 128 or 256) over BK = 64 slices of K, eight
-// waves (two per SIMD) in a 2 x 4 grid, each wave (BM/2) x 64 of 32x32x16
-// MFMA tiles.
+// Workgroup tile BM x 256 (BM = 256) over BK = 64 slices of K, eight waves
+// (two per SIMD) in a 2 x 4 grid, each wave (BM/2) x 64 of 32x32x16 MFMA
+// tiles.
 //
 // A and B slices go from global memory straight into LDS (direct-to-LDS
 // loads, 16 bytes per lane, one instruction = 8 rows x 128 bytes, so every
@@ -531,10 +531,11 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_q4_kernel(FfnArgs a)
 // contiguous run of logical tiles and its L2 serves the shared slices.
 constexpr int TL_BN = 256;   // B rows per tile (SwiGLU: 128 gate + 128 up)
 constexpr int N_XCD = 8;
-// Tile configurations: many rows per expert (compute-bound) use 256-row
-// tiles with two 64-wide K stages; fewer rows (weight-streaming) use 128-row
-// tiles with six 32-wide K stages, five in flight, to keep enough weight
-// bytes in flight per CU to cover HBM latency.
+// One configuration is launched: 256-row tiles, two 64-wide K stages (one
+// slice in flight).  The template also takes narrower slices and deeper
+// rings (NS stages, NS - 1 slices in flight); 128-row tiles with six 32-wide
+// stages and 256-row tiles with four 32-wide stages both measured slower at
+// every batch size past the panel range.
 constexpr int TL_WAVES = 8;
 
 // Logical tiles run group by group, n-block by n-block, row tiles (m)
@@ -869,23 +870,12 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
     }
     __builtin_amdgcn_sched_group_barrier(0x008, MT * NT - (MT + NT), 0);
   };
-  auto compute = [&](const bf16* Ab, const bf16* Bb) {
-    fetch(Ab, Bb, 0, 0);
-#pragma unroll
-    for (int ss = 0; ss < Geo::SUB; ++ss) {
-      const int cur = ss & 1;
-      if (ss + 1 < Geo::SUB) fetch(Ab, Bb, ss + 1, cur ^ 1);
-      mfmas(cur);
-      if (ss + 1 < Geo::SUB) interleave();
-      else __builtin_amdgcn_sched_group_barrier(0x008, MT * NT, 0);
-    }
-  };
-  // One slice in flight (two stages): the MFMAs of a slice's last substep
-  // are issued after the slice barrier, behind the next slice's first LDS
-  // reads, so the matrix cores work while those reads are in flight.  Their
-  // operands are in registers already (the barrier waited for the reads),
-  // so the stage they came from may be refilled meanwhile.  Before the first
-  // slice the deferred set holds zeros: its MFMAs add exact zeros.
+  // The MFMAs of a slice's last substep are issued after the slice barrier,
+  // behind the next slice's first LDS reads, so the matrix cores work while
+  // those reads are in flight.  Their operands are in registers already (the
+  // barrier waited for the reads), so the stage they came from may be
+  // refilled meanwhile.  Before the first slice the deferred set holds
+  // zeros: its MFMAs add exact zeros.
   constexpr int LS = (Geo::SUB - 1) & 1;   // register set of the last substep
   auto compute_deferred = [&](const bf16* Ab, const bf16* Bb) {
     fetch(Ab, Bb, 0, 0);
@@ -900,48 +890,39 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
       interleave();
     }
   };
-  if constexpr (D == 1) {
 #pragma unroll
-    for (int i = 0; i < MT; ++i) av[LS][i].u = u32x4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < MT; ++i) av[LS][i].u = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int j = 0; j < NT; ++j) bv[LS][j].u = u32x4{0u, 0u, 0u, 0u};
-  }
+  for (int j = 0; j < NT; ++j) bv[LS][j].u = u32x4{0u, 0u, 0u, 0u};
 
-  // prologue: slices 0..D-1 in flight, then wait for slice 0
+  // Prologue: slices 0..D-1 in flight (clamped to the last slice when the
+  // piece is shorter), then wait for slice 0.
 #pragma unroll
-  for (int s = 0; s < D; ++s)
-    if (s < nk) issue(s, As(s), Bs(s));
-  if (nk >= D) slice_barrier<(D - 1) * PER>();   // later prologue slices fly
-  else slice_barrier<0>();
+  for (int s = 0; s < D; ++s) issue(min(s, nk - 1), As(s), Bs(s));
+  slice_barrier<(D - 1) * PER>();
   // Main loop, NS slices per trip with constant stage indices.  Slice k
   // reads stage k % NS; before it, slice k + D is issued into stage
   // (k + D) % NS, last read by slice k - 1 (one barrier ago).  After slice k
   // the wave waits until slice k + 1 has landed: all later slices may stay
-  // in flight.  With one slice in flight (two stages) the slice body has no
-  // branch: the last slice issues itself again into the idle stage (one
-  // redundant slice per tile), which lets the compiler schedule the loads,
-  // the first LDS reads and the MFMAs of a slice as one block.
+  // in flight.  The slice body has no branch: near the end the last slice
+  // is issued again into the stage just freed (D redundant slices per tile,
+  // never read), so every slice issues PER loads and the wait count is
+  // constant; the loads, the first LDS reads and the MFMAs of a slice
+  // schedule as one block.
   for (int kt = 0; kt < nk; kt += NS) {
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
       const int k = kt + u;
       if (k < nk) {
-        if constexpr (D == 1) {
-          issue(min(k + 1, nk - 1), As((u + 1) % NS), Bs((u + 1) % NS));
-          compute_deferred(As(u), Bs(u));
-          slice_barrier<0>();
-        } else {
-          const bool more = k + D < nk;
-          if (more) issue(k + D, As((u + D) % NS), Bs((u + D) % NS));
-          compute(As(u), Bs(u));
-          if (more) slice_barrier<(D - 1) * PER>();
-          else slice_barrier<0>();
-        }
+        issue(min(k + D, nk - 1), As((u + D) % NS), Bs((u + D) % NS));
+        compute_deferred(As(u), Bs(u));
+        slice_barrier<(D - 1) * PER>();
       }
     }
   }
-
-  if constexpr (D == 1) mfmas(LS);   // the last slice's last substep
+  mfmas(LS);   // the last slice's last substep
+  // the redundant tail slices land before the stages are reused below
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- a K piece of a split tile: park the partial sums; the last piece
   // to arrive adds them all in piece order and stores the tile ----
@@ -1409,8 +1390,8 @@ hipError_t launch_mode(const FfnArgs& a, hipStream_t s, int sched, int rt,
       else if (rt == 2) ffn_stream_kernel<MODE, 2, 1><<<grid, ST_WAVES * 64, 0, s>>>(a);
       else ffn_stream_kernel<MODE, 4, 1><<<grid, ST_WAVES * 64, 0, s>>>(a);
     }
-  } else if (sched == 1 || sched == 3) {
-    // sched 1: BM = 256, sched 3: BM = 128; max_tiles counts m-tiles.  With
+  } else if (sched == 1) {
+    // 256-row tiles; max_tiles counts m-tiles.  With
     // a split workspace each XCD may need up to split_cpx more workgroups
     // for the pieces of its last round; their counters start at zero.
     const int ncols = MODE == UP_SWIGLU ? TL_BN / 2 : TL_BN;
@@ -1422,12 +1403,8 @@ hipError_t launch_mode(const FfnArgs& a, hipStream_t s, int sched, int rt,
       const hipError_t e = launch_fill_zero32(a.split_cnt, (long long)N_XCD * a.split_cpx, s);
       if (e != hipSuccess) return e;
     }
-    if (sched == 1)
-      ffn_tiled_kernel<MODE, 256, 64, 2, TL_WAVES>
-          <<<(unsigned)tiles, TL_WAVES * 64, 0, s>>>(a, NB);
-    else
-      ffn_tiled_kernel<MODE, 128, 32, 6, TL_WAVES>
-          <<<(unsigned)tiles, TL_WAVES * 64, 0, s>>>(a, NB);
+    ffn_tiled_kernel<MODE, 256, 64, 2, TL_WAVES>
+        <<<(unsigned)tiles, TL_WAVES * 64, 0, s>>>(a, NB);
   } else if (sched == 4) {
     // max_tiles counts panels of PN_BM rows
     constexpr int cols = PN_W * 16 * (MODE == UP_SWIGLU ? PN_NBG / 2 : PN_NBG);
@@ -1460,8 +1437,7 @@ int ffn_schedule(int dtype, int T, int k, int E) {
   const long long tk = (long long)T * k;
   if (tk <= 64LL * E) return 0;        // stream
   if (tk <= 256LL * E) return 4;       // panel
-  if (tk >= 1024LL * E) return 1;      // tiled, 256-row tiles
-  return 3;                            // tiled, 128-row tiles
+  return 1;                            // tiled, 256-row tiles
 }
 
 namespace {
@@ -1477,7 +1453,7 @@ Plan plan_of(const FfnArgs& a) {
     const int maxrows = a.T;   // a token picks an expert at most once
     p.rt = maxrows <= 16 ? 1 : (maxrows <= 32 ? 2 : 4);
   }
-  const int bm = p.sched == 1 ? 256 : (p.sched == 4 ? PN_BM : (p.sched == 3 ? 128 : F32_BM));
+  const int bm = p.sched == 1 ? 256 : (p.sched == 4 ? PN_BM : F32_BM);
   p.max_tiles = (int)((tk + bm - 1) / bm) + a.E +
                 (a.n_shared ? (a.T + bm - 1) / bm : 0);
   return p;

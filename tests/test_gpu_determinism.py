@@ -24,11 +24,11 @@ CASES = [
     # panel, shared expert
     W("det_panel", T=500, d_model=192, n_experts=4, top_k=2, d_ff=320,
       act="swiglu", dtype="bf16", capacity=0, n_shared=1, seed_index=51),
-    # 128-row tiles, split last round, drops
-    W("det_tiled128", T=1500, d_model=128, n_experts=4, top_k=2, d_ff=256,
+    # tiled, split last round, drops
+    W("det_tiled_drops", T=1500, d_model=128, n_experts=4, top_k=2, d_ff=256,
       act="gelu", dtype="bf16", capacity=700, seed_index=52),
-    # 256-row tiles, split last round
-    W("det_tiled256", T=4200, d_model=256, n_experts=2, top_k=1, d_ff=512,
+    # tiled, split last round
+    W("det_tiled", T=4200, d_model=256, n_experts=2, top_k=1, d_ff=512,
       act="swiglu", dtype="bf16", capacity=0, seed_index=53),
 ]
 OTHER = W("det_other", T=3000, d_model=128, n_experts=2, top_k=1, d_ff=256,

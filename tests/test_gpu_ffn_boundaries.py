@@ -1,15 +1,15 @@
 """GPU parity of the expert FFN (moe_expert_ffn) against the CPU oracle on
 hand-made groupings whose per-expert row counts sit on every boundary of the
 bf16 schedules: empty experts, one row, 15/16/17 rows (16-row MFMA tiles),
-127/128/129 rows (half and full 256-row panels, 128-row tiles), 255/256/257
-rows (one or two panels or 256-row tiles), with and without a shared expert,
+127/128/129 rows (half and full 256-row panels), 255/256/257 rows (one or
+two panels or 256-row tiles), with and without a shared expert,
 odd numbers of 64-wide K steps and partial weight blocks.  The schedule is
 chosen from T, k and E only (stream up to 64 assignments per expert on
 average, panel up to 256, tiled beyond), so each case fixes T*k/E and then
 places the counts freely (rows past offsets[E] are unused).  Each case runs
-through moe_expert_ffn (with workspace: the tiled schedules may split their
-last round along K) and through moe_expert_up + moe_expert_down (no
-workspace: never split).  Outputs are compared by max |gpu - oracle| /
+through moe_expert_ffn (with workspace: the tiled schedule may split its
+last round along K), through moe_expert_up + moe_expert_down without a
+workspace (never split) and with one (split as in moe_expert_ffn).  Outputs are compared by max |gpu - oracle| /
 max |oracle| over the computed rows (2e-2, bf16)."""
 
 import numpy as np
@@ -44,12 +44,12 @@ CASES = [
        d_ff=448, act="gelu", dtype="bf16", capacity=0, n_shared=1,
        seed_index=43),
      [15, 16, 17, 385]),
-    # 128-row tiles: 256*E < T*k < 1024*E
-    (W("ffnb_tiled128", T=400, d_model=192, n_experts=2, top_k=2, d_ff=320,
+    # tiled: T*k > 256*E; a ragged and a two-tile expert, shared expert
+    (W("ffnb_tiled_shared", T=400, d_model=192, n_experts=2, top_k=2, d_ff=320,
        act="swiglu", dtype="bf16", capacity=0, n_shared=1, seed_index=44),
      [127, 385]),
-    # 256-row tiles: T*k >= 1024*E
-    (W("ffnb_tiled256", T=2100, d_model=128, n_experts=2, top_k=1,
+    # tiled, many rows per expert
+    (W("ffnb_tiled", T=2100, d_model=128, n_experts=2, top_k=1,
        d_ff=384, act="gelu", dtype="bf16", capacity=0, seed_index=45),
      [255, 1025]),
 ]
@@ -68,10 +68,12 @@ def _grouping(counts, T, k, seed):
     return np.asarray(perm, np.int32), offsets
 
 
-def _gpu_up_down(inp, perm, offsets, wl):
-    """moe_expert_up then moe_expert_down (no workspace)."""
+def _gpu_up_down(inp, perm, offsets, wl, with_ws=False):
+    """moe_expert_up then moe_expert_down, with or without a workspace."""
     p = moe.problem_for(wl)
     dev = inp["x"].device
+    ws = (torch.empty(moe.moe_workspace_bytes(p), dtype=torch.uint8,
+                      device=dev) if with_ws else None)
     rows = wl.T * wl.top_k + wl.n_shared * wl.T
     h = torch.full((rows, wl.d_ff), float("nan"), dtype=wl.torch_dtype,
                    device=dev)
@@ -82,8 +84,8 @@ def _gpu_up_down(inp, perm, offsets, wl):
     if perm.size:
         pt[:perm.size] = torch.as_tensor(perm, device=dev)
     ot = torch.as_tensor(offsets, device=dev)
-    moe.moe_expert_up(p, inp["x"], pt, ot, inp, h)
-    moe.moe_expert_down(p, h, ot, inp, y)
+    moe.moe_expert_up(p, inp["x"], pt, ot, inp, h, ws)
+    moe.moe_expert_down(p, h, ot, inp, y, ws)
     torch.cuda.synchronize()
     return y
 
@@ -117,6 +119,10 @@ def test_expert_ffn_boundaries(wl, counts):
     err, worst = _errors(y, ref, offsets, counts, rows)
     y2 = host(_gpu_up_down(inp, perm, offsets, wl)).astype(np.float64)
     err2, worst2 = _errors(y2, ref, offsets, counts, rows)
+    y3 = host(_gpu_up_down(inp, perm, offsets, wl, with_ws=True)).astype(
+        np.float64)
+    err3, worst3 = _errors(y3, ref, offsets, counts, rows)
     log(f"  moe_expert_ffn rel err {err:.2e} (worst expert {worst:.2e}); "
-        f"up+down {err2:.2e} ({worst2:.2e})")
-    assert max(err, worst, err2, worst2) <= TOL["bf16"]
+        f"up+down {err2:.2e} ({worst2:.2e}); with workspace {err3:.2e} "
+        f"({worst3:.2e})")
+    assert max(err, worst, err2, worst2, err3, worst3) <= TOL["bf16"]

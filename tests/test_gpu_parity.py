@@ -66,10 +66,11 @@ SMALL = [
     W("gelu_panel_bias_drops", T=3000, d_model=256, n_experts=16, top_k=1,
       d_ff=448, act="gelu", dtype="bf16", capacity=200, zipf_s=0.3,
       seed_index=27),
-    # 128-row tiles (256*E < T*k < 1024*E) with SwiGLU
-    W("swiglu_tiled128", T=1500, d_model=128, n_experts=4, top_k=2,
+    # tiled just past the panel range (750 rows per expert: two full
+    # 256-row tiles and a ragged one) with SwiGLU
+    W("swiglu_tiled_mid", T=1500, d_model=128, n_experts=4, top_k=2,
       d_ff=256, act="swiglu", dtype="bf16", capacity=0, seed_index=28),
-    # 256-row tiles (T*k >= 1024*E), ragged M and partial N blocks
+    # tiled, many rows per expert: ragged M and partial N blocks
     W("swiglu_bm256", T=2200, d_model=128, n_experts=2, top_k=1, d_ff=384,
       act="swiglu", dtype="bf16", capacity=0, seed_index=23),
     W("gelu_bm256_shared_drops", T=2100, d_model=320, n_experts=2, top_k=2,
