@@ -269,9 +269,11 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(DispatchArgs a,
 // Experts Works", Token Dropping and Overflow Handling: overflow tokens go
 // to expert slots with room left, weighted by the new expert's router
 // probability).  Dropped assignments are visited in ascending id; each
-// takes a free slot drawn with Philox4x32-10, so the walk is sequential:
-// one wave, lanes = experts (4 per lane), the draws of a 64-assignment
-// chunk computed in parallel.
+// takes a free slot drawn with Philox4x32-10.  In general the walk is
+// sequential (a token's own experts leave the candidates): one wave, lanes
+// = experts (4 per lane), the draws of a 64-assignment chunk computed in
+// parallel.  With one slot per token the draws' ranges are known in
+// advance and the walk is decoded in parallel (reassign_k1_kernel).
 // ---------------------------------------------------------------------------
 
 // Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers:
@@ -525,6 +527,234 @@ __global__ __launch_bounds__(64) void reassign_kernel(ReassignArgs a) {
   }
 }
 
+// One slot per token (k = 1): the token's own expert overflowed, so it has
+// no free slot and every expert with room is a candidate; every draw while
+// slots last succeeds, so the j-th dropped assignment draws r_j =
+// floor(x_j * (M - j) / 2^32) over the M - j slots still free, with no
+// dependence on where the earlier draws landed.  Draw j takes the r_j-th
+// slot that remains (free slots laid out in ascending expert order), so the
+// walk is the decoding of an inversion table: position p_j in the initial
+// layout.  It is decoded bottom-up in LDS like a merge sort: a block of
+// draws holds its positions, sorted, relative to the layout left by all
+// earlier blocks; merging block A with the block B after it maps each b of
+// B to b + #{i : a_i - i <= b} (the b-th slot not taken by A) and each a_i
+// of A keeps its position; both land at their merged index, found by one
+// binary search in the other block.  Then p_j gives the expert, and each
+// draw's rank among its expert's moved rows (in draw order) comes from
+// per-wave ballot counts.  Same outputs as reassign_kernel.
+constexpr int RP_THREADS = 1024;
+constexpr int RP_WAVES = RP_THREADS / 64;
+constexpr int RP_MAXP = 16384;   // draws (two 64 KB LDS buffers)
+constexpr int RP_MAXE = 512;     // experts (per-wave count tables)
+constexpr int RP_PER = RP_MAXP / RP_THREADS;   // draws per thread
+
+// Exclusive prefix of v over the workgroup (RP_THREADS threads) and the
+// total; s_w holds RP_WAVES ints.  Whole workgroup.
+__device__ __forceinline__ int rp_block_scan(int v, int* s_w, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int inc = wave_incl_scan(v, lane);
+  if (lane == 63) s_w[wave] = inc;
+  __syncthreads();
+  int base = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < RP_WAVES; ++w) {
+    const int x = s_w[w];
+    if (w < wave) base += x;
+    total += x;
+  }
+  __syncthreads();
+  return base + inc - v;
+}
+
+// WQ: 64-expert slots per lane for the per-wave counts (E <= 64 * WQ).
+template <int WQ>
+__global__ __launch_bounds__(RP_THREADS) void reassign_k1_kernel(ReassignArgs a) {
+  __shared__ uint32_t buf0[RP_MAXP];
+  __shared__ uint32_t buf1[RP_MAXP];
+  __shared__ int s_pre[RP_MAXE + 1];   // exclusive prefix of free slots
+  __shared__ int s_mv[RP_MAXE];        // moved rows per expert
+  __shared__ int s_w[RP_WAVES];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tk = a.T;                  // k = 1
+  const int E = a.E;
+  int32_t* drops = a.perm;             // scratch: ids of the drawing drops
+
+  // free slots per expert and their exclusive prefix; M = s_pre[E]
+  for (int e0 = 0; e0 <= E; e0 += RP_THREADS) {
+    const int e = e0 + tid;
+    const int sp = e < E ? a.capacity - (a.off0[e + 1] - a.off0[e]) : 0;
+    int tot;
+    const int ex = rp_block_scan(sp, s_w, tot);
+    const int carry = e0 == 0 ? 0 : s_pre[e0];
+    __syncthreads();
+    if (e <= E) s_pre[e] = carry + ex;
+    if (e < E) s_mv[e] = 0;
+    __syncthreads();
+  }
+  const int M = s_pre[E];
+
+  // dropped assignments in ascending id; the first M of them draw
+  int nd = 0;
+  for (int b0 = 0; b0 < tk; b0 += RP_THREADS) {
+    const int aid = b0 + tid;
+    bool drop = false;
+    if (aid < tk) {
+      drop = a.slot_of[aid] < 0 && (unsigned)a.idx[aid] < (unsigned)E;
+      a.rslot[aid] = -1;
+      a.newe[aid] = -1;
+    }
+    int tot;
+    const int pos = nd + rp_block_scan(drop ? 1 : 0, s_w, tot);
+    if (drop && pos < M) drops[pos] = aid;
+    nd += tot;
+  }
+  const int P = min(nd, M);
+  __syncthreads();
+
+  // draw j: r_j over the M - j free slots, packed (r << 16) | j
+  for (int j = tid; j < P; j += RP_THREADS) {
+    const uint32_t aid = (uint32_t)drops[j];
+    const uint32_t x = philox_word0(aid, 0u, 0u, 0u, a.key0, a.key1);
+    const uint32_t r = (uint32_t)(((unsigned long long)x * (unsigned)(M - j)) >> 32);
+    buf0[j] = (r << 16) | (uint32_t)j;
+  }
+  __syncthreads();
+
+  uint32_t* cur = buf0;
+  uint32_t* nxt = buf1;
+  for (int h = 1; h < P; h <<= 1) {
+    for (int i = tid; i < P; i += RP_THREADS) {
+      const int s0 = i & ~(2 * h - 1);
+      const int off = i - s0;
+      const uint32_t v = cur[i];
+      const int pos = (int)(v >> 16);
+      if (off < h) {
+        // A element: its merged index adds the B positions below its
+        // count of untaken slots
+        const int b0 = s0 + h;
+        const int bn = max(0, min(s0 + 2 * h, P) - b0);
+        const int ap = pos - off;
+        int lo = 0, hi = bn;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if ((int)(cur[b0 + mid] >> 16) < ap) lo = mid + 1;
+          else hi = mid;
+        }
+        nxt[s0 + off + lo] = v;
+      } else {
+        // B element (A is a full block of h): skip the slots A took
+        const int jb = off - h;
+        int lo = 0, hi = h;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if ((int)(cur[s0 + mid] >> 16) - mid <= pos) lo = mid + 1;
+          else hi = mid;
+        }
+        nxt[s0 + jb + lo] = ((uint32_t)(pos + lo) << 16) | (v & 0xFFFFu);
+      }
+    }
+    __syncthreads();
+    uint32_t* t = cur;
+    cur = nxt;
+    nxt = t;
+  }
+
+  // expert of each position (the one whose free slots hold it), by draw
+  for (int i = tid; i < P; i += RP_THREADS) {
+    const uint32_t v = cur[i];
+    const int pos = (int)(v >> 16);
+    int lo = 0, hi = E;   // last e with s_pre[e] <= pos
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pre[mid] <= pos) lo = mid;
+      else hi = mid - 1;
+    }
+    nxt[v & 0xFFFFu] = (uint32_t)lo;
+  }
+  __syncthreads();
+  const uint32_t* ebd = nxt;   // expert by draw
+  int* cnt = (int*)cur;        // [RP_WAVES][E] counts, reused LDS
+
+  // Ranks in draw order.  Wave w takes draws [w*Q, (w+1)*Q), 64 at a
+  // time; lane l keeps the wave's count of experts l + 64q in wc[q].  In a
+  // chunk, each distinct expert is taken once: one ballot finds its draws,
+  // their ranks follow the count so far in lane order, and the owning lane
+  // adds them.  Pass 1 counts, the waves' counts are prefixed per expert,
+  // pass 2 ranks (earlier waves, earlier chunks, lower lanes).
+  const int Q = ((P + RP_WAVES - 1) / RP_WAVES + 63) & ~63;
+  const int jbeg = wave * Q, jend = min(P, jbeg + Q);
+  int wc[WQ];
+  auto walk = [&](bool ranks) {
+    for (int c = jbeg; c < jend; c += 64) {
+      const int j = c + lane;
+      const bool valid = j < jend;
+      const int e = valid ? (int)ebd[j] : -1;
+      int rank = -1;
+      uint64_t mask = __ballot(valid);
+      while (mask) {
+        const int l0 = __ffsll((unsigned long long)mask) - 1;
+        const int e0 = rdlane(e, l0);
+        const uint64_t m = __ballot(valid && e == e0);
+        int base = 0;
+#pragma unroll
+        for (int q = 0; q < WQ; ++q)
+          if ((e0 >> 6) == q) base = rdlane(wc[q], e0 & 63);
+        if (e == e0)
+          rank = base + (int)__builtin_amdgcn_mbcnt_hi(
+                            (uint32_t)(m >> 32),
+                            __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+#pragma unroll
+        for (int q = 0; q < WQ; ++q)
+          if ((e0 >> 6) == q && lane == (e0 & 63)) wc[q] += __popcll(m);
+        mask &= ~m;
+      }
+      if (ranks && valid) {
+        const int aid = drops[j];
+        a.newe[aid] = e;
+        a.rslot[aid] = rank;
+      }
+    }
+  };
+#pragma unroll
+  for (int q = 0; q < WQ; ++q) wc[q] = 0;
+  walk(false);
+#pragma unroll
+  for (int q = 0; q < WQ; ++q)
+    if (lane + 64 * q < E) cnt[wave * E + lane + 64 * q] = wc[q];
+  __syncthreads();
+  for (int e = tid; e < E; e += RP_THREADS) {
+    int run = 0;
+    for (int w = 0; w < RP_WAVES; ++w) {
+      const int x = cnt[w * E + e];
+      cnt[w * E + e] = run;
+      run += x;
+    }
+    s_mv[e] = run;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < WQ; ++q)
+    wc[q] = lane + 64 * q < E ? cnt[wave * E + lane + 64 * q] : 0;
+  walk(true);
+  __syncthreads();
+
+  // offsets over the kept plus moved rows (ascending expert)
+  int run = 0;
+  for (int e0 = 0; e0 < E; e0 += RP_THREADS) {
+    const int e = e0 + tid;
+    const int kept = e < E ? (a.off0[e + 1] - a.off0[e]) + s_mv[e] : 0;
+    int tot;
+    const int ex = rp_block_scan(kept, s_w, tot);
+    if (e < E) a.offsets[e] = run + ex;
+    run += tot;
+  }
+  if (tid == 0) {
+    a.offsets[E] = run;
+    *a.n_dropped = (int32_t)(tk - run);
+  }
+}
+
 // New rows: an expert's kept assignments keep their order and shift by the
 // rows moved into earlier experts; its moved ones follow them.  A moved
 // slot's gate: the new expert's score under the token's normaliser (its
@@ -613,7 +843,16 @@ hipError_t launch_reassign(const ReassignArgs& a, hipStream_t s) {
     else if (a.k <= 4) reassign_kernel<C, 4><<<1, 64, 0, s>>>(a);    \
     else reassign_kernel<C, 8><<<1, 64, 0, s>>>(a);                  \
   } while (0)
-  if (a.E <= 64) MOE_REASSIGN(1);
+  // k = 1 within the LDS bounds: the parallel decode (draws are at most
+  // min(T, E * capacity); positions and draw ids fit 16 bits)
+  const long long slots = (long long)a.E * a.capacity;
+  if (a.k == 1 && a.E <= RP_MAXE && slots <= 65536 &&
+      (tk < slots ? tk : slots) <= RP_MAXP) {
+    if (a.E <= 64) reassign_k1_kernel<1><<<1, RP_THREADS, 0, s>>>(a);
+    else if (a.E <= 128) reassign_k1_kernel<2><<<1, RP_THREADS, 0, s>>>(a);
+    else if (a.E <= 256) reassign_k1_kernel<4><<<1, RP_THREADS, 0, s>>>(a);
+    else reassign_k1_kernel<8><<<1, RP_THREADS, 0, s>>>(a);
+  } else if (a.E <= 64) MOE_REASSIGN(1);
   else if (a.E <= 128) MOE_REASSIGN(2);
   else MOE_REASSIGN(4);
 #undef MOE_REASSIGN

@@ -39,8 +39,29 @@ RE = [
     W("re_f32", T=64, d_model=64, n_experts=4, top_k=2, d_ff=64, act="gelu",
       dtype="f32", capacity=28, zipf_s=1.1, seed_index=55,
       overflow="reassign", overflow_seed=77),
+    # k = 1 with room to spare (every drop finds a slot; re_switch_top1 runs
+    # out of slots first); both take the parallel one-slot-per-token decode
+    W("re_k1_room", T=900, d_model=64, n_experts=16, top_k=1, d_ff=64,
+      act="gelu", dtype="bf16", capacity=80, zipf_s=1.1, seed_index=56,
+      overflow="reassign", overflow_seed=5),
+    # k = 1 with more than 64 experts (per-wave counts over several
+    # registers per lane)
+    W("re_k1_many_experts", T=2000, d_model=64, n_experts=200, top_k=1,
+      d_ff=64, act="gelu", dtype="bf16", capacity=12, zipf_s=1.1,
+      seed_index=59, overflow="reassign", overflow_seed=11),
+    # k = 1 past that decode's bounds (more than 16384 draws possible): the
+    # sequential walk
+    W("re_k1_sequential", T=20000, d_model=64, n_experts=4, top_k=1,
+      d_ff=64, act="gelu", dtype="bf16", capacity=5200, zipf_s=1.1,
+      seed_index=57, overflow="reassign", overflow_seed=6),
 ]
 IDS = [w.name for w in RE]
+# the dispatch entry also sees a batch where nothing overflows
+ENTRY = RE + [
+    W("re_k1_no_drop", T=300, d_model=64, n_experts=8, top_k=1, d_ff=64,
+      act="gelu", dtype="bf16", capacity=300, zipf_s=1.1, seed_index=58,
+      overflow="reassign", overflow_seed=8),
+]
 _cache = {}
 
 
@@ -71,7 +92,7 @@ def test_reassign_layer(wl):
     assert torch.equal(g["out"], g2["out"])
 
 
-@pytest.mark.parametrize("wl", RE, ids=IDS)
+@pytest.mark.parametrize("wl", ENTRY, ids=[w.name for w in ENTRY])
 def test_dispatch_reassign_entry(wl):
     inp, _ = inputs(wl)
     r = oracle_route(inp, wl)
