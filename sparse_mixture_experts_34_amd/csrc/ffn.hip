@@ -104,16 +104,23 @@ __device__ __forceinline__ void group_weights(const FfnArgs& a, int g,
 // ===========================================================================
 // A workgroup owns 32 output columns (two groups of 16) of one group; its 4
 // waves split the K steps into contiguous quarters, stream their weight rows
-// straight into MFMA B registers (3-deep prefetch ring) and add their
-// partial sums through LDS in the fixed order 0,1,2,3.  Two column groups
-// per workgroup halve the token-row (A) reads per weight byte.
+// into registers (3-deep prefetch ring) and add their partial sums through
+// LDS in the fixed order 0,1,2,3.  Two column groups per workgroup halve the
+// token-row (A) reads per weight byte.
+//
+// Weight loads are non-temporal and cover whole 128-byte lines: a load
+// instruction reads 8 rows x 128 bytes (lane l: row l / 8, bytes 16 * (l %
+// 8) of the step), which streams HBM at the rate of a plain sequential read
+// (the MFMA operand order, 16 rows x 4 interleaved 16-byte pieces per
+// instruction, reads the same bytes about 10% slower).  Each step's weight
+// registers then pass through a per-wave LDS slot into MFMA B order.
 constexpr int ST_WAVES = 4;
 constexpr int ST_KSTEP = 64;         // K per step (two 16x16x32 MFMAs)
 constexpr int ST_PF = 3;             // prefetch ring depth (steps)
 
 template <int NMAT, int RT, int CG>
 struct StreamBuf {
-  u32x4 b[NMAT][CG][2];      // 16 bf16 of one weight row per matrix, group
+  u32x4 b[NMAT][CG][2];      // rows 8h + lane/8 of group c, 16 bytes each
   u32x4 a[RT][2];            // 16 bf16 of one token row per row tile
 };
 
@@ -122,6 +129,7 @@ template <int MODE, int RT, int CG>
 __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
   constexpr int NMAT = MODE == UP_SWIGLU ? 2 : 1;
   __shared__ f32x4 red[ST_WAVES - 1][NMAT * CG * RT][64];
+  __shared__ u32x4 xs[ST_WAVES][NMAT * CG * 2][64];   // weight reshuffle
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = blockIdx.y;
   const Group gr = group_of(g, a.offsets, a.E, a.T, a.k);
@@ -140,14 +148,23 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
   const int s_beg = wave * nsteps / ST_WAVES;
   const int my_steps = (wave + 1) * nsteps / ST_WAVES - s_beg;
   const int koff = s_beg * ST_KSTEP + kq * 16;
-  // weight row of column group c; a partial last group re-reads row N-1
-  // and stores nothing for it
-  const bf16* brow[NMAT][CG];
+  // weight rows 16c + 8h + lane/8 of column group c, bytes 16 * (lane % 8)
+  // of each step; a partial last group re-reads row N-1 and stores nothing
+  // for it
+  const bf16* brow[NMAT][CG][2];
 #pragma unroll
   for (int m = 0; m < NMAT; ++m)
 #pragma unroll
     for (int c = 0; c < CG; ++c)
-      brow[m][c] = wm[m] + (size_t)min(n0 + 16 * c + col, N - 1) * K + koff;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        brow[m][c][h] = wm[m] +
+                        (size_t)min(n0 + 16 * c + 8 * h + (lane >> 3), N - 1) * K +
+                        s_beg * ST_KSTEP + (lane & 7) * 8;
+  // MFMA B order: lane (col, kq), MFMA h holds row col, 16-byte piece
+  // 2kq + h of the step (the A operand below takes the same pieces); in the
+  // load order that is register col / 8, lane 8 * (col % 8) + 2kq + h
+  const int xsrc = col >> 3, xlane = 8 * (col & 7) + 2 * kq;
 
   for (int rg = 0; rg < gr.rows; rg += RT * 16) {
     const int ntile = min(RT, (gr.rows - rg + 15) >> 4);
@@ -171,10 +188,11 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int c = 0; c < CG; ++c) {
-          b.b[m][c][0] = ldg16(brow[m][c] + k0);
-          b.b[m][c][1] = ldg16(brow[m][c] + k0 + 8);
-        }
+        for (int c = 0; c < CG; ++c)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            b.b[m][c][h] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(brow[m][c][h] + k0));
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         if (t < ntile) {
@@ -183,7 +201,26 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
         }
       }
     };
+    // the step's weight registers into this wave's LDS slot (load order);
+    // the slot's previous reads are done (in-order LDS within a wave)
+    auto stage = [&](const StreamBuf<NMAT, RT, CG>& b) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int c = 0; c < CG; ++c)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            xs[wave][(m * CG + c) * 2 + h][lane] = b.b[m][c][h];
+    };
     auto compute = [&](const StreamBuf<NMAT, RT, CG>& b) {
+      u32x4 wb[NMAT][CG][2];
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int c = 0; c < CG; ++c)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            wb[m][c][h] = xs[wave][(m * CG + c) * 2 + xsrc][xlane + h];
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         if (t < ntile) {
@@ -196,7 +233,7 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
 #pragma unroll
               for (int c = 0; c < CG; ++c) {
                 V16 bv;
-                bv.u = b.b[m][c][h];
+                bv.u = wb[m][c][h];
                 acc[m][c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     av.h, bv.h, acc[m][c][t], 0, 0, 0);
               }
@@ -212,8 +249,10 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
       for (int p = 0; p < ST_PF; ++p) {
         const int s = s0 + p;
         if (s < my_steps) {
-          compute(buf[p]);
+          stage(buf[p]);
+          const StreamBuf<NMAT, RT, CG> cur = buf[p];
           if (s + ST_PF < my_steps) load(buf[p], s + ST_PF);
+          compute(cur);
         }
       }
     }
