@@ -433,7 +433,10 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_q4_kernel(FfnArgs a)
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int c = 0; c < CG; ++c) {
-          b.code[m][c] = ldg16(crow[m][c] + (size_t)s * 1024);
+          // codes stream once: non-temporal (the scale/offset pairs,
+          // 1/16 of the bytes, measured better as ordinary loads)
+          b.code[m][c] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(crow[m][c] + (size_t)s * 1024));
           b.qp[m][c] = qrow[m][c][s * 16];
         }
 #pragma unroll
