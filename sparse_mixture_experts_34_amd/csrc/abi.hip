@@ -100,6 +100,12 @@ int32_t check_problem(const moe_problem* p) {
     return MOE_ENOTSUP;
   const long long rows = (long long)p->T * p->top_k + (long long)p->n_shared * p->T;
   if (rows >= (1LL << 31)) return MOE_ENOTSUP;
+  // the GEMMs address a row-major activation matrix and one expert's
+  // weight matrix with 32-bit element offsets
+  const long long wide = p->d_model > p->d_ff ? p->d_model : p->d_ff;
+  if ((rows + p->T) * wide >= (1LL << 32) ||
+      (long long)p->d_model * p->d_ff >= (1LL << 32))
+    return MOE_ENOTSUP;
   return MOE_OK;
 }
 

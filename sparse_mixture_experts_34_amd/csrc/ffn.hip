@@ -1108,6 +1108,7 @@ constexpr int PN_W = 8;       // waves per workgroup
 constexpr int PN_NBG = 2;     // 16-row weight groups per wave
 constexpr int PN_RA = 4;      // LDS operand reads issued ahead of the MFMAs
 
+
 // LDS slice: BM rows of 128 bytes; 16-byte chunk c of row r sits at
 // position c ^ ((r >> 1) & 7).
 __device__ __forceinline__ int pn_key(int r) { return (r >> 1) & 7; }
@@ -1152,6 +1153,7 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
   static_assert(CG * NMAT == NBG && AI * W * 64 * 8 == SL, "shape");
   __shared__ __attribute__((aligned(16))) bf16 S0[SL];
   __shared__ __attribute__((aligned(16))) bf16 S1[SL];
+  __shared__ u32x4 xs[W][NMAT * CG * 2][64];   // weight reshuffle per wave
   __shared__ int s_info[3];
 
   const int G = a.E + a.n_shared;
@@ -1195,12 +1197,20 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
   // 16 rows x 4 chunks hit every LDS bank once (the order 2kq + h measured
   // about three conflict cycles per read).  A partial last block re-reads
   // row N-1 and stores nothing for it.
-  const bf16* brow[NMAT][CG];
+  // Weights are loaded in whole 128-byte lines (register h of group c: rows
+  // 8h + lane/8, bytes 16 * (lane % 8) of the step; half lines per
+  // instruction were slower: DeepSeek-V3 layer 5.75 against 5.51 ms) and
+  // pass through a per-wave LDS slot into MFMA order: row col, chunk
+  // kq + 4h is register col / 8, lane 8 * (col % 8) + kq + 4h.  Plain loads:
+  // the non-temporal hint was mixed here (Switch faster, DeepSeek slower).
+  uint32_t boff[CG][2];   // element offsets (same rows in every matrix)
 #pragma unroll
-  for (int m = 0; m < NMAT; ++m)
+  for (int c = 0; c < CG; ++c)
 #pragma unroll
-    for (int c = 0; c < CG; ++c)
-      brow[m][c] = wm[m] + (size_t)min(nbase + 16 * (wave * CG + c) + col, N - 1) * K + kq * 8;
+    for (int h = 0; h < 2; ++h)
+      boff[c][h] = (uint32_t)min(nbase + 16 * (wave * CG + c) + 8 * h + (lane >> 3), N - 1) *
+                       (uint32_t)K + (uint32_t)((lane & 7) * 8);
+  const int xsrc = col >> 3, xlane = 8 * (col & 7) + kq;
   // MFMA A operand of row tile t, half h: row 16t + col, chunk kq + 4h; the
   // swizzle key of row 16t + col is key(col) for every t.
   const int aoff0 = col * PN_KSTEP + ((kq ^ pn_key(col)) << 3);
@@ -1227,11 +1237,21 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-      for (int c = 0; c < CG; ++c) {
-        b.b[m][c][0] = ldg16(brow[m][c] + k0);
-        b.b[m][c][1] = ldg16(brow[m][c] + k0 + 32);
-      }
+      for (int c = 0; c < CG; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) b.b[m][c][h] = ldg16(wm[m] + boff[c][h] + k0);
   };
+  // a weight slot into this wave's LDS slot (load order), then back in MFMA
+  // order; the slot's earlier reads are done (in-order LDS within a wave)
+  auto stageB = [&](const PanelB<NMAT, CG>& b) {
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int c = 0; c < CG; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) xs[wave][(m * CG + c) * 2 + h][lane] = b.b[m][c][h];
+  };
+
   f32x4 acc[NMAT][CG][MT];
 #pragma unroll
   for (int m = 0; m < NMAT; ++m)
@@ -1251,9 +1271,17 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
     const IntC<NA> na{};
     // MFMAs of one step: half h outermost, so the two MFMAs into one
     // accumulator are a tile sweep apart
-    auto compute = [&](const bf16* S, const PanelB<NMAT, CG>& b) {
+    // Per MFMA half h: the half's weight operands are read back from the
+    // wave's reshuffle slot (MFMA order), then the A operand of each tile.
+    auto compute = [&](const bf16* S) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
+        V16 bw[NMAT][CG];
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int c = 0; c < CG; ++c)
+            bw[m][c].u = xs[wave][(m * CG + c) * 2 + xsrc][xlane + 4 * h];
         const bf16* sa = S + (h ? aoff1 : aoff0);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -1262,37 +1290,37 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
 #pragma unroll
           for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-            for (int c = 0; c < CG; ++c) {
-              V16 bv;
-              bv.u = b.b[m][c][h];
-              acc[m][c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.h, bv.h, acc[m][c][t], 0, 0, 0);
-            }
+            for (int c = 0; c < CG; ++c)
+              acc[m][c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.h, bw[m][c].h, acc[m][c][t], 0, 0, 0);
         }
       }
-      // order: PN_RA operand reads ahead, then each tile's MFMAs followed
-      // by the next read (bounds the live operand registers)
+      // order: the first half's weight reads and PN_RA A reads ahead, then
+      // each tile's MFMAs followed by the next read (the second half's
+      // weight reads come in that stream ahead of its A reads)
       constexpr int NM = NMAT * CG;
       constexpr int RA = PN_RA < 2 * NT ? PN_RA : 2 * NT;
-      __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);   // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x100, NM + RA, 0);   // DS reads
 #pragma unroll
-      for (int i = 0; i < 2 * NT - RA; ++i) {
+      for (int i = 0; i < 2 * NT + NM - RA; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);   // MFMAs
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, RA * NM, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, RA * NM - NM * NM, 0);
     };
     // Step s (u = s mod U): reads slice s % 2 and weight slot s % (L+1);
     // first writes A step s+1 (register set (s+1) % L) into the other
-    // slice, whose readers finished at the last barrier, and reloads that
-    // set with A step s+1+L; after the MFMAs refills its weight slot with
-    // step s+1+L.
+    // slice, whose readers finished at the last barrier, and its weight
+    // slot into the wave's reshuffle slot; reloads the A set and refills
+    // the weight slot with step s+1+L, then runs the MFMAs (which read the
+    // weights back from the reshuffle slot in MFMA order).
     auto step = [&](int s, int u) {
       bf16* cur = (u & 1) ? S1 : S0;
       bf16* nxt = (u & 1) ? S0 : S1;
       storeA(na, ar[(u + 1) % L], nxt);
+      stageB(ring[u % NSLOT]);
       loadA(na, ar[(u + 1) % L], s + 1 + L);
-      compute(cur, ring[u % NSLOT]);
       loadB(ring[u % NSLOT], s + 1 + L);
+      compute(cur);
       lds_barrier();
     };
     // prologue in the loop's issue order: A step 0 into S0, then A step j
