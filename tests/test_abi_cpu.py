@@ -93,6 +93,11 @@ BAD = [
     (dict(scoring=2), moe.MOE_EINVAL),
     (dict(raw_gates=3), moe.MOE_EINVAL),
     (dict(overflow=2), moe.MOE_EINVAL),
+    # 32-bit GEMM offsets: one expert matrix of 2^32 elements, or activation
+    # rows past 2^32 elements
+    (dict(d_model=65536, d_ff=65536), moe.MOE_ENOTSUP),
+    (dict(T=2 ** 20, top_k=2, n_experts=8, d_model=2048, d_ff=2048),
+     moe.MOE_ENOTSUP),
 ]
 
 
