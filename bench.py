@@ -36,6 +36,8 @@ METRIC = ("MoE layer fwd tokens/s + % of bf16 MFMA / HBM roofline "
 # oracle sample (tokens whose expert outputs the oracle evaluates); routing
 # and dispatch of the oracle always cover the whole batch
 CPU_SAMPLE = {"mixtral_decode": 16, "mixtral_decode_int4": 2,
+              "mixtral_decode_tiled": 16, "mixtral_prefill_tiled": 48,
+              "switch_top1_cf1_tiled": 256, "deepseek_v3_tiled": 12,
               "mixtral_prefill": 48,
               "switch_top1_cf1": 256, "switch_top1_cf125": 256,
               "switch_top1_cf1_reassign": 256,
@@ -110,10 +112,15 @@ def main():
     # weights were last read two steps earlier, with the other copy read in
     # between, so the 256 MB memory-side cache gives no reuse across steps.
     q4 = wl.wquant == "int4"
+    tw = wl.wquant == "bf16_tiled"
     bf16_inp = inp
     if q4:
         # 4-bit expert weights, quantised on the device before timing
         inp = moe.quantize_weights(bf16_inp)
+    elif tw:
+        # bf16 expert weights in the GEMMs' tiled order, reordered on the
+        # device before timing
+        inp = moe.tile_weights(bf16_inp)
     wnames = [n for n in inp if n in moe.QUANT_MATRICES or
               n.endswith("_q") or n in ("b1", "b2", "shared_b1", "shared_b2")]
     inp_b = dict(inp)
@@ -273,7 +280,8 @@ def main():
                    "n_experts": E, "top_k": k, "d_ff": f, "act": wl.act,
                    "capacity": wl.capacity, "n_shared": wl.n_shared,
                    "expert_weights": "int4 (group 128, fp32 scale/offset)"
-                   if q4 else wl.dtype,
+                   if q4 else (wl.dtype + " (tiled order)" if tw
+                               else wl.dtype),
                    "scoring": wl.scoring, "raw_gates": wl.raw_gates,
                    "overflow": wl.overflow},
         "roofline": roof,

@@ -82,6 +82,7 @@ extern "C" {
 
 #define MOE_WQUANT_NONE 0 /* expert weights in the problem dtype          */
 #define MOE_WQUANT_INT4 1 /* expert weights as 4-bit codes, see below     */
+#define MOE_WQUANT_BF16_TILED 2 /* bf16 expert weights in tiled order    */
 #define MOE_Q4_GROUP 128  /* weights per (scale, offset) pair             */
 
 #define MOE_MAX_EXPERTS 256
@@ -105,7 +106,9 @@ extern "C" {
  *   wquant     MOE_WQUANT_NONE, or MOE_WQUANT_INT4 for 4-bit expert
  *              weights ([LBS] Production Considerations, Quantization for
  *              MoE); INT4 requires dtype BF16 and d_model, d_ff multiples
- *              of 128.  Zero-initialised structs get NONE.
+ *              of 128.  MOE_WQUANT_BF16_TILED: the same bf16 weights
+ *              stored in moe_tile_bf16's order (dtype BF16).
+ *              Zero-initialised structs get NONE.
  *   scoring    MOE_SCORING_SOFTMAX (default) or MOE_SCORING_SIGMOID
  *              ([FA] The knobs: softmax over all experts versus a
  *              per-expert sigmoid).  With sigmoid scores a selection bias
@@ -166,6 +169,11 @@ typedef struct moe_problem {
  * pairs (E*N*(K/128)*2 float32), in that function's tiled order; the
  * weight is offset + code * scale.  Biases stay in the problem dtype.  The
  * *_q pointers are ignored (may be NULL) without quantisation.
+ *
+ * With wquant = MOE_WQUANT_BF16_TILED the matrices w1, w_up, w2 (and the
+ * shared ones) hold the bf16 weights reordered by moe_tile_bf16 for the
+ * stacked [E*N, K] matrix (same size); biases are unchanged.  The values
+ * and the results are those of the row-major weights.
  */
 typedef struct moe_expert_weights {
   const void* w1;
@@ -388,6 +396,27 @@ int32_t moe_layer_forward(const moe_problem* p, const void* x,
  */
 int32_t moe_quantize_int4(const void* w, int64_t rows, int32_t K,
                           void* codes, float* qparams, hipStream_t stream);
+
+/*
+ * Reorder a row-major bf16 matrix [rows, K] (a stack of expert matrices
+ * [E*N, K]) into the tiled order read by the expert GEMMs when wquant =
+ * MOE_WQUANT_BF16_TILED.  For the callers that keep expert weights
+ * resident and serve many batches: the layout lets every weight load of
+ * the GEMMs read 1 KiB of consecutive bytes already in matrix-core
+ * operand order, instead of 16-byte pieces of 8 or 16 rows that must be
+ * reshuffled through LDS.  A storage order of this library, not of the
+ * method: tile (rb, kb) of 16 rows x 32 columns (1 KiB) sits at tile index
+ * rb * (K/32) + kb; inside it, 16-byte piece 16*q + r holds row 16*rb + r,
+ * columns 32*kb + 8*q .. 32*kb + 8*q + 7.  A permutation: out has rows*K
+ * bf16 like w.
+ *   w     [rows, K] bf16, device.
+ *   rows  a multiple of 16 (>= 0); K a positive multiple of 32.
+ *   out   rows*K bf16, device, must not overlap w.
+ * Enqueued on stream.  MOE_EINVAL for NULL pointers with rows > 0 or
+ * negative rows, MOE_ENOTSUP for other sizes.
+ */
+int32_t moe_tile_bf16(const void* w, int64_t rows, int32_t K, void* out,
+                      hipStream_t stream);
 
 /*
  * One step of auxiliary-loss-free balancing ([GN] DeepSeek-V3: the selection

@@ -26,14 +26,14 @@ LIB_PATH = os.path.join(PKG, "libmoe.so")
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_ACT_GELU, MOE_ACT_SWIGLU = 0, 1
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
-MOE_WQUANT_NONE, MOE_WQUANT_INT4 = 0, 1
+MOE_WQUANT_NONE, MOE_WQUANT_INT4, MOE_WQUANT_BF16_TILED = 0, 1, 2
 MOE_SCORING_SOFTMAX, MOE_SCORING_SIGMOID = 0, 1
 MOE_OVERFLOW_DROP, MOE_OVERFLOW_REASSIGN = 0, 1
 OVERFLOW = {"drop": MOE_OVERFLOW_DROP, "reassign": MOE_OVERFLOW_REASSIGN}
 SCORING = {"softmax": MOE_SCORING_SOFTMAX, "sigmoid": MOE_SCORING_SIGMOID}
 MOE_Q4_GROUP = 128
 WQUANT = {None: MOE_WQUANT_NONE, "none": MOE_WQUANT_NONE,
-          "int4": MOE_WQUANT_INT4}
+          "int4": MOE_WQUANT_INT4, "bf16_tiled": MOE_WQUANT_BF16_TILED}
 ACT = {"gelu": MOE_ACT_GELU, "swiglu": MOE_ACT_SWIGLU}
 DTYPE = {"f32": MOE_DTYPE_F32, "bf16": MOE_DTYPE_BF16}
 TORCH_DTYPE = {MOE_DTYPE_F32: torch.float32, MOE_DTYPE_BF16: torch.bfloat16}
@@ -82,6 +82,7 @@ _SIGS = {
     "moe_layer_forward": (_I32, [_P, _V, _V, _V, _V, _W, _V, _V, _V, _V, _V,
                                  _V, _SZ, _V]),
     "moe_quantize_int4": (_I32, [_V, ctypes.c_int64, _I32, _V, _V, _V]),
+    "moe_tile_bf16": (_I32, [_V, ctypes.c_int64, _I32, _V, _V]),
     "moe_update_select_bias": (_I32, [_P, _V, _V, ctypes.c_float, _V]),
     "moe_dispatch_reassign": (_I32, [_P, _V, _V, _V, _V, _V, _V, _V, _V, _V,
                                      _V, _V, _SZ, _V]),
@@ -286,6 +287,15 @@ def moe_quantize_int4(w, codes, qparams, stream=None):
            "moe_quantize_int4")
 
 
+def moe_tile_bf16(w, out, stream=None):
+    """``out`` (same shape and size as the bf16 matrix or stack ``w``, last
+    axis K) gets ``w`` in the GEMMs' tiled order."""
+    K = w.shape[-1]
+    rows = w.numel() // K if K else 0
+    _check(_lib.moe_tile_bf16(_ptr(w), rows, K, _ptr(out), _stream(stream)),
+           "moe_tile_bf16")
+
+
 def moe_dispatch_reassign(p, topk_idx, topk_gate, logits, prob_mean, counts,
                           offsets, perm, slot_of, n_dropped, aux_loss, ws,
                           stream=None):
@@ -326,6 +336,22 @@ def quantize_weights(inp: dict, stream=None) -> dict:
         moe_quantize_int4(w, codes, qp, stream)
         out[n] = codes
         out[n + "_q"] = qp
+    return out
+
+
+def tile_weights(inp: dict, stream=None) -> dict:
+    """A copy of a weights dict with every bf16 expert matrix replaced by
+    its tiled-order copy (same key, same shape), made on the device by
+    :func:`moe_tile_bf16`, for problems with wquant "bf16_tiled".  Biases
+    and the router stay as they are."""
+    out = dict(inp)
+    for n in QUANT_MATRICES:
+        w = inp.get(n)
+        if w is None:
+            continue
+        t = torch.empty_like(w)
+        moe_tile_bf16(w, t, stream)
+        out[n] = t
     return out
 
 
@@ -384,5 +410,5 @@ def flops_and_bytes(wl, counts, kept_total) -> tuple:
 
 __all__ = [n for n in dir() if n.startswith("moe_")] + [
     "problem", "problem_for", "expert_weights", "workspace", "layer_forward",
-    "quantize_weights", "QUANT_MATRICES",
+    "quantize_weights", "tile_weights", "QUANT_MATRICES",
     "flops_and_bytes", "MoEError", "synth", "library_path", "EXPORTS"]

@@ -66,7 +66,7 @@ Layout make_layout(const moe_problem& p) {
   // tiled expert GEMMs (bf16 weights): one partial tile and one counter
   // per CU for the K-split last round
   const int sched = ffn_schedule(p.dtype, p.T, p.top_k, p.n_experts);
-  L.split_cpx = (p.wquant == MOE_WQUANT_NONE && sched == 1)
+  L.split_cpx = (p.wquant != MOE_WQUANT_INT4 && sched == 1)
                     ? device_cus() / 8 : 0;
   L.split_part = take((size_t)8 * L.split_cpx * SPLIT_TILE_FLOATS * 4);
   L.split_cnt = take((size_t)8 * L.split_cpx * 4);
@@ -87,8 +87,11 @@ int32_t check_problem(const moe_problem* p) {
   if (p->dtype != MOE_DTYPE_F32 && p->dtype != MOE_DTYPE_BF16)
     return MOE_EINVAL;
   if (!isfinite(p->aux_coef)) return MOE_EINVAL;
-  if (p->wquant != MOE_WQUANT_NONE && p->wquant != MOE_WQUANT_INT4)
+  if (p->wquant != MOE_WQUANT_NONE && p->wquant != MOE_WQUANT_INT4 &&
+      p->wquant != MOE_WQUANT_BF16_TILED)
     return MOE_EINVAL;
+  if (p->wquant == MOE_WQUANT_BF16_TILED && p->dtype != MOE_DTYPE_BF16)
+    return MOE_ENOTSUP;
   if (p->scoring != MOE_SCORING_SOFTMAX && p->scoring != MOE_SCORING_SIGMOID)
     return MOE_EINVAL;
   if (p->raw_gates != 0 && p->raw_gates != 1) return MOE_EINVAL;
@@ -518,6 +521,16 @@ int32_t moe_quantize_int4(const void* w, int64_t rows, int32_t K,
   // 32-bit dispatch size
   if ((long long)rows * (K / 8) >= (1LL << 32) - 256) return MOE_ENOTSUP;
   return status_of(launch_quantize_int4(w, rows, K, codes, qparams, stream));
+}
+
+int32_t moe_tile_bf16(const void* w, int64_t rows, int32_t K, void* out,
+                      hipStream_t stream) {
+  if (rows < 0) return MOE_EINVAL;
+  if (K <= 0 || K % 32 != 0 || rows % 16 != 0) return MOE_ENOTSUP;
+  if (rows > 0 && (!w || !out)) return MOE_EINVAL;
+  // one thread per 16-byte piece: the grid must fit the 32-bit dispatch size
+  if ((long long)rows * (K / 8) >= (1LL << 32) - 256) return MOE_ENOTSUP;
+  return status_of(launch_tile_bf16(w, rows, K, out, stream));
 }
 
 int32_t moe_update_select_bias(const moe_problem* p, const int32_t* counts,

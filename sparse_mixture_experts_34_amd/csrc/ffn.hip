@@ -125,11 +125,13 @@ struct StreamBuf {
 };
 
 // CG = 16-column groups per workgroup.
-template <int MODE, int RT, int CG>
+// TW: weights in tiled order (one 1 KiB tile per MFMA B operand, read
+// straight into registers; no reshuffle).
+template <int MODE, int RT, int CG, bool TW>
 __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
   constexpr int NMAT = MODE == UP_SWIGLU ? 2 : 1;
   __shared__ f32x4 red[ST_WAVES - 1][NMAT * CG * RT][64];
-  __shared__ u32x4 xs[ST_WAVES][NMAT * CG * 2][64];   // weight reshuffle
+  __shared__ u32x4 xs[TW ? 1 : ST_WAVES][NMAT * CG * 2][64];   // reshuffle
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = blockIdx.y;
   const Group gr = group_of(g, a.offsets, a.E, a.T, a.k);
@@ -147,7 +149,21 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
   const int nsteps = K / ST_KSTEP;
   const int s_beg = wave * nsteps / ST_WAVES;
   const int my_steps = (wave + 1) * nsteps / ST_WAVES - s_beg;
-  const int koff = s_beg * ST_KSTEP + kq * 16;
+  // A operand of MFMA h: 8 elements at koff + 8h (row-major weights:
+  // piece 2kq + h of the step) or koff + 32h (tiled weights: the tile's
+  // columns 8kq .. 8kq + 7 of each 32-column block)
+  const int koff = s_beg * ST_KSTEP + kq * (TW ? 8 : 16);
+  constexpr int AH = TW ? 32 : 8;
+  // tiled weights: the tile of rows n0 + 16c (clamped to the last row
+  // block) and the wave's first 32-column block, this lane's 16 bytes
+  const bf16* btile[NMAT][CG];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int c = 0; c < CG; ++c)
+      btile[m][c] = wm[m] +
+                    ((size_t)min((n0 >> 4) + c, N / 16 - 1) * (K / 32) + 2 * s_beg) * 512 +
+                    lane * 8;
   // weight rows 16c + 8h + lane/8 of column group c, bytes 16 * (lane % 8)
   // of each step; a partial last group re-reads row N-1 and stores nothing
   // for it
@@ -191,19 +207,20 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
         for (int c = 0; c < CG; ++c)
 #pragma unroll
           for (int h = 0; h < 2; ++h)
-            b.b[m][c][h] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4*>(brow[m][c][h] + k0));
+            b.b[m][c][h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                TW ? btile[m][c] + (size_t)(2 * s + h) * 512 : brow[m][c][h] + k0));
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         if (t < ntile) {
           b.a[t][0] = ldg16(arow[t] + k0);
-          b.a[t][1] = ldg16(arow[t] + k0 + 8);
+          b.a[t][1] = ldg16(arow[t] + k0 + AH);
         }
       }
     };
     // the step's weight registers into this wave's LDS slot (load order);
     // the slot's previous reads are done (in-order LDS within a wave)
     auto stage = [&](const StreamBuf<NMAT, RT, CG>& b) {
+      if constexpr (TW) return;
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -220,7 +237,8 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
         for (int c = 0; c < CG; ++c)
 #pragma unroll
           for (int h = 0; h < 2; ++h)
-            wb[m][c][h] = xs[wave][(m * CG + c) * 2 + xsrc][xlane + h];
+            wb[m][c][h] = TW ? b.b[m][c][h]
+                             : xs[TW ? 0 : wave][(m * CG + c) * 2 + xsrc][xlane + h];
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         if (t < ntile) {
@@ -747,7 +765,10 @@ struct SliceGeom {
   }
 };
 
-template <int MODE, int BM, int BK, int NS, int WAVES>
+// TW: weights in tiled order: a B slice is 16 row blocks x 2 column
+// blocks of 1 KiB tiles, each loaded by one direct-to-LDS instruction and
+// kept in tile order in LDS (BK = 64).
+template <int MODE, int BM, int BK, int NS, int WAVES, bool TW>
 __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
                                                                   int NB) {
   using Geo = SliceGeom<BK>;
@@ -763,6 +784,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
   constexpr int D = NS - 1;                         // slices in flight
   constexpr int SA = BM * BK, SB = TL_BN * BK;      // elements per slice
   static_assert(IA >= 1 && IB >= 1, "every wave loads A and B rows");
+  static_assert(!TW || (BK == 64 && IB * WAVES * Geo::RPI == TL_BN &&
+                        TL_BN / 16 * 2 == IB * WAVES),
+                "tiled weights: one 1 KiB tile per B load instruction");
   // NS stages of A and B slices; every stage index below is a compile-time
   // constant, so the compiler can see that the stage being loaded never
   // aliases the stage being read and does not make LDS reads wait for the
@@ -855,6 +879,24 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
     }
     wrow = min(wrow, N - 1);
     bo[i] = (uint32_t)wrow * (uint32_t)K + ((lp ^ Geo::key(row)) << 3);
+    if constexpr (TW) {
+      // instruction ii = wave * IB + i loads tile (row block ii / 2 of the
+      // slice's B rows, column block ii % 2): weight row block of LDS rows
+      // 16 * (ii / 2) .. +15 (SwiGLU: gate or up rows, as above)
+      const int ii = wave * IB + i;
+      const int r0 = 16 * (ii >> 1);
+      int wr0;
+      if (MODE == UP_SWIGLU) {
+        bb[i] = (const bf16*)(((r0 >> 5) & 1) ? w1v : w0v);
+        wr0 = nbase + 32 * (r0 >> 6) + (r0 & 31);
+      } else {
+        bb[i] = (const bf16*)w0v;
+        wr0 = nbase + r0;
+      }
+      const int rbg = min(wr0 >> 4, N / 16 - 1);
+      bo[i] = ((uint32_t)rbg * (uint32_t)(K / 32) + (uint32_t)(ii & 1)) * 512u +
+              (uint32_t)(lane * 8);
+    }
   }
   auto issue = [&](int kt, bf16* Ad, bf16* Bd) {
     const int k0 = (kb + kt) * BK;
@@ -862,8 +904,12 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
     for (int i = 0; i < IA; ++i)
       dma16(abase_g + ao[i] + k0, Ad + (wave * IA + i) * Geo::RPI * BK);
 #pragma unroll
-    for (int i = 0; i < IB; ++i)
-      dma16(bb[i] + bo[i] + k0, Bd + (wave * IB + i) * Geo::RPI * BK);
+    for (int i = 0; i < IB; ++i) {
+      if constexpr (TW)
+        dma16(bb[i] + bo[i] + (size_t)(kb + kt) * 1024, Bd + (wave * IB + i) * 512);
+      else
+        dma16(bb[i] + bo[i] + k0, Bd + (wave * IB + i) * Geo::RPI * BK);
+    }
   };
 
   f32x16 acc[MT][NT];
@@ -880,6 +926,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
   const int akey = Geo::key(l31);
   const int arow0 = (wm * WM + l31) * BK;
   const int brow0 = (wn * WN + l31) * BK;
+  // tiled weights in LDS: row l31 of N-tile j is row block
+  // (wn*WN + 32j)/16 + l31/16, piece 16*(chunk % 4) + l31 % 16 of column
+  // block chunk / 4 (chunk 2ss + q)
+  const int tb0 = ((wn * WN) / 16 + (l31 >> 4)) * 1024 + (l31 & 15) * 8 + q * 128;
   // Operands of substep ss+1 are read from LDS before the MFMAs of substep
   // ss are issued, so LDS latency overlaps matrix work.  Two register sets
   // of operands, alternating by substep.
@@ -887,13 +937,14 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
   auto fetch = [&](const bf16* Ab, const bf16* Bb, int ss, int set) {
     const int pos = ((ss * 2 + q) ^ akey) << 3;
     const bf16* ap = Ab + arow0 + pos;
-    const bf16* bp = Bb + brow0 + pos;
+    const bf16* bp = TW ? Bb + tb0 + (ss >> 1) * 512 + (ss & 1) * 256 : Bb + brow0 + pos;
+    constexpr int BJ = TW ? 2048 : 32 * BK;   // next N-tile
 #pragma unroll
     for (int i = 0; i < MT; ++i)
       av[set][i].u = *reinterpret_cast<const u32x4*>(ap + i * 32 * BK);
 #pragma unroll
     for (int j = 0; j < NT; ++j)
-      bv[set][j].u = *reinterpret_cast<const u32x4*>(bp + j * 32 * BK);
+      bv[set][j].u = *reinterpret_cast<const u32x4*>(bp + j * BJ);
   };
   auto mfmas = [&](int set) {
 #pragma unroll
@@ -1140,7 +1191,9 @@ constexpr int pn_lcm(int x, int y) { return x / pn_gcd(x, y) * y; }
 // anyway, and for nothing later.
 // W waves per workgroup, NBG groups of 16 weight rows per wave (SwiGLU:
 // NBG/2 gate groups and the matching up groups).
-template <int MODE, int BM, int L, int W, int NBG>
+// TW: weights in tiled order (each weight load reads one 1 KiB tile in MFMA
+// operand order; no reshuffle).
+template <int MODE, int BM, int L, int W, int NBG, bool TW>
 __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
                                                               int NB) {
   constexpr int NMAT = MODE == UP_SWIGLU ? 2 : 1;
@@ -1153,7 +1206,7 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
   static_assert(CG * NMAT == NBG && AI * W * 64 * 8 == SL, "shape");
   __shared__ __attribute__((aligned(16))) bf16 S0[SL];
   __shared__ __attribute__((aligned(16))) bf16 S1[SL];
-  __shared__ u32x4 xs[W][NMAT * CG * 2][64];   // weight reshuffle per wave
+  __shared__ u32x4 xs[TW ? 1 : W][NMAT * CG * 2][64];   // reshuffle per wave
   __shared__ int s_info[3];
 
   const int G = a.E + a.n_shared;
@@ -1211,6 +1264,13 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
       boff[c][h] = (uint32_t)min(nbase + 16 * (wave * CG + c) + 8 * h + (lane >> 3), N - 1) *
                        (uint32_t)K + (uint32_t)((lane & 7) * 8);
   const int xsrc = col >> 3, xlane = 8 * (col & 7) + kq;
+  // tiled weights: element offset of group c's tile at column block 0
+  // (rows clamped to the last row block), this lane's 16 bytes
+  uint32_t toff[CG];
+#pragma unroll
+  for (int c = 0; c < CG; ++c)
+    toff[c] = (uint32_t)min((nbase >> 4) + wave * CG + c, N / 16 - 1) *
+                  (uint32_t)(K / 32) * 512u + (uint32_t)(lane * 8);
   // MFMA A operand of row tile t, half h: row 16t + col, chunk kq + 4h; the
   // swizzle key of row 16t + col is key(col) for every t.
   const int aoff0 = col * PN_KSTEP + ((kq ^ pn_key(col)) << 3);
@@ -1239,7 +1299,9 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
 #pragma unroll
       for (int c = 0; c < CG; ++c)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) b.b[m][c][h] = ldg16(wm[m] + boff[c][h] + k0);
+        for (int h = 0; h < 2; ++h)
+          b.b[m][c][h] = ldg16(wm[m] + (TW ? toff[c] + (uint32_t)(2 * min(s, nk - 1) + h) * 512u
+                                           : boff[c][h] + k0));
   };
   // a weight slot into this wave's LDS slot (load order), then back in MFMA
   // order; the slot's earlier reads are done (in-order LDS within a wave)
@@ -1273,7 +1335,7 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
     // accumulator are a tile sweep apart
     // Per MFMA half h: the half's weight operands are read back from the
     // wave's reshuffle slot (MFMA order), then the A operand of each tile.
-    auto compute = [&](const bf16* S) {
+    auto compute = [&](const bf16* S, const PanelB<NMAT, CG>& b) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         V16 bw[NMAT][CG];
@@ -1281,7 +1343,8 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
           for (int c = 0; c < CG; ++c)
-            bw[m][c].u = xs[wave][(m * CG + c) * 2 + xsrc][xlane + 4 * h];
+            bw[m][c].u = TW ? b.b[m][c][h]
+                            : xs[TW ? 0 : wave][(m * CG + c) * 2 + xsrc][xlane + 4 * h];
         const bf16* sa = S + (h ? aoff1 : aoff0);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -1299,13 +1362,14 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
       // weight reads come in that stream ahead of its A reads)
       constexpr int NM = NMAT * CG;
       constexpr int RA = PN_RA < 2 * NT ? PN_RA : 2 * NT;
-      __builtin_amdgcn_sched_group_barrier(0x100, NM + RA, 0);   // DS reads
+      constexpr int BR = TW ? 0 : NM;   // weight reads of a half from LDS
+      __builtin_amdgcn_sched_group_barrier(0x100, BR + RA, 0);   // DS reads
 #pragma unroll
-      for (int i = 0; i < 2 * NT + NM - RA; ++i) {
+      for (int i = 0; i < 2 * NT + BR - RA; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);   // MFMAs
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, RA * NM - NM * NM, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, RA * NM - BR * NM, 0);
     };
     // Step s (u = s mod U): reads slice s % 2 and weight slot s % (L+1);
     // first writes A step s+1 (register set (s+1) % L) into the other
@@ -1317,10 +1381,17 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
       bf16* cur = (u & 1) ? S1 : S0;
       bf16* nxt = (u & 1) ? S0 : S1;
       storeA(na, ar[(u + 1) % L], nxt);
-      stageB(ring[u % NSLOT]);
-      loadA(na, ar[(u + 1) % L], s + 1 + L);
-      loadB(ring[u % NSLOT], s + 1 + L);
-      compute(cur);
+      if constexpr (TW) {
+        // the MFMAs read the weight slot itself, then it is refilled
+        loadA(na, ar[(u + 1) % L], s + 1 + L);
+        compute(cur, ring[u % NSLOT]);
+        loadB(ring[u % NSLOT], s + 1 + L);
+      } else {
+        stageB(ring[u % NSLOT]);
+        loadA(na, ar[(u + 1) % L], s + 1 + L);
+        loadB(ring[u % NSLOT], s + 1 + L);
+        compute(cur, ring[u % NSLOT]);
+      }
       lds_barrier();
     };
     // prologue in the loop's issue order: A step 0 into S0, then A step j
@@ -1441,7 +1512,7 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(FfnArgs a) {
   }
 }
 
-template <int MODE>
+template <int MODE, bool TW>
 hipError_t launch_mode(const FfnArgs& a, hipStream_t s, int sched, int rt,
                        int max_tiles) {
   const int N = MODE == DOWN ? a.d : a.d_ff;
@@ -1452,13 +1523,13 @@ hipError_t launch_mode(const FfnArgs& a, hipStream_t s, int sched, int rt,
     const int cg = (long long)((N + 31) / 32) * G >= 512 ? 2 : 1;
     dim3 grid((N + 16 * cg - 1) / (16 * cg), G);
     if (cg == 2) {
-      if (rt == 1) ffn_stream_kernel<MODE, 1, 2><<<grid, ST_WAVES * 64, 0, s>>>(a);
-      else if (rt == 2) ffn_stream_kernel<MODE, 2, 2><<<grid, ST_WAVES * 64, 0, s>>>(a);
-      else ffn_stream_kernel<MODE, 4, 2><<<grid, ST_WAVES * 64, 0, s>>>(a);
+      if (rt == 1) ffn_stream_kernel<MODE, 1, 2, TW><<<grid, ST_WAVES * 64, 0, s>>>(a);
+      else if (rt == 2) ffn_stream_kernel<MODE, 2, 2, TW><<<grid, ST_WAVES * 64, 0, s>>>(a);
+      else ffn_stream_kernel<MODE, 4, 2, TW><<<grid, ST_WAVES * 64, 0, s>>>(a);
     } else {
-      if (rt == 1) ffn_stream_kernel<MODE, 1, 1><<<grid, ST_WAVES * 64, 0, s>>>(a);
-      else if (rt == 2) ffn_stream_kernel<MODE, 2, 1><<<grid, ST_WAVES * 64, 0, s>>>(a);
-      else ffn_stream_kernel<MODE, 4, 1><<<grid, ST_WAVES * 64, 0, s>>>(a);
+      if (rt == 1) ffn_stream_kernel<MODE, 1, 1, TW><<<grid, ST_WAVES * 64, 0, s>>>(a);
+      else if (rt == 2) ffn_stream_kernel<MODE, 2, 1, TW><<<grid, ST_WAVES * 64, 0, s>>>(a);
+      else ffn_stream_kernel<MODE, 4, 1, TW><<<grid, ST_WAVES * 64, 0, s>>>(a);
     }
   } else if (sched == 1) {
     // 256-row tiles; max_tiles counts m-tiles.  With
@@ -1473,14 +1544,14 @@ hipError_t launch_mode(const FfnArgs& a, hipStream_t s, int sched, int rt,
       const hipError_t e = launch_fill_zero32(a.split_cnt, (long long)N_XCD * a.split_cpx, s);
       if (e != hipSuccess) return e;
     }
-    ffn_tiled_kernel<MODE, 256, 64, 2, TL_WAVES>
+    ffn_tiled_kernel<MODE, 256, 64, 2, TL_WAVES, TW>
         <<<(unsigned)tiles, TL_WAVES * 64, 0, s>>>(a, NB);
   } else if (sched == 4) {
     // max_tiles counts panels of PN_BM rows
     constexpr int cols = PN_W * 16 * (MODE == UP_SWIGLU ? PN_NBG / 2 : PN_NBG);
     const int NB = (N + cols - 1) / cols;
     long long tiles = (long long)(max_tiles + N_XCD - 1) / N_XCD * N_XCD * NB;
-    ffn_panel_kernel<MODE, PN_BM, PN_L, PN_W, PN_NBG><<<(unsigned)tiles, PN_W * 64, 0, s>>>(a, NB);
+    ffn_panel_kernel<MODE, PN_BM, PN_L, PN_W, PN_NBG, TW><<<(unsigned)tiles, PN_W * 64, 0, s>>>(a, NB);
   } else {
     dim3 grid(max_tiles, (N + F32_BN - 1) / F32_BN);
     ffn_f32_kernel<MODE><<<grid, 256, 0, s>>>(a);
@@ -1552,20 +1623,25 @@ hipError_t launch_q4(const FfnArgs& a, hipStream_t s) {
 
 hipError_t launch_expert_up(const FfnArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  if (a.wquant) {
+  if (a.wquant == 1) {   // 4-bit codes
     if (a.act == 1) return launch_q4<UP_SWIGLU>(a, s);
     return launch_q4<UP_GELU>(a, s);
   }
   const Plan p = plan_of(a);
-  if (a.act == 1) return launch_mode<UP_SWIGLU>(a, s, p.sched, p.rt, p.max_tiles);
-  return launch_mode<UP_GELU>(a, s, p.sched, p.rt, p.max_tiles);
+  if (a.wquant == 2) {   // bf16 weights in tiled order
+    if (a.act == 1) return launch_mode<UP_SWIGLU, true>(a, s, p.sched, p.rt, p.max_tiles);
+    return launch_mode<UP_GELU, true>(a, s, p.sched, p.rt, p.max_tiles);
+  }
+  if (a.act == 1) return launch_mode<UP_SWIGLU, false>(a, s, p.sched, p.rt, p.max_tiles);
+  return launch_mode<UP_GELU, false>(a, s, p.sched, p.rt, p.max_tiles);
 }
 
 hipError_t launch_expert_down(const FfnArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  if (a.wquant) return launch_q4<DOWN>(a, s);
+  if (a.wquant == 1) return launch_q4<DOWN>(a, s);   // 4-bit codes
   const Plan p = plan_of(a);
-  return launch_mode<DOWN>(a, s, p.sched, p.rt, p.max_tiles);
+  if (a.wquant == 2) return launch_mode<DOWN, true>(a, s, p.sched, p.rt, p.max_tiles);
+  return launch_mode<DOWN, false>(a, s, p.sched, p.rt, p.max_tiles);
 }
 
 }  // namespace moe

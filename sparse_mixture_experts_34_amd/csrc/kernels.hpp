@@ -107,6 +107,7 @@ struct FfnArgs {
   const void *sw1, *sw_up, *sw2, *sb1, *sb2;
   void* h;   // [T*k + n_shared*T, d_ff] workspace
   void* y;   // [T*k + n_shared*T, d]
+  // wquant = 2: bf16 matrices in tiled order (moe_tile_bf16).
   // 4-bit weights: wquant = 1, matrices hold codes, *q the (scale, offset)
   // pairs per group of Q4_GROUP weights
   int wquant;
@@ -128,6 +129,9 @@ hipError_t launch_expert_down(const FfnArgs& a, hipStream_t s);
 constexpr int Q4_GROUP = 128;   // weights per (scale, offset) pair
 hipError_t launch_quantize_int4(const void* w, long long rows, int K,
                                 void* codes, float* qparams, hipStream_t s);
+// bf16 [rows, K] -> tiled order (16 x 32 tiles in 16x16x32 operand order)
+hipError_t launch_tile_bf16(const void* w, long long rows, int K, void* out,
+                            hipStream_t s);
 
 // ---- combine ---------------------------------------------------------------
 hipError_t launch_combine(int dtype, const void* x, const void* y,

@@ -89,4 +89,34 @@ hipError_t launch_quantize_int4(const void* w, long long rows, int K,
   return hipGetLastError();
 }
 
+// bf16 weights in tiled order: one thread per 16-byte piece p of the
+// output; tile t = p / 64 (row block rb = t / (K/32), column block kb =
+// t % (K/32)), piece u = p % 64 holds row 16*rb + u % 16, columns
+// 32*kb + 8*(u / 16) .. +8.  Output writes are contiguous.
+namespace {
+__global__ __launch_bounds__(256) void tile_bf16_kernel(
+    const bf16* __restrict__ w, long long n_pieces, int K,
+    bf16* __restrict__ out) {
+  const long long p = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (p >= n_pieces) return;
+  const int kbs = K / 32;
+  const long long t = p >> 6;
+  const int u = (int)(p & 63);
+  const long long rb = t / kbs;
+  const int kb = (int)(t - rb * kbs);
+  const long long row = rb * 16 + (u & 15);
+  const size_t src = (size_t)row * K + (size_t)kb * 32 + (u >> 4) * 8;
+  stg16(out + (size_t)p * 8, ldg16(w + src));
+}
+}  // namespace
+
+hipError_t launch_tile_bf16(const void* w, long long rows, int K, void* out,
+                            hipStream_t s) {
+  const long long n = rows * (K / 8);
+  if (n == 0) return hipSuccess;
+  tile_bf16_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
+      (const bf16*)w, n, K, (bf16*)out);
+  return hipGetLastError();
+}
+
 }  // namespace moe

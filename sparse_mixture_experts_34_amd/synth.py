@@ -48,7 +48,7 @@ class Workload:
     zipf_s: float = 0.0               # router bias -s*ln(e+1) when > 0
     select_bias_std: float = 0.0      # > 0: DeepSeek-style selection bias
     seed_index: int = 0
-    wquant: str | None = None         # "int4": 4-bit expert weights
+    wquant: str | None = None         # "int4" | "bf16_tiled" (see binding)
     scoring: str = "softmax"          # router scores: softmax | sigmoid
     raw_gates: bool = False           # gates without renormalisation
     overflow: str = "drop"            # drop | reassign (random free slot)
@@ -109,6 +109,13 @@ WORKLOADS = {
         d_ff=2048, act="swiglu", dtype="bf16", capacity=0, n_shared=1,
         select_bias_std=0.1, seed_index=4),
 }
+# The same layers with their bf16 expert weights stored in the GEMMs' tiled
+# order (same seeds, so the same weight values).
+for _n in ("mixtral_decode", "mixtral_prefill", "switch_top1_cf1",
+           "deepseek_v3"):
+    WORKLOADS[_n + "_tiled"] = replace(WORKLOADS[_n], name=_n + "_tiled",
+                                       wquant="bf16_tiled")
+del _n
 
 
 def weight_shapes(wl: Workload) -> dict:

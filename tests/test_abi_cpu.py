@@ -90,6 +90,8 @@ BAD = [
     (dict(wquant=1, dtype=0), moe.MOE_ENOTSUP),        # int4 needs bf16
     (dict(wquant=1, d_model=192), moe.MOE_ENOTSUP),    # K % 128 != 0
     (dict(wquant=1, d_ff=320), moe.MOE_ENOTSUP),
+    (dict(wquant=2, dtype=0), moe.MOE_ENOTSUP),        # tiled needs bf16
+    (dict(wquant=3), moe.MOE_EINVAL),
     (dict(scoring=2), moe.MOE_EINVAL),
     (dict(raw_gates=3), moe.MOE_EINVAL),
     (dict(overflow=2), moe.MOE_EINVAL),
@@ -221,6 +223,19 @@ def test_quantize_int4_validation():
         moe.MOE_ENOTSUP
     # nothing to do: OK without touching any pointer or the device
     assert lib.moe_quantize_int4(None, 0, 128, None, None, None) == moe.MOE_OK
+
+
+def test_tile_bf16_validation():
+    lib = binding._lib
+    f = 0x1000
+    assert lib.moe_tile_bf16(f, -16, 64, f, None) == moe.MOE_EINVAL
+    assert lib.moe_tile_bf16(f, 16, 48, f, None) == moe.MOE_ENOTSUP   # K % 32
+    assert lib.moe_tile_bf16(f, 16, 0, f, None) == moe.MOE_ENOTSUP
+    assert lib.moe_tile_bf16(f, 8, 64, f, None) == moe.MOE_ENOTSUP    # rows % 16
+    assert lib.moe_tile_bf16(None, 16, 64, f, None) == moe.MOE_EINVAL
+    assert lib.moe_tile_bf16(f, 16, 64, None, None) == moe.MOE_EINVAL
+    assert lib.moe_tile_bf16(f, 1 << 40, 64, f, None) == moe.MOE_ENOTSUP
+    assert lib.moe_tile_bf16(None, 0, 64, None, None) == moe.MOE_OK
 
 
 def test_struct_layouts_match_the_header():
