@@ -1300,8 +1300,11 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
       for (int c = 0; c < CG; ++c)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          b.b[m][c][h] = ldg16(wm[m] + (TW ? toff[c] + (uint32_t)(2 * min(s, nk - 1) + h) * 512u
-                                           : boff[c][h] + k0));
+          // tiled weights: non-temporal (measured faster there; on the
+          // row-major lines the hint was mixed)
+          b.b[m][c][h] = TW ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                                  wm[m] + toff[c] + (uint32_t)(2 * min(s, nk - 1) + h) * 512u))
+                            : ldg16(wm[m] + boff[c][h] + k0);
   };
   // a weight slot into this wave's LDS slot (load order), then back in MFMA
   // order; the slot's earlier reads are done (in-order LDS within a wave)
