@@ -35,7 +35,10 @@
 //           staged through LDS for 16-byte row stores, and each XCD's last
 //           round of tiles split along K over its CUs.
 // 4-bit weights use the stream schedule at every batch size; float32
-// problems use a plain float32 kernel (same grouping).
+// problems use a plain float32 kernel (same grouping).  bf16 weights may
+// also come in tiled order (wquant 2, moe_tile_bf16: 1 KiB tiles of 16 rows
+// x 32 columns in 16x16x32 operand order); every bf16 schedule has a
+// variant (template flag TW) that loads those tiles as they are.
 #include "common.hpp"
 #include "kernels.hpp"
 
