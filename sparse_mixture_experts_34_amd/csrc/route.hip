@@ -373,14 +373,28 @@ __global__ __launch_bounds__(RS_WAVES * 64) void route_select_kernel(
   }
 }
 
-__global__ void prob_mean_kernel(const float* __restrict__ partials,
-                                 float* __restrict__ pm, int nblk, int T,
-                                 int E) {
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    float v = 0.f;
-#pragma unroll 8
-    for (int b = 0; b < nblk; ++b) v += partials[(size_t)b * E + e];
-    pm[e] = T > 0 ? v / (float)T : 0.f;
+// Column means of the per-block probability partials [nblk, E], in a fixed
+// order: 64 experts per workgroup, PM_PARTS strided parts per expert (part
+// p adds blocks p, p + PM_PARTS, ...), then the parts added in order.
+constexpr int PM_PARTS = 16;
+__global__ __launch_bounds__(64 * PM_PARTS) void prob_mean_kernel(
+    const float* __restrict__ partials, float* __restrict__ pm, int nblk,
+    int T, int E) {
+  __shared__ float part[PM_PARTS][64];
+  const int lane = threadIdx.x & 63, p = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
+  float v = 0.f;
+  if (e < E) {
+#pragma unroll 4
+    for (int b = p; b < nblk; b += PM_PARTS) v += partials[(size_t)b * E + e];
+  }
+  part[p][lane] = v;
+  __syncthreads();
+  if (p == 0 && e < E) {
+    float sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < PM_PARTS; ++q) sum += part[q][lane];
+    pm[e] = T > 0 ? sum / (float)T : 0.f;
   }
 }
 
@@ -452,7 +466,8 @@ hipError_t launch_route_select_from(const float* part, int ksplit,
 
 hipError_t launch_prob_mean(const float* partials, float* prob_mean, int nblk,
                             int T, int E, hipStream_t s) {
-  prob_mean_kernel<<<1, 256, 0, s>>>(partials, prob_mean, nblk, T, E);
+  prob_mean_kernel<<<(E + 63) / 64, 64 * PM_PARTS, 0, s>>>(partials, prob_mean,
+                                                           nblk, T, E);
   return hipGetLastError();
 }
 
