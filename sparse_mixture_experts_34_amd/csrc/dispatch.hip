@@ -114,8 +114,10 @@ __device__ void scan_all(int* chunk, int nchunks, const DispatchArgs& a,
   const int need = max(max(nchunks, (n_part + 15) / 16), 1);
   int tpe = 1;
   while (tpe < need && tpe * 2 * E <= NTHR) tpe *= 2;
-  const int e = t / tpe, j = t % tpe;
-  const bool act = e < E;
+  // expert-minor: consecutive lanes take consecutive experts of one chunk
+  // row, so the chunk and partial loads are coalesced
+  const bool act = t < tpe * E;
+  const int e = act ? t % E : E, j = act ? t / E : 0;
   // ---- per-chunk counts -> chunk base ranks, per-expert totals ----------
   const int cpt = (nchunks + tpe - 1) / tpe;
   const int c0 = min(j * cpt, nchunks), c1 = min(c0 + cpt, nchunks);
@@ -129,7 +131,7 @@ __device__ void scan_all(int* chunk, int nchunks, const DispatchArgs& a,
   int base = 0, count = 0;
   if (act) {
     for (int jj = 0; jj < tpe; ++jj) {
-      const int v = red_i[e * tpe + jj];
+      const int v = red_i[jj * E + e];
       if (jj < j) base += v;
       count += v;
     }
@@ -184,7 +186,7 @@ __device__ void scan_all(int* chunk, int nchunks, const DispatchArgs& a,
     float pm;
     if (a.partials) {
       float v = 0.f;
-      for (int jj = 0; jj < tpe; ++jj) v += red_f[e * tpe + jj];
+      for (int jj = 0; jj < tpe; ++jj) v += red_f[jj * E + e];
       pm = v / (float)a.T;
       if (a.prob_mean_out) a.prob_mean_out[e] = pm;
     } else {
