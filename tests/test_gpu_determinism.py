@@ -7,6 +7,8 @@ layer three times through one workspace, with another problem's call in
 between (its split counters and partial tiles share the workspace area), and
 every output must match the first call bit for bit."""
 
+from dataclasses import replace
+
 import pytest
 import torch
 
@@ -31,12 +33,18 @@ CASES = [
     W("det_tiled", T=4200, d_model=256, n_experts=2, top_k=1, d_ff=512,
       act="swiglu", dtype="bf16", capacity=0, seed_index=53),
 ]
+# the same schedules with tiled bf16 weights
+CASES += [replace(w, name=w.name + "_tw", wquant="bf16_tiled")
+          for w in CASES[1:]]
 OTHER = W("det_other", T=3000, d_model=128, n_experts=2, top_k=1, d_ff=256,
           act="gelu", dtype="bf16", capacity=0, seed_index=54)
 
 
 def _layer(inp, wl, ws):
     p = moe.problem_for(wl)
+    if wl.wquant == "bf16_tiled":
+        inp = dict(inp, **{n: v for n, v in moe.tile_weights(inp).items()
+                           if n in moe.QUANT_MATRICES})
     dev = inp["x"].device
     out = torch.empty_like(inp["x"])
     aux = torch.empty(1, dtype=torch.float32, device=dev)

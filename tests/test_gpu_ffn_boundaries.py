@@ -9,8 +9,11 @@ average, panel up to 256, tiled beyond), so each case fixes T*k/E and then
 places the counts freely (rows past offsets[E] are unused).  Each case runs
 through moe_expert_ffn (with workspace: the tiled schedule may split its
 last round along K), through moe_expert_up + moe_expert_down without a
-workspace (never split) and with one (split as in moe_expert_ffn).  Outputs are compared by max |gpu - oracle| /
+workspace (never split) and with one (split as in moe_expert_ffn), with the
+weights row-major and in moe_tile_bf16's tiled order.  Outputs are compared by max |gpu - oracle| /
 max |oracle| over the computed rows (2e-2, bf16)."""
+
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -103,15 +106,20 @@ def _errors(y, ref, offsets, counts, rows):
     return err, worst
 
 
+@pytest.mark.parametrize("tiled", [False, True], ids=["rowmajor", "tiled"])
 @pytest.mark.parametrize("wl,counts", CASES, ids=[c[0].name for c in CASES])
-def test_expert_ffn_boundaries(wl, counts):
-    log(f"ffn boundaries {wl.name}: counts {counts}")
+def test_expert_ffn_boundaries(wl, counts, tiled):
+    log(f"ffn boundaries {wl.name} ({'tiled' if tiled else 'row-major'} "
+        f"weights): counts {counts}")
     inp = synth.make_inputs(wl, device="cuda")
     perm, offsets = _grouping(counts, wl.T, wl.top_k, wl.seed())
-    y = host(gpu_expert_ffn(inp, perm, offsets, wl)).astype(np.float64)
     ref = oracle.expert_ffn(host(inp["x"]), perm, offsets,
                             synth.oracle_weights(inp, wl), wl.act, wl.top_k,
                             n_shared=wl.n_shared)
+    if tiled:
+        wl = replace(wl, wquant="bf16_tiled")
+        inp = moe.tile_weights(inp)
+    y = host(gpu_expert_ffn(inp, perm, offsets, wl)).astype(np.float64)
     T, k = wl.T, wl.top_k
     rows = np.arange(offsets[-1])
     if wl.n_shared:
