@@ -22,10 +22,12 @@ namespace {
 
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float* f);
+// bf16 rows (x, the expert outputs) are each read once here: non-temporal
+// loads (the DeepSeek-V3 combine 131 -> 117 us)
 template <>
 __device__ __forceinline__ void load8<bf16>(const bf16* p, float* f) {
   V16 v;
-  v.u = ldg16(p);
+  v.u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 #pragma unroll
   for (int i = 0; i < 8; ++i) f[i] = (float)v.h[i];
 }
