@@ -1144,10 +1144,12 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
 // once.  A workgroup owns a panel of up to PN_BM rows of one group and 16*CG
 // weight rows per wave (256 per workgroup: SwiGLU 128 gate + the matching
 // 128 up rows, else 256 output columns), over the whole of K.  Each wave
-// streams its own weight rows from HBM straight into MFMA B registers
-// (16x16x32, PF-deep register ring, as in the stream schedule); the panel's
-// token rows (A) are read once per workgroup with ordinary loads, written to
-// a double-buffered, XOR-swizzled LDS slice and read by all eight waves.
+// streams its own weight rows from HBM into a register ring, in whole
+// 128-byte lines that a per-wave LDS slot reshuffles into 16x16x32 B
+// operand order (or, with tiled weights, as 1 KiB tiles already in that
+// order); the panel's token rows (A) are read once per workgroup with
+// ordinary loads, written to a double-buffered, XOR-swizzled LDS slice and
+// read by all eight waves.
 // Row tiles past the panel's rows issue no MFMAs and no loads, so a ragged
 // expert costs its own rows, not a full tile.  Every load is an ordinary
 // compiler-visible load, so the compiler's waits are exact: a wait for one
