@@ -12,9 +12,11 @@
 // each weight is split exactly into hi + mid + lo bf16 parts, so with bf16
 // x every product is exact in float32 and the three MFMAs accumulate a
 // float32-accurate dot product at matrix-core speed.  A float32 x is split
-// the same way (six part products).  Large T: 64 tokens x 64 experts per
-// workgroup; small T: the K dimension is split across workgroups and the
-// partial sums are added, in a fixed order, by kernel 2.
+// the same way (six part products).  64 tokens x 64 experts per
+// workgroup, the K dimension split over its four waves and, for small T,
+// across workgroups (the partial sums are added, in a fixed order, by
+// kernel 2).  Past 2048 bf16 tokens a wide variant takes 256 tokens per
+// workgroup and shares each split weight slice through LDS.
 //
 // Kernel 2 (route_select): one wave per token.  Sum the K-split partials,
 // add the router bias, softmax (max-subtracted), choose k experts by k
@@ -187,11 +189,140 @@ __global__ __launch_bounds__(RL_THREADS) void router_logits_kernel(
   }
 }
 
+// Large batches (bf16 x): 256 tokens x 64 experts per workgroup, the four
+// waves on 64 tokens each.  Each K step's 64 x 64 router-weight slice is
+// loaded once per workgroup (wave w loads expert tile w), split into its
+// three bf16 parts and kept in LDS in MFMA operand order for all four waves,
+// so the float32 weights cross L2 once per 256 tokens instead of once per 64.
+// Double-buffered LDS, one barrier per step; each wave loads the next step's
+// x and weights while it computes.  A wave adds its steps in order and
+// writes its own tokens' partial logits (no cross-wave reduction).
+constexpr int RLW_TT = 4;                            // 16-token tiles per wave
+constexpr int RLW_TOK = ROUTE_WAVES * RLW_TT * 16;   // tokens per workgroup
+constexpr int RLW_MAX_KSPLIT = 8;                    // K slices at most
+
+__global__ __launch_bounds__(RL_THREADS) void router_logits_wide_kernel(
+    const bf16* __restrict__ x, const float* __restrict__ wr,
+    float* __restrict__ part, int T, int d, int E, int ksplit) {
+  // [stage][expert tile][part * 2 + half][lane]
+  __shared__ u32x4 bs[2][4][6][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int row = lane & 15;
+  const int kq = lane >> 4;
+  const int t0 = blockIdx.x * RLW_TOK + wave * (RLW_TT * 16);
+  const int e0 = blockIdx.y * RL_EXP_TILE;
+  const int ks = blockIdx.z;
+  const int klen = d / ksplit;   // multiple of 64 (host checks)
+  const int kbeg = ks * klen;
+  const int nsteps = klen / RL_KSTEP;
+  const int ntile = min(4, (E - e0 + 15) >> 4);
+  const int ttok = max(0, min(RLW_TT, (T - t0 + 15) >> 4));   // this wave
+
+  const bf16* xr[RLW_TT];
+#pragma unroll
+  for (int i = 0; i < RLW_TT; ++i) {
+    const int t = min(t0 + 16 * i + row, T - 1);
+    xr[i] = x + (size_t)t * d + kbeg + kq * 16;
+  }
+  // this wave's expert tile of the weight slice (rows past E re-read the
+  // last expert; their parts are never used)
+  const bool wload = wave < ntile;
+  const float* wrow =
+      wr + (size_t)min(e0 + 16 * wave + row, E - 1) * d + kbeg + kq * 16;
+
+  f32x4 acc[RLW_TT][4];
+#pragma unroll
+  for (int i = 0; i < RLW_TT; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // raw operands of the next step: x as the two bf16x8 halves, weights as
+  // 16 floats
+  u32x4 xn[RLW_TT][2], wn[4];
+  auto fetch = [&](int s) {
+    const int k0 = s * RL_KSTEP;
+#pragma unroll
+    for (int i = 0; i < RLW_TT; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) xn[i][h] = ldg16(xr[i] + k0 + 8 * h);
+    if (wload) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wn[q] = ldg16(wrow + k0 + 4 * q);
+    }
+  };
+  if (nsteps > 0) fetch(0);
+  for (int s = 0; s < nsteps; ++s) {
+    const int st = s & 1;
+    V16 xc[RLW_TT][2];
+#pragma unroll
+    for (int i = 0; i < RLW_TT; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) xc[i][h].u = xn[i][h];
+    if (wload) {
+      // split the 16 weights into hi / mid / lo, two 8-wide halves each
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        V16 hi, mid, lo;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          V16 w;
+          w.u = wn[(8 * h + q) >> 2];
+          bf16 a, b, c;
+          split3(w.f[q & 3], a, b, c);
+          hi.h[q] = a;
+          mid.h[q] = b;
+          lo.h[q] = c;
+        }
+        bs[st][wave][0 + h][lane] = hi.u;
+        bs[st][wave][2 + h][lane] = mid.u;
+        bs[st][wave][4 + h][lane] = lo.u;
+      }
+    }
+    if (s + 1 < nsteps) fetch(s + 1);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j < ntile) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          V16 b[3];
+#pragma unroll
+          for (int pb = 0; pb < 3; ++pb) b[pb].u = bs[st][j][2 * pb + h][lane];
+#pragma unroll
+          for (int i = 0; i < RLW_TT; ++i) {
+            if (i < ttok) {
+              f32x4 c = acc[i][j];
+#pragma unroll
+              for (int pb = 0; pb < 3; ++pb)
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xc[i][h].h,
+                                                            b[pb].h, c, 0, 0, 0);
+              acc[i][j] = c;
+            }
+          }
+        }
+      }
+    }
+  }
+  // accumulator layout: lane holds expert 16j + (lane & 15) and tokens
+  // 16i + 4*(lane >> 4) + r
+#pragma unroll
+  for (int i = 0; i < RLW_TT; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + 16 * i + 4 * kq + r, e = e0 + 16 * j + row;
+        if (t < T && e < E) part[((size_t)ks * T + t) * E + e] = acc[i][j][r];
+      }
+}
+
 constexpr int RS_WAVES = ROUTE_WAVES;
 
 // MAXC experts per lane (E <= 64*MAXC), KSM = largest K split, PF: load the
 // next token's partial logits while the current token is processed (used
-// when a wave handles several tokens; the K split is then at most 2).
+// when a wave handles several tokens; the K split is then at most
+// RLW_MAX_KSPLIT).
 template <int MAXC, int KSM, bool PF>
 __global__ __launch_bounds__(RS_WAVES * 64) void route_select_kernel(
     const float* __restrict__ part, int ksplit,
@@ -209,28 +340,30 @@ __global__ __launch_bounds__(RS_WAVES * 64) void route_select_kernel(
 
   const int tbeg = (blockIdx.x * RS_WAVES + wave) * tpw;
   const int tend = min(tbeg + tpw, T);
-  constexpr int NB = PF ? 2 : 1;
-  float pv[NB][MAXC][KSM];
-  auto fetch = [&](int t, int buf) {
+  // pvn: the partial logits being fetched (the next token's with PF), pvc:
+  // the current token's (a copy taken at the top of each token, so every
+  // register index is a compile-time constant)
+  float pvn[MAXC][KSM], pvc[MAXC][KSM];
+  auto fetch = [&](int t) {
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
       const int e = lane + 64 * c;
 #pragma unroll
       for (int s = 0; s < KSM; ++s)
-        pv[buf][c][s] = (e < E && s < ksplit)
-                            ? part[((size_t)s * T + t) * E + e] : 0.f;
+        pvn[c][s] = (e < E && s < ksplit)
+                        ? part[((size_t)s * T + t) * E + e] : 0.f;
     }
   };
-  if (PF && tbeg < tend) fetch(tbeg, 0);
+  if (PF && tbeg < tend) fetch(tbeg);
   for (int i = 0; i < tpw; ++i) {
     const int t = tbeg + i;
     if (t >= tend) break;   // wave-uniform
-    const int cur = PF ? (i & 1) : 0;
-    if (PF) {
-      if (t + 1 < tend) fetch(t + 1, cur ^ 1);
-    } else {
-      fetch(t, 0);
-    }
+    if (!PF) fetch(t);
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c)
+#pragma unroll
+      for (int s = 0; s < KSM; ++s) pvc[c][s] = pvn[c][s];
+    if (PF && t + 1 < tend) fetch(t + 1);
     float l[MAXC], key[MAXC];
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
@@ -239,10 +372,10 @@ __global__ __launch_bounds__(RS_WAVES * 64) void route_select_kernel(
       key[c] = -INFINITY;
       if (e < E) {
         // K-slice partial sums added in slice order
-        float v = pv[cur][c][0];
+        float v = pvc[c][0];
 #pragma unroll
         for (int s = 1; s < KSM; ++s)
-          if (s < ksplit) v += pv[cur][c][s];
+          if (s < ksplit) v += pvc[c][s];
         if (router_bias) v += router_bias[e];
         l[c] = v;
         // sigmoid scores with a selection bias: the bias is on the score
@@ -400,18 +533,31 @@ __global__ __launch_bounds__(64 * PM_PARTS) void prob_mean_kernel(
 
 }  // namespace
 
+// Batches that take the wide router kernel: bf16 x past 2048 tokens (the
+// batches whose select waves handle several tokens each).
+static bool router_wide(int T, int dtype) { return dtype == 1 && route_tpw(T) > 1; }
+
 // Number of K slices for the router GEMM: each slice a whole number of
-// 64-wide steps (at least 4, one per wave), the largest split up to
-// ROUTER_MAX_KSPLIT that keeps the grid within about 1024 workgroups, so
-// that small batches and wide routers still fill the chip with independent
-// load chains.
+// 64-wide steps (at least 4), the largest split that keeps the grid within
+// about 1024 workgroups (wide kernel: 512 workgroups of 256 tokens, at most
+// RLW_MAX_KSPLIT slices), so that small batches and wide routers still fill
+// the chip with independent load chains.
 int router_ksplit(int T, int d, int E, int dtype) {
-  const int tt = dtype == 1 ? 64 : 16;
-  const long long blocks = (long long)((T + tt - 1) / tt) *
-                           ((E + RL_EXP_TILE - 1) / RL_EXP_TILE);
   const int steps = d / RL_KSTEP;
+  const long long etiles = (E + RL_EXP_TILE - 1) / RL_EXP_TILE;
+  if (router_wide(T, dtype)) {
+    const long long blocks = (long long)((T + RLW_TOK - 1) / RLW_TOK) * etiles;
+    int best = 1;
+    for (int ks = 2; ks <= RLW_MAX_KSPLIT; ks *= 2) {
+      if (steps % ks != 0 || steps / ks < 4 || blocks * ks > 512) break;
+      best = ks;
+    }
+    return best;
+  }
+  const int tt = dtype == 1 ? 64 : 16;
+  const long long blocks = (long long)((T + tt - 1) / tt) * etiles;
   // a wave of the select kernel that handles several tokens sums at most
-  // two slices per token
+  // RLW_MAX_KSPLIT slices per token; float32 x keeps two
   const int kmax = route_tpw(T) > 1 ? 2 : ROUTER_MAX_KSPLIT;
   int best = 1;
   for (int ks = 2; ks <= kmax; ++ks) {
@@ -426,7 +572,12 @@ hipError_t launch_router_logits_partial(int dtype, const void* x,
                                         const float* wr, float* part, int T,
                                         int d, int E, int ksplit,
                                         hipStream_t s) {
-  if (dtype == 1) {
+  if (router_wide(T, dtype)) {
+    dim3 grid((T + RLW_TOK - 1) / RLW_TOK, (E + RL_EXP_TILE - 1) / RL_EXP_TILE,
+              ksplit);
+    router_logits_wide_kernel<<<grid, RL_THREADS, 0, s>>>(
+        (const bf16*)x, wr, part, T, d, E, ksplit);
+  } else if (dtype == 1) {
     dim3 grid((T + 63) / 64, (E + RL_EXP_TILE - 1) / RL_EXP_TILE, ksplit);
     router_logits_kernel<bf16, 1, 4><<<grid, RL_THREADS, 0, s>>>(
         (const bf16*)x, wr, part, T, d, E, ksplit);
@@ -451,10 +602,10 @@ hipError_t launch_route_select_from(const float* part, int ksplit,
       part, ksplit, router_bias, select_bias, logits, idx, gate, partials, T, \
       E, k, tpw, scoring, raw)
   const int mc = (E + 63) / 64;
-  if (tpw > 1) {   // several tokens per wave: K split <= 2, prefetch
-    if (mc == 1) MOE_SELECT(1, 2, true);
-    else if (mc == 2) MOE_SELECT(2, 2, true);
-    else MOE_SELECT(4, 2, true);
+  if (tpw > 1) {   // several tokens per wave: K split <= 8, prefetch
+    if (mc == 1) MOE_SELECT(1, RLW_MAX_KSPLIT, true);
+    else if (mc == 2) MOE_SELECT(2, RLW_MAX_KSPLIT, true);
+    else MOE_SELECT(4, RLW_MAX_KSPLIT, true);
   } else {
     if (mc == 1) MOE_SELECT(1, ROUTER_MAX_KSPLIT, false);
     else if (mc == 2) MOE_SELECT(2, ROUTER_MAX_KSPLIT, false);
