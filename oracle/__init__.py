@@ -41,8 +41,4 @@ from .moe import (  # noqa: F401
     Q4_GROUP,
     quantize_int4,
     dequantize_int4,
-    pack_int4,
-    unpack_int4,
-    pack_qparams,
-    int4_bytes,
 )

@@ -206,41 +206,45 @@ def topk_margin(x, w_router, k, router_bias=None, select_bias=None,
 def dispatch(idx, E, cap):
     """Group assignments by expert under a per-expert capacity.
 
-    For each expert e, the (token, slot) pairs routed to it are listed in
-    ascending token order, the order a row-major nonzero of the [T, k]
-    mask yields in [RC] "How a sparse MoE layer works"; the first ``cap``
-    are kept and the rest are dropped (their MoE output is zero and the
-    residual carries the token: [LBS] "The Capacity Factor" and "Token
-    Dropping and Overflow Handling", zero-output strategy).  cap <= 0 means
-    no limit.
+    The rule ([RC] "How a sparse MoE layer works", the capacity check; [LBS]
+    "The Capacity Factor" and "Token Dropping and Overflow Handling",
+    zero-output strategy): an expert accepts the assignments routed to it in
+    ascending token order until it holds ``cap`` of them; the rest are
+    dropped (their MoE output is zero and the residual carries the token).
+    cap <= 0 means no limit.
+
+    Stated here as ranks: visiting the assignments a = t*k + j in ascending
+    a (so ascending token, a token's k experts being distinct), the rank of
+    a is the number of earlier assignments to the same expert; a is kept
+    iff its rank is below ``cap``.  Kept assignments of expert e occupy
+    rows offsets[e] + rank of the grouped batch, offsets being the
+    exclusive scan of the per-expert kept counts.
 
     Returns counts[E] (assignments routed, before the cut), kept[E],
-    offsets[E+1] (exclusive scan of kept), perm[offsets[E]] (assignment ids
-    t*k+j, grouped by expert, ascending token inside each group),
-    slot_of[T*k] (row of perm holding that assignment, -1 if dropped) and
+    offsets[E+1], perm[offsets[E]] (assignment id held by each grouped row),
+    slot_of[T*k] (grouped row of each assignment, -1 if dropped) and
     n_dropped.
     """
     idx = np.asarray(idx, np.int64)
     T, k = idx.shape
+    expert_of = idx.reshape(-1)
     counts = np.zeros(E, np.int64)
-    kept = np.zeros(E, np.int64)
-    perm = []
-    slot_of = np.full(T * k, -1, np.int64)
-    for e in range(E):
-        rows, slots = np.nonzero(idx == e)      # row-major: ascending t
-        counts[e] = rows.size
-        n_keep = rows.size if cap <= 0 else min(rows.size, cap)
-        kept[e] = n_keep
-        for t, j in zip(rows[:n_keep], slots[:n_keep]):
-            a = int(t) * k + int(j)
-            slot_of[a] = len(perm)
-            perm.append(a)
+    rank = np.zeros(T * k, np.int64)
+    for a in range(T * k):
+        e = int(expert_of[a])
+        rank[a] = counts[e]
+        counts[e] += 1
+    keep = rank >= 0 if cap <= 0 else rank < cap
+    kept = counts.copy() if cap <= 0 else np.minimum(counts, cap)
     offsets = np.zeros(E + 1, np.int64)
     offsets[1:] = np.cumsum(kept)
+    slot_of = np.full(T * k, -1, np.int64)
+    slot_of[keep] = offsets[expert_of[keep]] + rank[keep]
+    perm = np.zeros(int(offsets[E]), np.int64)
+    perm[slot_of[keep]] = np.nonzero(keep)[0]
     n_dropped = int(T * k - offsets[E])
     return {"counts": counts, "kept": kept, "offsets": offsets,
-            "perm": np.asarray(perm, np.int64), "slot_of": slot_of,
-            "n_dropped": n_dropped}
+            "perm": perm, "slot_of": slot_of, "n_dropped": n_dropped}
 
 
 # ---------------------------------------------------------------------------
@@ -601,62 +605,3 @@ def dequantize_int4(q, scale, offset):
     s = np.repeat(np.asarray(scale, F64), Q4_GROUP, axis=1)
     o = np.repeat(np.asarray(offset, F64), Q4_GROUP, axis=1)
     return o + q * s
-
-
-def pack_int4(q):
-    """Pack codes [rows, K] (rows a multiple of 16) into the library's
-    storage bytes, returned as [rows/16, K/128, 64, 16].
-
-    Storage is tiled for the GEMM's MFMA operand order (a storage format
-    of this library, not of the pages): one 1024-byte tile per 16 rows x
-    one group of 128 weights, tiles row-block-major then group; inside a
-    tile, 16-byte slot m = col + 16*kq holds row col's weights
-    kq*32 .. kq*32+31 of the group as four little-endian 32-bit words
-    (word h: weights kq*32 + 8h + 0..7).  In a word of eight consecutive
-    weights k0..k7, nibble i (bits 4i..4i+3) holds k_(2i) for i < 4 and
-    k_(2(i-4)+1) for i >= 4: even weights in the low half-word, odd
-    weights in the high half-word."""
-    q = np.asarray(q, np.uint32)
-    rows, K = q.shape
-    assert rows % 16 == 0 and K % Q4_GROUP == 0
-    # [row block, col, group, kq, h, 8 weights]
-    k8 = q.reshape(rows // 16, 16, K // Q4_GROUP, 4, 4, 8)
-    word = np.zeros(k8.shape[:-1], np.uint32)
-    for i in range(4):
-        word |= k8[..., 2 * i] << np.uint32(4 * i)
-        word |= k8[..., 2 * i + 1] << np.uint32(16 + 4 * i)
-    # -> [row block, group, kq, col, h]: slot m = col + 16*kq
-    tiles = word.transpose(0, 2, 3, 1, 4).reshape(rows // 16,
-                                                   K // Q4_GROUP, 64, 4)
-    return np.ascontiguousarray(tiles).astype("<u4").view(np.uint8)
-
-
-def unpack_int4(packed, rows, K):
-    """Inverse of :func:`pack_int4`: codes [rows, K] from the stored
-    bytes (any shape holding rows*K/2 bytes in storage order)."""
-    b = np.ascontiguousarray(np.asarray(packed, np.uint8)).reshape(-1)
-    word = b.view("<u4").reshape(rows // 16, K // Q4_GROUP, 4, 16, 4)
-    # [row block, group, kq, col, h] -> [row block, col, group, kq, h]
-    word = word.transpose(0, 3, 1, 2, 4)
-    q = np.zeros(word.shape + (8,), np.uint8)
-    for i in range(4):
-        q[..., 2 * i] = (word >> np.uint32(4 * i)) & 15
-        q[..., 2 * i + 1] = (word >> np.uint32(16 + 4 * i)) & 15
-    return q.reshape(rows, K)
-
-
-def pack_qparams(scale, offset):
-    """Store the per-group (scale, offset) pairs [rows, K/128] in the
-    library's tiled order [rows/16, K/128, 16, 2]: one 128-byte tile per
-    16 rows x one group, row col's pair at position col."""
-    s = np.asarray(scale, np.float32)
-    o = np.asarray(offset, np.float32)
-    rows, G = s.shape
-    st = np.stack([s, o], axis=-1).reshape(rows // 16, 16, G, 2)
-    return np.ascontiguousarray(st.transpose(0, 2, 1, 3))
-
-
-def int4_bytes(rows, K):
-    """Storage bytes of a [rows, K] matrix in this format: K/2 code bytes
-    per row plus a float32 scale and offset per group."""
-    return rows * (K // 2) + rows * (K // Q4_GROUP) * 8

@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 import torch
 
+import int4_format
 import oracle
 import sparse_mixture_experts_34_amd as moe
 from gpu_helpers import AUX_RTOL, TOL, gpu_layer, host, log, make, rel_inf
@@ -35,8 +36,8 @@ def oracle_quantize(w2d):
     """Stored code bytes and (scale, offset) floats, both flat, in the
     library's tiled order."""
     q, s, o = oracle.quantize_int4(w2d)
-    return (oracle.pack_int4(q).reshape(-1),
-            oracle.pack_qparams(s, o).reshape(-1))
+    return (int4_format.pack_int4(q).reshape(-1),
+            int4_format.pack_qparams(s, o).reshape(-1))
 
 
 def assert_same_quant(codes, qp, w_host):

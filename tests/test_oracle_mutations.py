@@ -6,6 +6,7 @@ import math
 import numpy as np
 import pytest
 
+import int4_format
 import oracle
 import oracle.moe as om
 import oracle_pins
@@ -219,7 +220,6 @@ def m_token_from_assignment_by_E(mp):
 _layer = om.layer_forward
 _quantize = om.quantize_int4
 _dequantize = om.dequantize_int4
-_pack = om.pack_int4
 
 
 def m_q4_floor(mp):
@@ -260,14 +260,15 @@ def m_q4_pack_untiled(mp):
             word |= k8[:, :, 2 * i] << np.uint32(4 * i)
             word |= k8[:, :, 2 * i + 1] << np.uint32(16 + 4 * i)
         return word.astype("<u4").view(np.uint8).reshape(rows, K // 2)
-    _patch(mp, "pack_int4", pack_int4)
+    # the format helper the GPU byte comparisons use
+    mp.setattr(int4_format, "pack_int4", pack_int4)
 
 
 def m_q4_qparams_row_major(mp):
     def pack_qparams(scale, offset):
         return np.stack([np.asarray(scale, np.float32),
                          np.asarray(offset, np.float32)], axis=-1)
-    _patch(mp, "pack_qparams", pack_qparams)
+    mp.setattr(int4_format, "pack_qparams", pack_qparams)
 
 
 def m_sigmoid_bias_on_logits(mp):
@@ -328,6 +329,37 @@ def m_reassign_gate_unnormalised(mp):
                lambda scores_t, orig_idx_t, e, renormalize: scores_t[e])
 
 
+def m_reassign_gate_new_normaliser(mp):
+    # normalised over the token's experts after the move instead of the
+    # experts it originally chose
+    _disp = om.dispatch_reassign
+
+    def dispatch_reassign(idx, scores, gate, E, cap, seed, renormalize=True):
+        r = _disp(idx, scores, gate, E, cap, seed, renormalize)
+        if renormalize:
+            sc = np.asarray(scores, np.float64)
+            moved = np.argwhere(r["idx"] != np.asarray(idx))
+            for t, j in moved:
+                r["gate"][t, j] = sc[t, r["idx"][t, j]] / \
+                    sc[t, r["idx"][t]].sum()
+        return r
+    _patch(mp, "dispatch_reassign", dispatch_reassign)
+
+
+def m_reassign_gate_softmax_under_sigmoid(mp):
+    # under sigmoid scoring, the moved slot weighted by the softmax
+    # probability of the new expert
+    _disp = om.dispatch_reassign
+
+    def dispatch_reassign(idx, scores, gate, E, cap, seed, renormalize=True):
+        sc = np.asarray(scores, np.float64)
+        if sc.size and not np.allclose(sc.sum(axis=1), 1.0):
+            with np.errstate(divide="ignore"):
+                sc = om.softmax(np.log(sc) - np.log1p(-sc))
+        return _disp(idx, sc, gate, E, cap, seed, renormalize)
+    _patch(mp, "dispatch_reassign", dispatch_reassign)
+
+
 def m_philox_swapped_products(mp):
     _ph = om.philox4x32
 
@@ -359,6 +391,8 @@ MUTATIONS = [m_no_renormalise, m_tie_to_higher_index, m_bias_in_gates,
              m_raw_gates_renormalised, m_sigmoid_probs_unnormalised,
              m_bias_update_wrong_sign, m_reassign_own_expert_allowed,
              m_reassign_uniform_over_experts, m_reassign_gate_unnormalised,
+             m_reassign_gate_new_normaliser,
+             m_reassign_gate_softmax_under_sigmoid,
              m_philox_swapped_products]
 
 
