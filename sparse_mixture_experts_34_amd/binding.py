@@ -123,6 +123,59 @@ def _ptr(t):
     return t.data_ptr()
 
 
+_F32, _I32T, _U8 = torch.float32, torch.int32, torch.uint8
+
+
+def _arg(t, dtype, name):
+    """Device pointer of a tensor argument after checking what the C side
+    cannot see: the tensor lives on a GPU, is contiguous and has the
+    element type the entry point reads.  ``None`` is NULL and a plain int
+    is taken as a raw device address (unchecked)."""
+    if t is None or isinstance(t, int):
+        return _ptr(t)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t)}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous (row-major)")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _ws(ws):
+    """(pointer, bytes) of a workspace tensor; it is counted in bytes, so
+    it must be uint8."""
+    if ws is None:
+        return None, 0
+    return _arg(ws, _U8, "ws"), ws.numel()
+
+
+def _act(p):
+    """torch dtype of the problem's activations, experts and outputs."""
+    return TORCH_DTYPE.get(p.dtype)
+
+
+def _weights(p, weights):
+    """The C weights struct, each tensor checked for device, contiguity and
+    the element type the problem's weight format implies."""
+    if isinstance(weights, moe_expert_weights):
+        return weights
+    act = _act(p)
+    mat = _U8 if p.wquant == MOE_WQUANT_INT4 else act
+    for n, t in weights.items():
+        if not isinstance(t, torch.Tensor):
+            continue
+        if n in QUANT_MATRICES:
+            _arg(t, mat, n)
+        elif n.endswith("_q") and n[:-2] in QUANT_MATRICES:
+            _arg(t, _F32, n)
+        elif n in ("b1", "b2", "shared_b1", "shared_b2"):
+            _arg(t, act, n)
+    return expert_weights(weights)
+
+
 def _stream(stream):
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -212,67 +265,86 @@ def workspace(p: moe_problem, device="cuda") -> torch.Tensor:
 
 def moe_route(p, x, w_router, router_bias, select_bias, logits, topk_idx,
               topk_gate, prob_mean, ws, stream=None):
-    _check(_lib.moe_route(ctypes.byref(p), _ptr(x), _ptr(w_router),
-                          _ptr(router_bias), _ptr(select_bias), _ptr(logits),
-                          _ptr(topk_idx), _ptr(topk_gate), _ptr(prob_mean),
-                          _ptr(ws), ws.numel() if ws is not None else 0,
+    wp, wn = _ws(ws)
+    _check(_lib.moe_route(ctypes.byref(p), _arg(x, _act(p), "x"),
+                          _arg(w_router, _F32, "w_router"),
+                          _arg(router_bias, _F32, "router_bias"),
+                          _arg(select_bias, _F32, "select_bias"),
+                          _arg(logits, _F32, "logits"),
+                          _arg(topk_idx, _I32T, "topk_idx"),
+                          _arg(topk_gate, _F32, "topk_gate"),
+                          _arg(prob_mean, _F32, "prob_mean"), wp, wn,
                           _stream(stream)), "moe_route")
 
 
 def moe_dispatch(p, topk_idx, prob_mean, counts, offsets, perm, slot_of,
                  n_dropped, aux_loss, ws, stream=None):
-    _check(_lib.moe_dispatch(ctypes.byref(p), _ptr(topk_idx),
-                             _ptr(prob_mean), _ptr(counts), _ptr(offsets),
-                             _ptr(perm), _ptr(slot_of), _ptr(n_dropped),
-                             _ptr(aux_loss), _ptr(ws),
-                             ws.numel() if ws is not None else 0,
+    wp, wn = _ws(ws)
+    _check(_lib.moe_dispatch(ctypes.byref(p),
+                             _arg(topk_idx, _I32T, "topk_idx"),
+                             _arg(prob_mean, _F32, "prob_mean"),
+                             _arg(counts, _I32T, "counts"),
+                             _arg(offsets, _I32T, "offsets"),
+                             _arg(perm, _I32T, "perm"),
+                             _arg(slot_of, _I32T, "slot_of"),
+                             _arg(n_dropped, _I32T, "n_dropped"),
+                             _arg(aux_loss, _F32, "aux_loss"), wp, wn,
                              _stream(stream)), "moe_dispatch")
 
 
 def moe_expert_ffn(p, x, perm, offsets, weights, y, ws, stream=None):
-    w = weights if isinstance(weights, moe_expert_weights) else \
-        expert_weights(weights)
-    _check(_lib.moe_expert_ffn(ctypes.byref(p), _ptr(x), _ptr(perm),
-                               _ptr(offsets), ctypes.byref(w), _ptr(y),
-                               _ptr(ws), ws.numel() if ws is not None else 0,
+    w = _weights(p, weights)
+    wp, wn = _ws(ws)
+    _check(_lib.moe_expert_ffn(ctypes.byref(p), _arg(x, _act(p), "x"),
+                               _arg(perm, _I32T, "perm"),
+                               _arg(offsets, _I32T, "offsets"),
+                               ctypes.byref(w), _arg(y, _act(p), "y"), wp, wn,
                                _stream(stream)), "moe_expert_ffn")
 
 
 def moe_expert_up(p, x, perm, offsets, weights, h, ws=None, stream=None):
-    w = weights if isinstance(weights, moe_expert_weights) else \
-        expert_weights(weights)
-    _check(_lib.moe_expert_up(ctypes.byref(p), _ptr(x), _ptr(perm),
-                              _ptr(offsets), ctypes.byref(w), _ptr(h),
-                              _ptr(ws), ws.numel() if ws is not None else 0,
+    w = _weights(p, weights)
+    wp, wn = _ws(ws)
+    _check(_lib.moe_expert_up(ctypes.byref(p), _arg(x, _act(p), "x"),
+                              _arg(perm, _I32T, "perm"),
+                              _arg(offsets, _I32T, "offsets"),
+                              ctypes.byref(w), _arg(h, _act(p), "h"), wp, wn,
                               _stream(stream)), "moe_expert_up")
 
 
 def moe_expert_down(p, h, offsets, weights, y, ws=None, stream=None):
-    w = weights if isinstance(weights, moe_expert_weights) else \
-        expert_weights(weights)
-    _check(_lib.moe_expert_down(ctypes.byref(p), _ptr(h), _ptr(offsets),
-                                ctypes.byref(w), _ptr(y), _ptr(ws),
-                                ws.numel() if ws is not None else 0,
-                                _stream(stream)), "moe_expert_down")
+    w = _weights(p, weights)
+    wp, wn = _ws(ws)
+    _check(_lib.moe_expert_down(ctypes.byref(p), _arg(h, _act(p), "h"),
+                                _arg(offsets, _I32T, "offsets"),
+                                ctypes.byref(w), _arg(y, _act(p), "y"), wp,
+                                wn, _stream(stream)), "moe_expert_down")
 
 
 def moe_combine(p, x_residual, y, slot_of, topk_gate, out, stream=None):
-    _check(_lib.moe_combine(ctypes.byref(p), _ptr(x_residual), _ptr(y),
-                            _ptr(slot_of), _ptr(topk_gate), _ptr(out),
+    _check(_lib.moe_combine(ctypes.byref(p),
+                            _arg(x_residual, _act(p), "x_residual"),
+                            _arg(y, _act(p), "y"),
+                            _arg(slot_of, _I32T, "slot_of"),
+                            _arg(topk_gate, _F32, "topk_gate"),
+                            _arg(out, _act(p), "out"),
                             _stream(stream)), "moe_combine")
 
 
 def moe_layer_forward(p, x, w_router, router_bias, select_bias, weights, out,
                       aux_loss, counts, n_dropped, topk_idx, ws,
                       stream=None):
-    w = weights if isinstance(weights, moe_expert_weights) else \
-        expert_weights(weights)
-    _check(_lib.moe_layer_forward(ctypes.byref(p), _ptr(x), _ptr(w_router),
-                                  _ptr(router_bias), _ptr(select_bias),
-                                  ctypes.byref(w), _ptr(out), _ptr(aux_loss),
-                                  _ptr(counts), _ptr(n_dropped),
-                                  _ptr(topk_idx), _ptr(ws),
-                                  ws.numel() if ws is not None else 0,
+    w = _weights(p, weights)
+    wp, wn = _ws(ws)
+    _check(_lib.moe_layer_forward(ctypes.byref(p), _arg(x, _act(p), "x"),
+                                  _arg(w_router, _F32, "w_router"),
+                                  _arg(router_bias, _F32, "router_bias"),
+                                  _arg(select_bias, _F32, "select_bias"),
+                                  ctypes.byref(w), _arg(out, _act(p), "out"),
+                                  _arg(aux_loss, _F32, "aux_loss"),
+                                  _arg(counts, _I32T, "counts"),
+                                  _arg(n_dropped, _I32T, "n_dropped"),
+                                  _arg(topk_idx, _I32T, "topk_idx"), wp, wn,
                                   _stream(stream)), "moe_layer_forward")
 
 
@@ -282,8 +354,10 @@ def moe_quantize_int4(w, codes, qparams, stream=None):
     float32 [..., K/128, 2]."""
     K = w.shape[-1]
     rows = w.numel() // K if K else 0
-    _check(_lib.moe_quantize_int4(_ptr(w), rows, K, _ptr(codes),
-                                  _ptr(qparams), _stream(stream)),
+    _check(_lib.moe_quantize_int4(_arg(w, torch.bfloat16, "w"), rows, K,
+                                  _arg(codes, _U8, "codes"),
+                                  _arg(qparams, _F32, "qparams"),
+                                  _stream(stream)),
            "moe_quantize_int4")
 
 
@@ -292,25 +366,31 @@ def moe_tile_bf16(w, out, stream=None):
     axis K) gets ``w`` in the GEMMs' tiled order."""
     K = w.shape[-1]
     rows = w.numel() // K if K else 0
-    _check(_lib.moe_tile_bf16(_ptr(w), rows, K, _ptr(out), _stream(stream)),
+    _check(_lib.moe_tile_bf16(_arg(w, torch.bfloat16, "w"), rows, K,
+                              _arg(out, torch.bfloat16, "out"),
+                              _stream(stream)),
            "moe_tile_bf16")
 
 
 def moe_dispatch_reassign(p, topk_idx, topk_gate, logits, prob_mean, counts,
                           offsets, perm, slot_of, n_dropped, aux_loss, ws,
                           stream=None):
+    wp, wn = _ws(ws)
     _check(_lib.moe_dispatch_reassign(
-        ctypes.byref(p), _ptr(topk_idx), _ptr(topk_gate), _ptr(logits),
-        _ptr(prob_mean), _ptr(counts), _ptr(offsets), _ptr(perm),
-        _ptr(slot_of), _ptr(n_dropped), _ptr(aux_loss), _ptr(ws),
-        ws.numel() if ws is not None else 0, _stream(stream)),
+        ctypes.byref(p), _arg(topk_idx, _I32T, "topk_idx"),
+        _arg(topk_gate, _F32, "topk_gate"), _arg(logits, _F32, "logits"),
+        _arg(prob_mean, _F32, "prob_mean"), _arg(counts, _I32T, "counts"),
+        _arg(offsets, _I32T, "offsets"), _arg(perm, _I32T, "perm"),
+        _arg(slot_of, _I32T, "slot_of"), _arg(n_dropped, _I32T, "n_dropped"),
+        _arg(aux_loss, _F32, "aux_loss"), wp, wn, _stream(stream)),
         "moe_dispatch_reassign")
 
 
 def moe_update_select_bias(p, counts, select_bias, gamma, stream=None):
-    _check(_lib.moe_update_select_bias(ctypes.byref(p), _ptr(counts),
-                                       _ptr(select_bias), gamma,
-                                       _stream(stream)),
+    _check(_lib.moe_update_select_bias(ctypes.byref(p),
+                                       _arg(counts, _I32T, "counts"),
+                                       _arg(select_bias, _F32, "select_bias"),
+                                       gamma, _stream(stream)),
            "moe_update_select_bias")
 
 

@@ -335,3 +335,16 @@ def test_status_strings():
     assert "unknown" in moe.moe_status_string(99)
     with pytest.raises(moe.MoEError):
         binding._check(moe.MOE_EINVAL, "x")
+
+
+def test_binding_rejects_host_tensors():
+    # the binding checks what the C side cannot see before any call: a
+    # host tensor where a device pointer is expected is refused
+    import torch
+    p = moe.problem(4, 64, 4, 2, 64, dtype="f32")
+    x = torch.zeros(4, 64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        moe.moe_combine(p, x, x, None, None, x)
+    with pytest.raises(TypeError, match="torch.Tensor"):
+        moe.moe_route(p, [0.0], None, None, None, None, None, None, None,
+                      None)

@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import oracle
+import sparse_mixture_experts_34_amd as moe
 from gpu_helpers import (AUX_RTOL, GATE_TOL, TOL, check_dispatch,
                          gpu_combine, gpu_dispatch, gpu_expert_ffn,
                          gpu_layer, gpu_route, host, log, make, oracle_layer,
@@ -223,3 +224,21 @@ def test_token_order_decides_drops():
     assert host(g["counts"]).tolist() == host(g2["counts"]).tolist()
     assert rel_inf(host(g2["out"]), o2["out"]) <= TOL["f32"]
     assert not np.array_equal(o["slot_of"] >= 0, o2["slot_of"] >= 0)
+
+
+def test_binding_rejects_strided_and_mistyped():
+    # a strided view or a wrong element type would reach the C ABI as a
+    # raw pointer and be read as something else; the binding refuses both
+    wl = synth.WORKLOADS["tiny_gelu_f32"]
+    p = moe.problem_for(wl)
+    x = torch.zeros(wl.T, 2 * wl.d_model, device="cuda")
+    y = torch.zeros(wl.T * wl.top_k, wl.d_model, device="cuda")
+    slot = torch.zeros(wl.T * wl.top_k, dtype=torch.int32, device="cuda")
+    gate = torch.zeros(wl.T, wl.top_k, device="cuda")
+    out = torch.zeros(wl.T, wl.d_model, device="cuda")
+    with pytest.raises(ValueError, match="contiguous"):
+        moe.moe_combine(p, x[:, ::2], y, slot, gate, out)
+    with pytest.raises(TypeError, match="int32"):
+        moe.moe_combine(p, out, y, slot.long(), gate, out)
+    with pytest.raises(TypeError, match="bfloat16"):
+        moe.moe_combine(p, out.bfloat16(), y, slot, gate, out)
