@@ -13,7 +13,11 @@ Prints one JSON line.  Besides the headline tokens/s it reports
                 launch stream in a second timed pass that runs the layer as
                 its separate C-ABI steps;
   layer_roofline the whole step against max(F / 2.5 PFLOP/s, B / 8 TB/s);
-  cpu_baseline  the CPU oracle timed on this host on a bounded sample.
+  cpu_baseline  the CPU oracle timed on this host on a bounded sample, with
+                the GPU output's error on the sampled tokens;
+  mixtral_prefill  (default decode run only) the same record for the
+                Mixtral-shaped prefill layer (T=8192), the MFMA-bound half of
+                the metric, timed after the decode layer.
 """
 
 from __future__ import annotations
@@ -51,6 +55,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixtral_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="with the default decode workload, skip the "
+                    "Mixtral-shaped prefill record (the MFMA-bound half)")
     ap.add_argument("--cpu-tokens", type=int, default=None)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the benchmark, run a plain device-to-device "
@@ -93,15 +100,46 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    import torch
+
+    from sparse_mixture_experts_34_amd import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    res, bf16_inp, gpu = measure(wl, args.steps, args.warmup, dev)
+    res = {"metric": METRIC, **res}
+    if args.workload == "mixtral_decode" and not args.no_prefill:
+        # the compute-bound half of the metric: the Mixtral-shaped prefill
+        # layer, timed the same way after the decode layer
+        pre, _, _ = measure(synth.WORKLOADS["mixtral_prefill"],
+                            min(args.steps, 20), min(args.warmup, 5), dev)
+        torch.cuda.empty_cache()
+        res["mixtral_prefill"] = {
+            n: pre[n] for n in ("value", "unit", "ms_per_step", "config",
+                                "roofline", "layer_roofline", "kernels_us",
+                                "step_ms_percentiles", "routing", "steps",
+                                "warmup")}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, bf16_inp, args.cpu_tokens,
+                                           gpu_idx=gpu["idx"],
+                                           gpu_out=gpu["out"])
+    print(json.dumps(res), flush=True)
+    if args.copy_calibration_mib > 0:
+        copy_calibration(args.copy_calibration_mib)
+
+
+def measure(wl, steps, warmup, dev):
+    """Time one workload: K whole-layer steps (the headline), then the same
+    layer as its separate C-ABI steps with HIP events on the launch stream
+    (per-kernel durations, dominant-kernel roofline).  Returns the record,
+    the bf16 inputs and the GPU's routing and output of the last step."""
     import numpy as np
     import torch
 
     import sparse_mixture_experts_34_amd as moe
     from sparse_mixture_experts_34_amd import synth
 
-    wl = synth.WORKLOADS[args.workload]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     inp = synth.make_inputs(wl, device=dev)
     p = moe.problem_for(wl)
     ws = moe.workspace(p, dev)
@@ -145,18 +183,18 @@ def main():
             ev[1].record()
 
     # ---- headline pass: K whole-layer calls ------------------------------
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     torch.cuda.synchronize()
-    t_step = (time.perf_counter() - t0) / args.steps
+    t_step = (time.perf_counter() - t0) / steps
     # per-step spread: a second pass with HIP events around every call
     sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-           for _ in range(args.steps)]
-    for i in range(args.steps):
+           for _ in range(steps)]
+    for i in range(steps):
         step(i, sev[i])
     torch.cuda.synchronize()
     st = np.array([e[0].elapsed_time(e[1]) for e in sev])
@@ -203,15 +241,15 @@ def main():
         ev[5].record()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)]
-           for _ in range(args.steps)]
-    for i in range(args.warmup):
+           for _ in range(steps)]
+    for i in range(warmup):
         step_parts(evs[0], i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step_parts(evs[i], i)
     torch.cuda.synchronize()
-    t_parts = (time.perf_counter() - t0) / args.steps
+    t_parts = (time.perf_counter() - t0) / steps
     per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
            * 1e-3 for j, n in enumerate(names)}
     same = bool(torch.equal(out, out2))
@@ -264,12 +302,11 @@ def main():
     drop_frac = n_dropped / max(T * k, 1)
 
     res = {
-        "metric": METRIC,
         "value": round(T / t_step, 3),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(t_step * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -300,18 +337,15 @@ def main():
         "weight_copies": 2,
         "parts_match_layer_output": same,
         "routing": {"counts": cnt, "touched_experts": touched - wl.n_shared,
+                    "kept_assignments": kept_total,
                     "n_dropped": n_dropped,
                     "drop_fraction": round(drop_frac, 5),
                     "within_20pct_of_uniform": healthy,
                     "drop_alert_over_2pct": drop_frac > 0.02,
                     "aux_loss": float(aux.item())},
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, bf16_inp, args.cpu_tokens,
-                                           gpu_idx=idx.cpu().numpy())
-    print(json.dumps(res), flush=True)
-    if args.copy_calibration_mib > 0:
-        copy_calibration(args.copy_calibration_mib)
+    gpu = {"idx": idx.cpu().numpy(), "out": out.float().cpu().numpy()}
+    return res, bf16_inp, gpu
 
 
 def copy_calibration(mib):
@@ -330,12 +364,15 @@ def kept_total_rows(kept_total, wl):
     return kept_total + wl.n_shared * wl.T
 
 
-def cpu_baseline(wl, inp, n_tokens=None, gpu_idx=None):
+def cpu_baseline(wl, inp, n_tokens=None, gpu_idx=None, gpu_out=None):
     """The CPU oracle (float64, numpy/OpenBLAS) on a bounded sample: routing
     and capacity dispatch over the whole batch plus the expert FFNs and
     combine of a token sample.  Weights are copied to host memory before
     the clock starts.  With ``gpu_idx``, also counts the tokens whose
-    selected experts differ from the oracle's (expected 0)."""
+    selected experts differ from the oracle's (expected 0); with
+    ``gpu_out`` (the GPU layer's output, host array), reports its error on
+    the sampled tokens: max |gpu - oracle| / max |oracle| of the output and
+    of its MoE part (output minus residual)."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info
@@ -384,18 +421,29 @@ def cpu_baseline(wl, inp, n_tokens=None, gpu_idx=None):
         if nme.startswith("shared_"):
             w[nme] = prep(hx(inp[nme]), nme)
     t0 = time.perf_counter()
-    oracle.layer_forward(x, wr, w, k=wl.top_k, cap=wl.capacity, act=wl.act,
-                         n_shared=wl.n_shared, alpha=wl.aux_coef,
-                         router_bias=rb, select_bias=sb, tokens=tokens,
-                         scoring=wl.scoring, renormalize=renorm,
-                         reassign_seed=reseed)
+    o = oracle.layer_forward(x, wr, w, k=wl.top_k, cap=wl.capacity,
+                             act=wl.act, n_shared=wl.n_shared,
+                             alpha=wl.aux_coef, router_bias=rb,
+                             select_bias=sb, tokens=tokens,
+                             scoring=wl.scoring, renormalize=renorm,
+                             reassign_seed=reseed)
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()
                    if i.get("internal_api") in ("openblas", "mkl", "blis")]
                   or [1])
-    return {"value": round(n / dt, 4), "unit": "tokens/s", "cores": threads,
+    errs = {}
+    if gpu_out is not None:
+        def rel(a, b):
+            den = np.abs(b).max()
+            return float(np.abs(a - b).max() / den) if den else 0.0
+        g = np.asarray(gpu_out, np.float64)[tokens]
+        xs = np.asarray(x, np.float64)[tokens]
+        errs = {"out_rel_err_vs_gpu": rel(g, o["out"]),
+                "moe_delta_rel_err_vs_gpu": rel(g - xs, o["out"] - xs)}
+    return {"value": round(n / dt, 4), "unit": "tokens/s",
+            "cores": len(os.sched_getaffinity(0)), "blas_threads": threads,
             "kind": "oracle", "seconds": round(dt, 3),
-            "routing_flips_vs_gpu": flips,
+            "routing_flips_vs_gpu": flips, **errs,
             "sample": ("4-bit weights quantised and dequantised by the oracle "
                        "before timing; " if q4 else "") +
                       f"{n} of {wl.T} tokens: float64 routing + capacity "
