@@ -37,8 +37,9 @@
  * - Each call validates all its arguments on the host first; a non-zero
  *   status means nothing was enqueued.  MOE_OK means the work was enqueued
  *   on `stream`; results are valid when the stream reaches that point.
- * - The library holds no mutable global state; calls are reentrant.  Two
- *   calls that share an output or workspace buffer must not overlap.
+ * - The library holds no mutable global state, except the scratch of
+ *   moe_layer_forward_noalloc (below); calls are reentrant.  Two calls that
+ *   share an output or workspace buffer must not overlap.
  * - Element types: `x`, expert weights and biases, `y` and `out` all have
  *   the problem's dtype (MOE_DTYPE_F32 or MOE_DTYPE_BF16).  Router weights,
  *   router/selection biases, logits, gates and probabilities are float32
@@ -87,6 +88,8 @@ extern "C" {
 
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOP_K 8
+/* scratch bytes per GPU of moe_layer_forward_noalloc (32 MiB) */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /*
  * Problem description.
@@ -366,6 +369,37 @@ int32_t moe_layer_forward(const moe_problem* p, const void* x,
                           float* aux_loss, int32_t* counts,
                           int32_t* n_dropped, int32_t* topk_idx, void* ws,
                           size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_layer_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, outputs and results as moe_layer_forward,
+ * without the workspace: the intermediates live in a scratch area of
+ * MOE_NOALLOC_SCRATCH_BYTES that the library's code object holds on each
+ * GPU it runs on, from the first call on that GPU until the process ends.
+ * The call itself allocates nothing (no hipMalloc, no allocating library
+ * routine); the first call on a GPU looks up the scratch's device address.
+ *   Limit: the problem's intermediates must fit the scratch, which holds
+ *   decode-sized batches (about 450 tokens of the Mixtral-shaped layer:
+ *   k * (d_ff + d_model) * 2 bytes per token for H and Y, plus small
+ *   routing buffers); beyond it the call returns MOE_EWORKSPACE and
+ *   enqueues nothing.  The tiled expert GEMMs never split their last round
+ *   along K here (no room is kept for the partial tiles); results agree with
+ *   moe_layer_forward up to the float32 summation order of those tiles and
+ *   are bit-identical wherever no tile is split.
+ *   Concurrency: every call on a GPU uses that GPU's one scratch area, and
+ *   each call leaves its intermediates there; calls that overlap on one GPU
+ *   (on different streams, or from different threads without ordering)
+ *   race and give undefined results.  Calls on one stream are ordered.
+ */
+int32_t moe_layer_forward_noalloc(const moe_problem* p, const void* x,
+                                  const float* w_router,
+                                  const float* router_bias,
+                                  const float* select_bias,
+                                  const moe_expert_weights* w, void* out,
+                                  float* aux_loss, int32_t* counts,
+                                  int32_t* n_dropped, int32_t* topk_idx,
+                                  hipStream_t stream);
 
 /*
  * Group-wise 4-bit round-to-nearest quantisation of a bf16 weight matrix

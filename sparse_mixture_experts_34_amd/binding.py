@@ -32,6 +32,7 @@ MOE_OVERFLOW_DROP, MOE_OVERFLOW_REASSIGN = 0, 1
 OVERFLOW = {"drop": MOE_OVERFLOW_DROP, "reassign": MOE_OVERFLOW_REASSIGN}
 SCORING = {"softmax": MOE_SCORING_SOFTMAX, "sigmoid": MOE_SCORING_SIGMOID}
 MOE_Q4_GROUP = 128
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 WQUANT = {None: MOE_WQUANT_NONE, "none": MOE_WQUANT_NONE,
           "int4": MOE_WQUANT_INT4, "bf16_tiled": MOE_WQUANT_BF16_TILED}
 ACT = {"gelu": MOE_ACT_GELU, "swiglu": MOE_ACT_SWIGLU}
@@ -81,6 +82,8 @@ _SIGS = {
     "moe_combine": (_I32, [_P, _V, _V, _V, _V, _V, _V]),
     "moe_layer_forward": (_I32, [_P, _V, _V, _V, _V, _W, _V, _V, _V, _V, _V,
                                  _V, _SZ, _V]),
+    "moe_layer_forward_noalloc": (_I32, [_P, _V, _V, _V, _V, _W, _V, _V, _V,
+                                         _V, _V, _V]),
     "moe_quantize_int4": (_I32, [_V, ctypes.c_int64, _I32, _V, _V, _V]),
     "moe_tile_bf16": (_I32, [_V, ctypes.c_int64, _I32, _V, _V]),
     "moe_update_select_bias": (_I32, [_P, _V, _V, ctypes.c_float, _V]),
@@ -346,6 +349,21 @@ def moe_layer_forward(p, x, w_router, router_bias, select_bias, weights, out,
                                   _arg(n_dropped, _I32T, "n_dropped"),
                                   _arg(topk_idx, _I32T, "topk_idx"), wp, wn,
                                   _stream(stream)), "moe_layer_forward")
+
+
+def moe_layer_forward_noalloc(p, x, w_router, router_bias, select_bias,
+                              weights, out, aux_loss, counts, n_dropped,
+                              topk_idx, stream=None):
+    w = _weights(p, weights)
+    _check(_lib.moe_layer_forward_noalloc(
+        ctypes.byref(p), _arg(x, _act(p), "x"),
+        _arg(w_router, _F32, "w_router"),
+        _arg(router_bias, _F32, "router_bias"),
+        _arg(select_bias, _F32, "select_bias"), ctypes.byref(w),
+        _arg(out, _act(p), "out"), _arg(aux_loss, _F32, "aux_loss"),
+        _arg(counts, _I32T, "counts"), _arg(n_dropped, _I32T, "n_dropped"),
+        _arg(topk_idx, _I32T, "topk_idx"), _stream(stream)),
+        "moe_layer_forward_noalloc")
 
 
 def moe_quantize_int4(w, codes, qparams, stream=None):

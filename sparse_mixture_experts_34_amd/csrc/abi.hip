@@ -4,6 +4,10 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
+#include <hip/hip_runtime.h>
+
 #include "../../include/moe.h"
 #include "kernels.hpp"
 
@@ -29,7 +33,9 @@ struct Layout {
   int split_cpx;   // CUs per XCD the split area holds (0: none)
 };
 
-Layout make_layout(const moe_problem& p) {
+// split: whether the tiled expert GEMMs get the K-split area (the no-alloc
+// entry point's layout has none; its tiled GEMMs then never split).
+Layout make_layout(const moe_problem& p, bool split = true) {
   Layout L;
   const long long T = p.T, E = p.n_experts, k = p.top_k;
   const long long rows = T * k + (long long)p.n_shared * T;
@@ -66,7 +72,7 @@ Layout make_layout(const moe_problem& p) {
   // tiled expert GEMMs (bf16 weights): one partial tile and one counter
   // per CU for the K-split last round
   const int sched = ffn_schedule(p.dtype, p.T, p.top_k, p.n_experts);
-  L.split_cpx = (p.wquant != MOE_WQUANT_INT4 && sched == 1)
+  L.split_cpx = (split && p.wquant != MOE_WQUANT_INT4 && sched == 1)
                     ? device_cus() / 8 : 0;
   L.split_part = take((size_t)8 * L.split_cpx * SPLIT_TILE_FLOATS * 4);
   L.split_cnt = take((size_t)8 * L.split_cpx * 4);
@@ -207,6 +213,131 @@ void with_split(FfnArgs& a, const Layout& L, char* ws) {
 
 }  // namespace
 
+namespace {
+
+ReassignArgs reassign_args(const moe_problem* p, int32_t* idx, float* gate,
+                           const float* logits, const int32_t* off0,
+                           int32_t* offsets, int32_t* perm, int32_t* slot_of,
+                           int32_t* n_dropped, int32_t* rslot,
+                           int32_t* newe) {
+  ReassignArgs r;
+  r.idx = idx;
+  r.gate = gate;
+  r.logits = logits;
+  r.off0 = off0;
+  r.offsets = offsets;
+  r.perm = perm;
+  r.slot_of = slot_of;
+  r.n_dropped = n_dropped;
+  r.rslot = rslot;
+  r.newe = newe;
+  r.T = p->T;
+  r.E = p->n_experts;
+  r.k = p->top_k;
+  r.capacity = p->capacity;
+  r.scoring = p->scoring;
+  r.raw = p->raw_gates;
+  r.key0 = (uint32_t)(p->overflow_seed & 0xFFFFFFFFu);
+  r.key1 = (uint32_t)(p->overflow_seed >> 32);
+  return r;
+}
+
+// Scratch of moe_layer_forward_noalloc: the workspace of that entry point,
+// a device global of the library's code object, so each GPU the library
+// runs on holds its own copy until the process ends.  Host code never
+// uses the name as an address (on the host it is only a stand-in for the
+// symbol); the device address comes from hipGetSymbolAddress, looked up
+// once per device with that device current, and is what kernels receive.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[MAX_DEVICES];   // scratch's address on each device
+
+int32_t scratch_of_current_device(char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_EHIP;
+  if (dev < 0 || dev >= MAX_DEVICES) return MOE_ENOTSUP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+      return MOE_EHIP;
+    g_scratch_ptr[dev] = (char*)ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+// Steps 1-5 of the layer, enqueued with the workspace wsb laid out as L.
+// Arguments are validated by the callers.
+int32_t layer_forward_in(const moe_problem* p, const void* x,
+                         const float* w_router, const float* router_bias,
+                         const float* select_bias,
+                         const moe_expert_weights* w, void* out,
+                         float* aux_loss, int32_t* counts, int32_t* n_dropped,
+                         int32_t* topk_idx, char* wsb, const Layout& L,
+                         hipStream_t stream) {
+  if (p->T == 0) {
+    if (aux_loss) MOE_TRY(launch_fill_zero32(aux_loss, 1, stream));
+    if (counts) MOE_TRY(launch_fill_zero32(counts, p->n_experts, stream));
+    if (n_dropped) MOE_TRY(launch_fill_zero32(n_dropped, 1, stream));
+    return MOE_OK;
+  }
+  int32_t* idx = topk_idx ? topk_idx : (int32_t*)(wsb + L.idx);
+  float* gate = (float*)(wsb + L.gate);
+  float* part = (float*)(wsb + L.part);
+  float* rpart = (float*)(wsb + L.rpart);
+  MOE_TRY(launch_router_logits_partial(p->dtype, x, w_router, part, p->T,
+                                       p->d_model, p->n_experts, L.ksplit,
+                                       stream));
+  const bool reassign =
+      p->overflow == MOE_OVERFLOW_REASSIGN && p->capacity > 0;
+  float* logits = reassign ? (float*)(wsb + L.logits) : nullptr;
+  MOE_TRY(launch_route_select_from(part, L.ksplit, router_bias, select_bias,
+                                   logits, idx, gate, rpart, p->T,
+                                   p->n_experts, p->top_k, p->scoring,
+                                   p->raw_gates, stream));
+  DispatchArgs a;
+  a.idx = idx;
+  a.prob_mean_in = nullptr;
+  a.partials = rpart;
+  a.n_partials = L.nrb;
+  a.prob_mean_out = (float*)(wsb + L.pmean);
+  a.counts = counts ? counts : (int32_t*)(wsb + L.counts);
+  a.offsets = (int32_t*)(wsb + L.offsets);
+  a.perm = (int32_t*)(wsb + L.perm);
+  a.slot_of = (int32_t*)(wsb + L.slot);
+  a.n_dropped = n_dropped ? n_dropped : (int32_t*)(wsb + L.ndrop);
+  a.aux = aux_loss ? aux_loss : (float*)(wsb + L.aux);
+  a.chunk_ws = (int32_t*)(wsb + L.chunk);
+  a.T = p->T;
+  a.E = p->n_experts;
+  a.k = p->top_k;
+  a.capacity = p->capacity;
+  a.aux_coef = p->aux_coef;
+  if (reassign) a.offsets = (int32_t*)(wsb + L.off0);
+  MOE_TRY(launch_dispatch(a, stream));
+  if (reassign) {
+    a.offsets = (int32_t*)(wsb + L.offsets);
+    MOE_TRY(launch_reassign(
+        reassign_args(p, idx, gate, logits, (int32_t*)(wsb + L.off0),
+                      a.offsets, a.perm, a.slot_of, a.n_dropped,
+                      (int32_t*)(wsb + L.rslot), (int32_t*)(wsb + L.newe)),
+        stream));
+  }
+  void* y = wsb + L.y;
+  FfnArgs f = ffn_args(p, x, a.perm, a.offsets, w, wsb + L.h, y);
+  with_split(f, L, wsb);
+  MOE_TRY(launch_expert_up(f, stream));
+  MOE_TRY(launch_expert_down(f, stream));
+  MOE_TRY(launch_combine(p->dtype, x, y, a.slot_of, gate, out, p->T,
+                         p->d_model, p->top_k, p->n_shared, stream));
+  return MOE_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t moe_capacity(int32_t T, int32_t top_k, int32_t n_experts,
@@ -298,34 +429,6 @@ int32_t moe_dispatch(const moe_problem* p, const int32_t* topk_idx,
   return status_of(launch_dispatch(a, stream));
 }
 
-namespace {
-ReassignArgs reassign_args(const moe_problem* p, int32_t* idx, float* gate,
-                           const float* logits, const int32_t* off0,
-                           int32_t* offsets, int32_t* perm, int32_t* slot_of,
-                           int32_t* n_dropped, int32_t* rslot,
-                           int32_t* newe) {
-  ReassignArgs r;
-  r.idx = idx;
-  r.gate = gate;
-  r.logits = logits;
-  r.off0 = off0;
-  r.offsets = offsets;
-  r.perm = perm;
-  r.slot_of = slot_of;
-  r.n_dropped = n_dropped;
-  r.rslot = rslot;
-  r.newe = newe;
-  r.T = p->T;
-  r.E = p->n_experts;
-  r.k = p->top_k;
-  r.capacity = p->capacity;
-  r.scoring = p->scoring;
-  r.raw = p->raw_gates;
-  r.key0 = (uint32_t)(p->overflow_seed & 0xFFFFFFFFu);
-  r.key1 = (uint32_t)(p->overflow_seed >> 32);
-  return r;
-}
-}  // namespace
 
 int32_t moe_dispatch_reassign(const moe_problem* p, int32_t* topk_idx,
                               float* topk_gate, const float* logits,
@@ -452,64 +555,30 @@ int32_t moe_layer_forward(const moe_problem* p, const void* x,
   if ((st = check_weights(p, w))) return st;
   if (p->T > 0 && (!x || !w_router || !out)) return MOE_EINVAL;
   if ((st = check_ws(p, ws, ws_bytes))) return st;
-  if (p->T == 0) {
-    if (aux_loss) MOE_TRY(launch_fill_zero32(aux_loss, 1, stream));
-    if (counts) MOE_TRY(launch_fill_zero32(counts, p->n_experts, stream));
-    if (n_dropped) MOE_TRY(launch_fill_zero32(n_dropped, 1, stream));
-    return MOE_OK;
-  }
-  const Layout L = make_layout(*p);
-  char* wsb = (char*)ws;
-  int32_t* idx = topk_idx ? topk_idx : (int32_t*)(wsb + L.idx);
-  float* gate = (float*)(wsb + L.gate);
-  float* part = (float*)(wsb + L.part);
-  float* rpart = (float*)(wsb + L.rpart);
-  MOE_TRY(launch_router_logits_partial(p->dtype, x, w_router, part, p->T,
-                                       p->d_model, p->n_experts, L.ksplit,
-                                       stream));
-  const bool reassign =
-      p->overflow == MOE_OVERFLOW_REASSIGN && p->capacity > 0;
-  float* logits = reassign ? (float*)(wsb + L.logits) : nullptr;
-  MOE_TRY(launch_route_select_from(part, L.ksplit, router_bias, select_bias,
-                                   logits, idx, gate, rpart, p->T,
-                                   p->n_experts, p->top_k, p->scoring,
-                                   p->raw_gates, stream));
-  DispatchArgs a;
-  a.idx = idx;
-  a.prob_mean_in = nullptr;
-  a.partials = rpart;
-  a.n_partials = L.nrb;
-  a.prob_mean_out = (float*)(wsb + L.pmean);
-  a.counts = counts ? counts : (int32_t*)(wsb + L.counts);
-  a.offsets = (int32_t*)(wsb + L.offsets);
-  a.perm = (int32_t*)(wsb + L.perm);
-  a.slot_of = (int32_t*)(wsb + L.slot);
-  a.n_dropped = n_dropped ? n_dropped : (int32_t*)(wsb + L.ndrop);
-  a.aux = aux_loss ? aux_loss : (float*)(wsb + L.aux);
-  a.chunk_ws = (int32_t*)(wsb + L.chunk);
-  a.T = p->T;
-  a.E = p->n_experts;
-  a.k = p->top_k;
-  a.capacity = p->capacity;
-  a.aux_coef = p->aux_coef;
-  if (reassign) a.offsets = (int32_t*)(wsb + L.off0);
-  MOE_TRY(launch_dispatch(a, stream));
-  if (reassign) {
-    a.offsets = (int32_t*)(wsb + L.offsets);
-    MOE_TRY(launch_reassign(
-        reassign_args(p, idx, gate, logits, (int32_t*)(wsb + L.off0),
-                      a.offsets, a.perm, a.slot_of, a.n_dropped,
-                      (int32_t*)(wsb + L.rslot), (int32_t*)(wsb + L.newe)),
-        stream));
-  }
-  void* y = wsb + L.y;
-  FfnArgs f = ffn_args(p, x, a.perm, a.offsets, w, wsb + L.h, y);
-  with_split(f, L, wsb);
-  MOE_TRY(launch_expert_up(f, stream));
-  MOE_TRY(launch_expert_down(f, stream));
-  MOE_TRY(launch_combine(p->dtype, x, y, a.slot_of, gate, out, p->T,
-                         p->d_model, p->top_k, p->n_shared, stream));
-  return MOE_OK;
+  return layer_forward_in(p, x, w_router, router_bias, select_bias, w, out,
+                          aux_loss, counts, n_dropped, topk_idx, (char*)ws,
+                          make_layout(*p), stream);
+}
+
+int32_t moe_layer_forward_noalloc(const moe_problem* p, const void* x,
+                                  const float* w_router,
+                                  const float* router_bias,
+                                  const float* select_bias,
+                                  const moe_expert_weights* w, void* out,
+                                  float* aux_loss, int32_t* counts,
+                                  int32_t* n_dropped, int32_t* topk_idx,
+                                  hipStream_t stream) {
+  int32_t st = check_problem(p);
+  if (st) return st;
+  if ((st = check_weights(p, w))) return st;
+  if (p->T > 0 && (!x || !w_router || !out)) return MOE_EINVAL;
+  const Layout L = make_layout(*p, false);
+  if (L.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_EWORKSPACE;
+  char* sp = nullptr;
+  if ((st = scratch_of_current_device(&sp))) return st;
+  return layer_forward_in(p, x, w_router, router_bias, select_bias, w, out,
+                          aux_loss, counts, n_dropped, topk_idx, sp, L,
+                          stream);
 }
 
 int32_t moe_quantize_int4(const void* w, int64_t rows, int32_t K,

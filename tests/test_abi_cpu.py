@@ -131,6 +131,9 @@ def test_bad_problem_rejected_by_every_entry(kw, code):
     assert lib.moe_layer_forward(p, fake, fake, None, None, ctypes.byref(w),
                                  fake, None, None, None, None, fake, 1 << 40,
                                  None) == code
+    assert lib.moe_layer_forward_noalloc(p, fake, fake, None, None,
+                                         ctypes.byref(w), fake, None, None,
+                                         None, None, None) == code
 
 
 def test_null_problem_and_pointers():
@@ -348,3 +351,26 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(TypeError, match="torch.Tensor"):
         moe.moe_route(p, [0.0], None, None, None, None, None, None, None,
                       None)
+
+
+def test_noalloc_scratch_limit():
+    # a problem whose intermediates exceed the per-GPU scratch is refused on
+    # the host, before any device call; one that fits passes validation
+    lib = binding._lib
+    f = 0x1000
+    W = binding.moe_expert_weights
+    w = W(f, f, f, None, None)
+    big = _prob(T=1024, d_model=4096, d_ff=14336, n_experts=8, top_k=2)
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(big), f, f, None, None,
+                                         ctypes.byref(w), f, None, None,
+                                         None, None, None) == \
+        moe.MOE_EWORKSPACE
+    n = ctypes.c_size_t(0)
+    small = _prob(T=400, d_model=4096, d_ff=14336, n_experts=8, top_k=2)
+    assert lib.moe_workspace_bytes(ctypes.byref(small), ctypes.byref(n)) == 0
+    assert n.value <= moe.MOE_NOALLOC_SCRATCH_BYTES
+    # missing x / router / out
+    assert lib.moe_layer_forward_noalloc(ctypes.byref(small), None, f, None,
+                                         None, ctypes.byref(w), f, None,
+                                         None, None, None, None) == \
+        moe.MOE_EINVAL
