@@ -276,9 +276,12 @@ int32_t moe_dispatch(const moe_problem* p, const int32_t* topk_idx,
  *   prob_mean, counts, offsets, perm, slot_of, n_dropped, aux_loss: as in
  *              moe_dispatch (counts and aux from the routing decisions
  *              before the cut and before reassignment).
- * The draws are sequential in a (each takes a free slot), so this step
- * runs in one wave per call; it costs about one microsecond per hundred
- * overflow assignments.
+ * The draws are sequential in a (each takes a free slot).  With one slot
+ * per token (k = 1, at most 16384 possible draws, 65536 slots and 512
+ * experts) every draw finds a slot while slots last, and the whole sequence
+ * is decoded in parallel in one 1024-thread workgroup (about 2.2 us per
+ * hundred drops on the Switch-shaped layer: 0.30 ms for 13721); otherwise
+ * one wave walks the drops in order (about 10 us per hundred).
  */
 int32_t moe_dispatch_reassign(const moe_problem* p, int32_t* topk_idx,
                               float* topk_gate, const float* logits,

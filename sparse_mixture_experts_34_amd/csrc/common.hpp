@@ -64,9 +64,12 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* f) {
   return r;
 }
 
-// Split a float into three bf16 parts with v == hi + mid + lo up to the
-// last bit or two of v's 24-bit significand; each difference below is exact
-// in float32, so products of the parts with a bf16 value are exact.
+// Split a float into three bf16 parts with v == hi + mid + lo exactly for
+// every float with 2^-100 <= |v| < 2^120 (each part takes the next 8 bits of
+// the 24-bit significand, the rounding residue moving its sign into the next
+// part; outside that range the last part can underflow bf16 or hi can round
+// to infinity); each difference below is exact in float32, so products of
+// the parts with a bf16 value are exact.
 __device__ __forceinline__ void split3(float v, bf16& hi, bf16& mid, bf16& lo) {
   hi = (bf16)v;
   float r1 = v - (float)hi;
