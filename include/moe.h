@@ -99,8 +99,10 @@ extern "C" {
  *   top_k      experts per token k, 1..min(E, 8).
  *   d_ff       expert intermediate size, a positive multiple of 64.
  *              Size limits (MOE_ENOTSUP beyond them): d_model * d_ff <
- *              2^32, and (T*top_k + (n_shared+1)*T) * max(d_model, d_ff)
- *              < 2^32 (the GEMMs use 32-bit element offsets).
+ *              2^32, (T*top_k + (n_shared+1)*T) * max(d_model, d_ff)
+ *              < 2^32 (the GEMMs use 32-bit element offsets; it also
+ *              keeps x under 2^32 bytes for the 32-bit byte offsets its
+ *              rows are gathered with).
  *   n_shared   always-on shared experts, 0 or 1 ([GN] DeepSeek-V3).
  *   capacity   per-expert cap on kept assignments; <= 0 means no cap.
  *   act        MOE_ACT_GELU or MOE_ACT_SWIGLU.

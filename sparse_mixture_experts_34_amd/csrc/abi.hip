@@ -115,6 +115,8 @@ int32_t check_problem(const moe_problem* p) {
   if ((rows + p->T) * wide >= (1LL << 32) ||
       (long long)p->d_model * p->d_ff >= (1LL << 32))
     return MOE_ENOTSUP;
+  // (this also keeps x under 2^32 bytes, 2*T*d <= (T*k + T)*d, so the
+  // 256-row GEMM tiles can gather its rows with 32-bit byte offsets)
   return MOE_OK;
 }
 

@@ -39,6 +39,8 @@
 // also come in tiled order (wquant 2, moe_tile_bf16: 1 KiB tiles of 16 rows
 // x 32 columns in 16x16x32 operand order); every bf16 schedule has a
 // variant (template flag TW) that loads those tiles as they are.
+#include <utility>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -723,23 +725,38 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
 // 16 bytes per lane from global memory straight into LDS: lane l's bytes land
-// at lds_base + 16*l (lds_base must be the same for the whole wave).  The
-// instruction has no destination registers.  It is written as inline asm so
-// that the compiler does not track it: its own waitcnt analysis would
-// otherwise make every later LDS read wait for all loads in flight.  The
-// kernel orders these loads itself with s_waitcnt vmcnt at each slice
-// barrier; a compiler-generated vmcnt wait can only wait longer (vector
-// loads complete in order).
-__device__ __forceinline__ void dma16(const void* src, bf16* lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(lds_void_t*)lds_base);   // wave-uniform
+// at the wave's LDS address + 16*l.  The instruction has no destination
+// registers.  It is written as inline asm so that the compiler does not
+// track it: its own waitcnt analysis would otherwise make every later LDS
+// read wait for all loads in flight.  The kernel orders these loads itself
+// with s_waitcnt vmcnt at each slice barrier; a compiler-generated vmcnt
+// wait can only wait longer (vector loads complete in order).
+// The load uses a wave-uniform 64-bit base in scalar registers and a 32-bit
+// per-lane byte offset (the scalar-base addressing form): one vector
+// register per load instead of a 64-bit address, and no 64-bit vector add.
+// The wave's 64 x 16 bytes land at LDS byte address lds + IMM (lds
+// uniform; IMM a constant folded into the m0 write, so that the compiler
+// does not keep one register per load for the LDS addresses).  The scalar
+// add writes SCC, which the clobber list declares.
+template <int IMM>
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff,
+                                       uint32_t lds) {
   asm volatile(
-      "s_mov_b32 m0, %1\n\t"
+      "s_add_u32 m0, %2, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
+      "global_load_lds_dwordx4 %0, %1"
       :
-      : "v"(src), "s"(m0)
-      : "memory", "m0");
+      : "v"(voff), "s"(sbase), "s"(lds), "n"(IMM)
+      : "memory", "m0", "scc");
+}
+
+// dma16s for loads I... of a wave: load i from sbase(i) at offset voff[i]
+// into LDS lds + i * STRIDE.
+template <int STRIDE, typename SB, int... I>
+__device__ __forceinline__ void dma16s_seq(SB sbase, const uint32_t* voff,
+                                           uint32_t lds,
+                                           std::integer_sequence<int, I...>) {
+  (dma16s<I * STRIDE>(sbase(I), voff[I], lds), ...);
 }
 
 // End of a K slice: wait until at most N of this wave's vector-memory loads
@@ -834,9 +851,16 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
   const int G = a.E + a.n_shared;
   const int Kd = MODE == DOWN ? a.d_ff : a.d;
   if (!find_tile_split<TL_THREADS>(a, G, BM, NB, Kd / BK, s_info)) return;
-  const int g = s_info[0], r0 = s_info[1], nb = s_info[2];
-  const int kb = s_info[3], ke = s_info[4], item = s_info[5];
-  const Group gr = group_of(g, a.offsets, a.E, a.T, a.k);
+  // tile parameters are workgroup-uniform: keep them in scalar registers
+  const int g = __builtin_amdgcn_readfirstlane(s_info[0]);
+  const int r0 = __builtin_amdgcn_readfirstlane(s_info[1]);
+  const int nb = __builtin_amdgcn_readfirstlane(s_info[2]);
+  const int kb = __builtin_amdgcn_readfirstlane(s_info[3]);
+  const int ke = __builtin_amdgcn_readfirstlane(s_info[4]);
+  const int item = __builtin_amdgcn_readfirstlane(s_info[5]);
+  Group gr = group_of(g, a.offsets, a.E, a.T, a.k);
+  gr.out0 = __builtin_amdgcn_readfirstlane(gr.out0);
+  gr.rows = __builtin_amdgcn_readfirstlane(gr.rows);
   const int N = MODE == DOWN ? a.d : a.d_ff;
   const int K = MODE == DOWN ? a.d_ff : a.d;
   const int ncols = MODE == UP_SWIGLU ? TL_BN / 2 : TL_BN;   // outputs per tile
@@ -845,74 +869,101 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
   group_weights<MODE>(a, g, gr.shared, N, K, w0v, w1v, biasv);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
   const int l31 = lane & 31, q = lane >> 5;
 
   // Loads: wave w fills A rows [w*IA*RPI, (w+1)*IA*RPI) and B rows likewise,
   // RPI rows per instruction; lane l covers row RPI*i + l/CPR, LDS position
-  // l%CPR, i.e. global chunk (l%CPR) ^ key(row).  32-bit element offsets.
+  // l%CPR, i.e. global chunk (l%CPR) ^ key(row).  Each load instruction has
+  // a wave-uniform base (scalar registers) and a 32-bit per-lane byte
+  // offset: A of the up GEMMs is based at x (token rows gathered through
+  // perm, T*d*2 < 2^32 bytes), A of the down GEMM at the tile's first row of
+  // H, B at the tile's first weight row (or first tile row block).
   const int lr = lane / Geo::CPR;
   const int lp = lane % Geo::CPR;
-  const bf16* abase_g = (const bf16*)(MODE == DOWN ? a.h : a.x);
+  const char* abase = MODE == DOWN
+      ? (const char*)a.h + (size_t)(gr.out0 + r0) * K * 2
+      : (const char*)a.x;
   uint32_t ao[IA];
 #pragma unroll
   for (int i = 0; i < IA; ++i) {
     const int row = (wave * IA + i) * Geo::RPI + lr;
     const int ai = min(r0 + row, gr.rows - 1);
-    const int arow_g = MODE == DOWN ? gr.out0 + ai
-                                    : (gr.shared ? ai : a.perm[gr.out0 + ai] / a.k);
-    ao[i] = (uint32_t)arow_g * (uint32_t)K + ((lp ^ Geo::key(row)) << 3);
+    const int arow = MODE == DOWN ? ai - r0
+                                  : (gr.shared ? ai : a.perm[gr.out0 + ai] / a.k);
+    ao[i] = (uint32_t)arow * ((uint32_t)K * 2u) + ((lp ^ Geo::key(row)) << 4);
   }
   // B rows: SwiGLU block b = r >> 6 holds gate cols [32b, 32b+32) in rows
   // [64b, 64b+32) and the matching up cols in [64b+32, 64b+64), so wave
-  // column wn's two N-tiles are a gate tile and its up tile.
+  // column wn's two N-tiles are a gate tile and its up tile.  An instruction's
+  // 8 (or, tiled, 16) rows lie in one of them: its matrix is uniform, and
+  // the two matrices' bases (at the tile's first weight row, or first tile
+  // row block) are the only B bases.
+  const size_t bskip = TW ? (size_t)(nbase >> 4) * (K / 32) * 512
+                          : (size_t)nbase * K;
+  const char* bm0 = (const char*)((const bf16*)w0v + bskip);
+  const char* bm1 = MODE == UP_SWIGLU
+      ? (const char*)((const bf16*)w1v + bskip) : bm0;
   uint32_t bo[IB];
-  const bf16* bb[IB];
+  bool bup[IB];   // load i reads the up matrix (SwiGLU), uniform
 #pragma unroll
   for (int i = 0; i < IB; ++i) {
-    const int row = (wave * IB + i) * Geo::RPI + lr;
+    const int row0 = (wave * IB + i) * Geo::RPI;   // first row, uniform
+    const int row = row0 + lr;
     int wrow;
     if (MODE == UP_SWIGLU) {
-      bb[i] = (const bf16*)(((row >> 5) & 1) ? w1v : w0v);
+      bup[i] = ((row0 >> 5) & 1) != 0;
       wrow = nbase + 32 * (row >> 6) + (row & 31);
     } else {
-      bb[i] = (const bf16*)w0v;
+      bup[i] = false;
       wrow = nbase + row;
     }
     wrow = min(wrow, N - 1);
-    bo[i] = (uint32_t)wrow * (uint32_t)K + ((lp ^ Geo::key(row)) << 3);
+    bo[i] = (uint32_t)(wrow - nbase) * ((uint32_t)K * 2u) +
+            ((lp ^ Geo::key(row)) << 4);
     if constexpr (TW) {
       // instruction ii = wave * IB + i loads tile (row block ii / 2 of the
       // slice's B rows, column block ii % 2): weight row block of LDS rows
       // 16 * (ii / 2) .. +15 (SwiGLU: gate or up rows, as above)
       const int ii = wave * IB + i;
-      const int r0 = 16 * (ii >> 1);
+      const int t0 = 16 * (ii >> 1);
       int wr0;
       if (MODE == UP_SWIGLU) {
-        bb[i] = (const bf16*)(((r0 >> 5) & 1) ? w1v : w0v);
-        wr0 = nbase + 32 * (r0 >> 6) + (r0 & 31);
+        bup[i] = ((t0 >> 5) & 1) != 0;
+        wr0 = nbase + 32 * (t0 >> 6) + (t0 & 31);
       } else {
-        bb[i] = (const bf16*)w0v;
-        wr0 = nbase + r0;
+        wr0 = nbase + t0;
       }
       const int rbg = min(wr0 >> 4, N / 16 - 1);
-      bo[i] = ((uint32_t)rbg * (uint32_t)(K / 32) + (uint32_t)(ii & 1)) * 512u +
-              (uint32_t)(lane * 8);
+      bo[i] = ((uint32_t)(rbg - (nbase >> 4)) * (uint32_t)(K / 32) +
+               (uint32_t)(ii & 1)) * 1024u + (uint32_t)(lane * 16);
     }
   }
-  auto issue = [&](int kt, bf16* Ad, bf16* Bd) {
-    const int k0 = (kb + kt) * BK;
-#pragma unroll
-    for (int i = 0; i < IA; ++i)
-      dma16(abase_g + ao[i] + k0, Ad + (wave * IA + i) * Geo::RPI * BK);
-#pragma unroll
-    for (int i = 0; i < IB; ++i) {
-      if constexpr (TW)
-        dma16(bb[i] + bo[i] + (size_t)(kb + kt) * 1024, Bd + (wave * IB + i) * 512);
-      else
-        dma16(bb[i] + bo[i] + k0, Bd + (wave * IB + i) * Geo::RPI * BK);
-    }
+  // LDS byte addresses of the stages (link-time constants) and of this
+  // wave's first load in a stage
+  auto lds_of = [](const bf16* p) -> uint32_t {
+    return (uint32_t)(uintptr_t)(lds_void_t*)p;
+  };
+  const uint32_t a_lds[6] = {lds_of(A0), lds_of(A1), lds_of(A2),
+                             lds_of(A3), lds_of(A4), lds_of(A5)};
+  const uint32_t b_lds[6] = {lds_of(B0), lds_of(B1), lds_of(B2),
+                             lds_of(B3), lds_of(B4), lds_of(B5)};
+  constexpr int ASTR = Geo::RPI * BK * 2;            // LDS bytes per A load
+  constexpr int BSTR = TW ? 1024 : Geo::RPI * BK * 2;
+  const uint32_t a_w = (uint32_t)(wave * IA * ASTR);
+  const uint32_t b_w = (uint32_t)(wave * IB * BSTR);
+  auto issue = [&](int kt, int st) {
+    const size_t ka = (size_t)(kb + kt) * BK * 2;            // bytes along K
+    const size_t kw = TW ? (size_t)(kb + kt) * 2048 : ka;    // weight bytes
+    const char* ak = abase + ka;
+    const char* b0k = bm0 + kw;
+    const char* b1k = bm1 + kw;
+    dma16s_seq<ASTR>([&](int) { return ak; }, ao, a_lds[st] + a_w,
+                     std::make_integer_sequence<int, IA>());
+    dma16s_seq<BSTR>([&](int i) { return bup[i] ? b1k : b0k; }, bo,
+                     b_lds[st] + b_w, std::make_integer_sequence<int, IB>());
   };
 
   f32x16 acc[MT][NT];
@@ -994,7 +1045,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
   // Prologue: slices 0..D-1 in flight (clamped to the last slice when the
   // piece is shorter), then wait for slice 0.
 #pragma unroll
-  for (int s = 0; s < D; ++s) issue(min(s, nk - 1), As(s), Bs(s));
+  for (int s = 0; s < D; ++s) issue(min(s, nk - 1), s);
   slice_barrier<(D - 1) * PER>();
   // Main loop, NS slices per trip with constant stage indices.  Slice k
   // reads stage k % NS; before it, slice k + D is issued into stage
@@ -1010,7 +1061,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
     for (int u = 0; u < NS; ++u) {
       const int k = kt + u;
       if (k < nk) {
-        issue(min(k + D, nk - 1), As((u + D) % NS), Bs((u + D) % NS));
+        issue(min(k + D, nk - 1), (u + D) % NS);
         compute_deferred(As(u), Bs(u));
         slice_barrier<(D - 1) * PER>();
       }
