@@ -41,7 +41,7 @@ Layout make_layout(const moe_problem& p, bool split = true) {
   const long long rows = T * k + (long long)p.n_shared * T;
   const size_t esz = p.dtype == MOE_DTYPE_BF16 ? 2 : 4;
   L.ksplit = router_ksplit(p.T, p.d_model, p.n_experts, p.dtype);
-  L.nrb = route_blocks(p.T);
+  L.nrb = route_partial_rows(p.T, p.n_experts);
   L.nchunks = dispatch_chunks(T * k);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -157,6 +157,29 @@ int32_t check_weights(const moe_problem* p, const moe_expert_weights* w) {
 }
 
 int32_t status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+// Step 1 for T > 0: the fused kernel for small batches with few experts,
+// otherwise the router GEMM (K-split partial logits in `part`) and the
+// select kernel.  Writes rpart, the route_partial_rows(T, E) rows of
+// probability partials.
+hipError_t route_on(const moe_problem* p, const void* x, const float* w_router,
+                    const float* router_bias, const float* select_bias,
+                    float* logits, int32_t* idx, float* gate, float* part,
+                    float* rpart, int ksplit, hipStream_t stream) {
+  if (route_fused(p->T, p->n_experts))
+    return launch_route_fused(p->dtype, x, w_router, router_bias,
+                              select_bias, logits, idx, gate, rpart, p->T,
+                              p->d_model, p->n_experts, p->top_k, p->scoring,
+                              p->raw_gates, stream);
+  hipError_t e = launch_router_logits_partial(p->dtype, x, w_router, part,
+                                              p->T, p->d_model, p->n_experts,
+                                              ksplit, stream);
+  if (e != hipSuccess) return e;
+  return launch_route_select_from(part, ksplit, router_bias, select_bias,
+                                  logits, idx, gate, rpart, p->T,
+                                  p->n_experts, p->top_k, p->scoring,
+                                  p->raw_gates, stream);
+}
 
 #define MOE_TRY(expr)                                    \
   do {                                                   \
@@ -290,16 +313,11 @@ int32_t layer_forward_in(const moe_problem* p, const void* x,
   float* gate = (float*)(wsb + L.gate);
   float* part = (float*)(wsb + L.part);
   float* rpart = (float*)(wsb + L.rpart);
-  MOE_TRY(launch_router_logits_partial(p->dtype, x, w_router, part, p->T,
-                                       p->d_model, p->n_experts, L.ksplit,
-                                       stream));
   const bool reassign =
       p->overflow == MOE_OVERFLOW_REASSIGN && p->capacity > 0;
   float* logits = reassign ? (float*)(wsb + L.logits) : nullptr;
-  MOE_TRY(launch_route_select_from(part, L.ksplit, router_bias, select_bias,
-                                   logits, idx, gate, rpart, p->T,
-                                   p->n_experts, p->top_k, p->scoring,
-                                   p->raw_gates, stream));
+  MOE_TRY(route_on(p, x, w_router, router_bias, select_bias, logits, idx,
+                   gate, part, rpart, L.ksplit, stream));
   DispatchArgs a;
   a.idx = idx;
   a.prob_mean_in = nullptr;
@@ -377,13 +395,8 @@ int32_t moe_route(const moe_problem* p, const void* x, const float* w_router,
   char* w = (char*)ws;
   float* part = (float*)(w + L.part);
   float* rpart = (float*)(w + L.rpart);
-  MOE_TRY(launch_router_logits_partial(p->dtype, x, w_router, part, p->T,
-                                       p->d_model, p->n_experts, L.ksplit,
-                                       stream));
-  MOE_TRY(launch_route_select_from(part, L.ksplit, router_bias, select_bias,
-                                   logits, topk_idx, topk_gate, rpart, p->T,
-                                   p->n_experts, p->top_k, p->scoring,
-                                   p->raw_gates, stream));
+  MOE_TRY(route_on(p, x, w_router, router_bias, select_bias, logits,
+                   topk_idx, topk_gate, part, rpart, L.ksplit, stream));
   MOE_TRY(launch_prob_mean(rpart, prob_mean, L.nrb, p->T, p->n_experts,
                            stream));
   return MOE_OK;

@@ -245,6 +245,68 @@ __global__ __launch_bounds__(DW * 64) void dispatch_scatter_kernel(
                 lane);
 }
 
+// Decode-sized batches (at most 64 assignments and 64 experts): the whole
+// dispatch in one wave, with no workgroup barrier.  Lane a holds assignment
+// a (token a / k, slot a % k) and, as an expert, lane e; one ballot per
+// expert gives its count and every assignment's rank among its expert's in
+// ascending a (= ascending token); kept counts are scanned across lanes;
+// an assignment is kept iff its rank is below the capacity, at row
+// offsets[e] + rank.  The probability partial rows are added in row order
+// per expert, the aux terms by the fixed DPP butterfly of wave_sum.  An
+// expert index outside [0, E) is neither counted nor kept.
+__global__ __launch_bounds__(64) void dispatch_wave_kernel(DispatchArgs a) {
+  const int lane = threadIdx.x;
+  const int tk = a.T * a.k;
+  const int E = a.E;
+  int my_e = lane < tk ? a.idx[lane] : -1;
+  if (my_e >= E) my_e = -1;
+  int cnt = 0, rank = 0;
+  for (int e = 0; e < E; ++e) {
+    const uint64_t m = __ballot(my_e == e);
+    if (lane == e) cnt = __popcll(m);
+    if (my_e == e) rank = __popcll(m & ((1ull << lane) - 1ull));
+  }
+  const int kept = lane < E ? (a.capacity > 0 ? min(cnt, a.capacity) : cnt) : 0;
+  int incl = kept;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  const int excl = incl - kept;
+  const int total = __shfl(incl, 63, 64);
+  if (lane < E) {
+    a.counts[lane] = cnt;
+    a.offsets[lane] = excl;
+  }
+  if (lane == 0) {
+    a.offsets[E] = total;
+    *a.n_dropped = tk - total;
+  }
+  const int base = __shfl(excl, my_e < 0 ? 0 : my_e, 64);
+  if (lane < tk) {
+    const bool keep = my_e >= 0 && (a.capacity <= 0 || rank < a.capacity);
+    const int slot = keep ? base + rank : -1;
+    a.slot_of[lane] = slot;
+    if (keep) a.perm[slot] = lane;
+    if (lane >= total) a.perm[lane] = -1;
+  }
+  // probability means and the aux loss
+  float pm = 0.f;
+  if (lane < E) {
+    if (a.partials) {
+      float v = 0.f;
+      for (int r = 0; r < a.n_partials; ++r) v += a.partials[(size_t)r * E + lane];
+      pm = v / (float)a.T;
+      if (a.prob_mean_out) a.prob_mean_out[lane] = pm;
+    } else {
+      pm = a.prob_mean_in ? a.prob_mean_in[lane] : 0.f;
+    }
+  }
+  const float term = wave_sum(lane < E ? ((float)cnt / (float)a.T) * pm : 0.f);
+  if (lane == 0 && a.aux) *a.aux = a.aux_coef * (float)E * term;
+}
+
 // Everything in one workgroup when there are at most DW chunks.
 __global__ __launch_bounds__(256) void dispatch_small_kernel(DispatchArgs a,
                                                              int nchunks) {
@@ -823,6 +885,10 @@ __global__ void fill_zero32_kernel(uint32_t* p, long long n) {
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   const long long tk = (long long)a.T * a.k;
   const int nchunks = dispatch_chunks(tk);
+  if (tk <= 64 && a.E <= 64) {
+    dispatch_wave_kernel<<<1, 64, 0, s>>>(a);
+    return hipGetLastError();
+  }
   if (nchunks <= DW) {
     dispatch_small_kernel<<<1, 256, 0, s>>>(a, nchunks);
     return hipGetLastError();

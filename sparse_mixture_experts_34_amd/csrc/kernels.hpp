@@ -49,6 +49,18 @@ hipError_t launch_route_select_from(const float* part, int ksplit,
                                     int32_t* idx, float* gate,
                                     float* partials, int T, int E, int k,
                                     int scoring, int raw, hipStream_t s);
+// Small batches with few experts (decode) take one fused kernel: router
+// linear, scores, top-k, gates and one row of probability partials per
+// token.  route_partial_rows: rows of partials the route step writes
+// (T fused, route_blocks(T) otherwise).
+bool route_fused(int T, int E);
+int route_partial_rows(int T, int E);
+hipError_t launch_route_fused(int dtype, const void* x, const float* wr,
+                              const float* router_bias,
+                              const float* select_bias, float* logits,
+                              int32_t* idx, float* gate, float* partials,
+                              int T, int d, int E, int k, int scoring,
+                              int raw, hipStream_t s);
 // select_bias[e] += gamma * sign(mean count - counts[e]).
 hipError_t launch_update_select_bias(const int32_t* counts, float* bias,
                                      float gamma, int E, hipStream_t s);

@@ -317,6 +317,136 @@ __global__ __launch_bounds__(RL_THREADS) void router_logits_wide_kernel(
       }
 }
 
+// One token's choice from its float32 logits l (router bias included; lane
+// holds experts lane + 64c, -inf past E): the selection keys (the logit, or
+// with a selection bias the logit or sigmoid score plus the bias), the
+// scores (softmax, or per-expert sigmoid), k rounds of wave argmax on (key,
+// index) with equal keys going to the lower index, and the gates; lane j < k
+// writes slot j of token t.  Adds the token's scores scaled to sum to 1 to
+// psum (the aux loss's P).  Whole wave.
+template <int MAXC>
+__device__ __forceinline__ void select_token(
+    const float (&l)[MAXC], int t, int lane, const float* __restrict__ select_bias,
+    int32_t* __restrict__ idx_out, float* __restrict__ gate_out,
+    float (&psum)[MAXC], int E, int k, int scoring, int raw) {
+  float key[MAXC];
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int e = lane + 64 * c;
+    // sigmoid scores with a selection bias: the bias is on the score scale;
+    // otherwise the logit orders the choice
+    key[c] = e >= E ? -INFINITY
+             : select_bias ? (scoring ? sigmoid_f(l[c]) : l[c]) + select_bias[e]
+                           : l[c];
+  }
+  // per-token scores: softmax probs, or sigmoid scores; P accumulates
+  // the scores scaled to sum to 1
+  float m = -INFINITY, inv;
+  float ex[MAXC], se = 0.f;
+  if (!scoring) {
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) m = fmaxf(m, l[c]);
+    m = wave_max(m);
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const int e = lane + 64 * c;
+      ex[c] = (e < E) ? __expf(l[c] - m) : 0.f;
+      se += ex[c];
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const int e = lane + 64 * c;
+      ex[c] = (e < E) ? sigmoid_f(l[c]) : 0.f;
+      se += ex[c];
+    }
+  }
+  se = wave_sum(se);
+  inv = 1.0f / se;
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) psum[c] += ex[c] * inv;
+
+  // k rounds of wave argmax on (key desc, index asc); lane j keeps the
+  // winner of round j (slot j) and its logit.
+  bool taken[MAXC];
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) taken[c] = (lane + 64 * c) >= E;
+  int my_idx = 0;
+  float my_l = -INFINITY;
+  for (int j = 0; j < k; ++j) {
+    float bk = -INFINITY, bl = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      // indices rise with c: strict > keeps the lower index on ties
+      if (!taken[c] && (bi == 0x7fffffff || key[c] > bk)) {
+        bk = key[c];
+        bi = lane + 64 * c;
+        bl = l[c];
+      }
+    }
+    // wave argmax on (key desc, index asc): a total order, so the DPP
+    // steps of the wave reductions give the same winner in any order
+    auto take = [&](float ok, int oi, float ol) {
+      const bool better = (oi != 0x7fffffff) &&
+                          (bi == 0x7fffffff || ok > bk || (ok == bk && oi < bi));
+      if (better) {
+        bk = ok;
+        bi = oi;
+        bl = ol;
+      }
+    };
+#define MOE_ARGMAX_STEP(CTRL, RM)                                       \
+    take(dpp_f<CTRL, RM>(bk, bk), dpp_i<CTRL, RM>(bi, bi),           \
+         dpp_f<CTRL, RM>(bl, bl))
+    MOE_ARGMAX_STEP(DPP_QUAD_1032, 0xf);
+    MOE_ARGMAX_STEP(DPP_QUAD_2301, 0xf);
+    MOE_ARGMAX_STEP(DPP_ROW_HALF_MIRROR, 0xf);
+    MOE_ARGMAX_STEP(DPP_ROW_MIRROR, 0xf);
+    MOE_ARGMAX_STEP(DPP_ROW_BCAST15, 0xa);
+    MOE_ARGMAX_STEP(DPP_ROW_BCAST31, 0xc);
+#undef MOE_ARGMAX_STEP
+    bk = lane63(bk);
+    bi = __builtin_amdgcn_readlane(bi, 63);
+    bl = lane63(bl);
+    // every lane now holds the same winner
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c)
+      if (lane + 64 * c == bi) taken[c] = true;
+    if (lane == j) {
+      my_idx = bi;
+      my_l = bl;
+    }
+  }
+  // gates.  Softmax, renormalised: chosen probabilities over their sum,
+  // i.e. a softmax over the chosen logits (the shared normaliser
+  // cancels).  Softmax, raw: the chosen probability.  Sigmoid: the chosen
+  // score, over the chosen scores' sum when renormalised.
+  float g;
+  if (!scoring) {
+    if (!raw) {
+      const float mc = wave_max(lane < k ? my_l : -INFINITY);
+      const float ej = lane < k ? __expf(my_l - mc) : 0.f;
+      const float sj = wave_sum(ej);
+      g = ej / sj;
+    } else {
+      g = __expf(my_l - m) * inv;
+    }
+  } else {
+    const float sc = lane < k ? sigmoid_f(my_l) : 0.f;
+    if (!raw) {
+      const float sj = wave_sum(sc);
+      g = sc / sj;
+    } else {
+      g = sc;
+    }
+  }
+  if (lane < k) {
+    idx_out[(size_t)t * k + lane] = my_idx;
+    gate_out[(size_t)t * k + lane] = g;
+  }
+}
+
 constexpr int RS_WAVES = ROUTE_WAVES;
 
 // MAXC experts per lane (E <= 64*MAXC), KSM = largest K split, PF: load the
@@ -364,12 +494,11 @@ __global__ __launch_bounds__(RS_WAVES * 64) void route_select_kernel(
 #pragma unroll
       for (int s = 0; s < KSM; ++s) pvc[c][s] = pvn[c][s];
     if (PF && t + 1 < tend) fetch(t + 1);
-    float l[MAXC], key[MAXC];
+    float l[MAXC];
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
       const int e = lane + 64 * c;
       l[c] = -INFINITY;
-      key[c] = -INFINITY;
       if (e < E) {
         // K-slice partial sums added in slice order
         float v = pvc[c][0];
@@ -378,119 +507,11 @@ __global__ __launch_bounds__(RS_WAVES * 64) void route_select_kernel(
           if (s < ksplit) v += pvc[c][s];
         if (router_bias) v += router_bias[e];
         l[c] = v;
-        // sigmoid scores with a selection bias: the bias is on the score
-        // scale; otherwise the logit orders the choice
-        key[c] = select_bias ? (scoring ? sigmoid_f(v) : v) + select_bias[e]
-                             : v;
         if (logits_out) logits_out[(size_t)t * E + e] = v;
       }
     }
-    // per-token scores: softmax probs, or sigmoid scores; P accumulates
-    // the scores scaled to sum to 1
-    float m = -INFINITY, inv;
-    float ex[MAXC], se = 0.f;
-    if (!scoring) {
-#pragma unroll
-      for (int c = 0; c < MAXC; ++c) m = fmaxf(m, l[c]);
-      m = wave_max(m);
-#pragma unroll
-      for (int c = 0; c < MAXC; ++c) {
-        const int e = lane + 64 * c;
-        ex[c] = (e < E) ? __expf(l[c] - m) : 0.f;
-        se += ex[c];
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < MAXC; ++c) {
-        const int e = lane + 64 * c;
-        ex[c] = (e < E) ? sigmoid_f(l[c]) : 0.f;
-        se += ex[c];
-      }
-    }
-    se = wave_sum(se);
-    inv = 1.0f / se;
-#pragma unroll
-    for (int c = 0; c < MAXC; ++c) psum[c] += ex[c] * inv;
-
-    // k rounds of wave argmax on (key desc, index asc); lane j keeps the
-    // winner of round j (slot j) and its logit.
-    bool taken[MAXC];
-#pragma unroll
-    for (int c = 0; c < MAXC; ++c) taken[c] = (lane + 64 * c) >= E;
-    int my_idx = 0;
-    float my_l = -INFINITY;
-    for (int j = 0; j < k; ++j) {
-      float bk = -INFINITY, bl = -INFINITY;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int c = 0; c < MAXC; ++c) {
-        // indices rise with c: strict > keeps the lower index on ties
-        if (!taken[c] && (bi == 0x7fffffff || key[c] > bk)) {
-          bk = key[c];
-          bi = lane + 64 * c;
-          bl = l[c];
-        }
-      }
-      // wave argmax on (key desc, index asc): a total order, so the DPP
-      // steps of the wave reductions give the same winner in any order
-      auto take = [&](float ok, int oi, float ol) {
-        const bool better = (oi != 0x7fffffff) &&
-                            (bi == 0x7fffffff || ok > bk || (ok == bk && oi < bi));
-        if (better) {
-          bk = ok;
-          bi = oi;
-          bl = ol;
-        }
-      };
-#define MOE_ARGMAX_STEP(CTRL, RM)                                       \
-      take(dpp_f<CTRL, RM>(bk, bk), dpp_i<CTRL, RM>(bi, bi),           \
-           dpp_f<CTRL, RM>(bl, bl))
-      MOE_ARGMAX_STEP(DPP_QUAD_1032, 0xf);
-      MOE_ARGMAX_STEP(DPP_QUAD_2301, 0xf);
-      MOE_ARGMAX_STEP(DPP_ROW_HALF_MIRROR, 0xf);
-      MOE_ARGMAX_STEP(DPP_ROW_MIRROR, 0xf);
-      MOE_ARGMAX_STEP(DPP_ROW_BCAST15, 0xa);
-      MOE_ARGMAX_STEP(DPP_ROW_BCAST31, 0xc);
-#undef MOE_ARGMAX_STEP
-      bk = lane63(bk);
-      bi = __builtin_amdgcn_readlane(bi, 63);
-      bl = lane63(bl);
-      // every lane now holds the same winner
-#pragma unroll
-      for (int c = 0; c < MAXC; ++c)
-        if (lane + 64 * c == bi) taken[c] = true;
-      if (lane == j) {
-        my_idx = bi;
-        my_l = bl;
-      }
-    }
-    // gates.  Softmax, renormalised: chosen probabilities over their sum,
-    // i.e. a softmax over the chosen logits (the shared normaliser
-    // cancels).  Softmax, raw: the chosen probability.  Sigmoid: the chosen
-    // score, over the chosen scores' sum when renormalised.
-    float g;
-    if (!scoring) {
-      if (!raw) {
-        const float mc = wave_max(lane < k ? my_l : -INFINITY);
-        const float ej = lane < k ? __expf(my_l - mc) : 0.f;
-        const float sj = wave_sum(ej);
-        g = ej / sj;
-      } else {
-        g = __expf(my_l - m) * inv;
-      }
-    } else {
-      const float sc = lane < k ? sigmoid_f(my_l) : 0.f;
-      if (!raw) {
-        const float sj = wave_sum(sc);
-        g = sc / sj;
-      } else {
-        g = sc;
-      }
-    }
-    if (lane < k) {
-      idx_out[(size_t)t * k + lane] = my_idx;
-      gate_out[(size_t)t * k + lane] = g;
-    }
+    select_token<MAXC>(l, t, lane, select_bias, idx_out, gate_out, psum, E,
+                       k, scoring, raw);
   }
   // per-block probability partial sums, waves added in order 0..3
   for (int e = lane; e < 256; e += 64) psum_s[wave][e] = 0.f;
@@ -504,6 +525,123 @@ __global__ __launch_bounds__(RS_WAVES * 64) void route_select_kernel(
     v += psum_s[3][e];
     partials[(size_t)blockIdx.x * E + e] = v;
   }
+}
+
+// Fused route for small batches with few experts (decode): one workgroup
+// per token runs the router linear, the softmax, the top-k and the gates in
+// one launch.  The router GEMM is float32 on the vector units (a handful of
+// tokens leaves the matrix cores nothing to fill): thread i takes the K
+// chunks of 8 at 8i, 8i + 8*RF_THREADS, ... for every expert, adding the
+// products in K order; each expert's 256 partial sums are reduced within
+// each 16-lane row by DPP butterflies (quad, half-row and row mirrors, so
+// every lane of a row holds the same sum) and the 16 row sums added in a
+// fixed order through LDS.  Wave 0 then scores, chooses and gates the token
+// with the select kernel's own code.  The token's scores scaled to sum to 1
+// are its row of the probability partials (one row per token).
+constexpr int RF_THREADS = 256;
+constexpr int RF_MAXE = 8;       // experts per token held in registers
+constexpr int RF_MAXT = 128;     // tokens (workgroups) the fused path takes
+
+template <typename XT>
+__device__ __forceinline__ void load8f(const XT* p, float* out);
+template <>
+__device__ __forceinline__ void load8f<bf16>(const bf16* p, float* out) {
+  V16 a;
+  a.u = ldg16(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i] = (float)a.h[i];
+}
+template <>
+__device__ __forceinline__ void load8f<float>(const float* p, float* out) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    V16 v;
+    v.u = ldg16(p + 4 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[4 * i + j] = v.f[j];
+  }
+}
+
+template <typename XT>
+__global__ __launch_bounds__(RF_THREADS) void route_fused_kernel(
+    const XT* __restrict__ x, const float* __restrict__ wr,
+    const float* __restrict__ router_bias,
+    const float* __restrict__ select_bias, float* __restrict__ logits_out,
+    int32_t* __restrict__ idx_out, float* __restrict__ gate_out,
+    float* __restrict__ partials, int d, int E, int k, int scoring,
+    int raw) {
+  __shared__ float red[RF_MAXE][RF_THREADS / 16];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float acc[RF_MAXE];
+#pragma unroll
+  for (int e = 0; e < RF_MAXE; ++e) acc[e] = 0.f;
+  const XT* xr = x + (size_t)t * d;
+  // RF_U chunks per thread per trip, all their loads issued before the
+  // first product (one memory latency per trip, not one per chunk); chunks
+  // past d are skipped, the products still added in K order
+  constexpr int RF_U = 2;
+  for (int k0 = tid * 8; k0 < d; k0 += RF_U * RF_THREADS * 8) {
+    float xv[RF_U][8];
+    V16 w[RF_U][RF_MAXE][2];
+#pragma unroll
+    for (int u = 0; u < RF_U; ++u) {
+      const int kk = k0 + u * RF_THREADS * 8;
+      if (kk < d) {
+        load8f<XT>(xr + kk, xv[u]);
+#pragma unroll
+        for (int e = 0; e < RF_MAXE; ++e) {
+          if (e < E) {
+            w[u][e][0].u = ldg16(wr + (size_t)e * d + kk);
+            w[u][e][1].u = ldg16(wr + (size_t)e * d + kk + 4);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < RF_U; ++u) {
+      if (k0 + u * RF_THREADS * 8 < d) {
+#pragma unroll
+        for (int e = 0; e < RF_MAXE; ++e) {
+          if (e < E) {
+            float a = acc[e];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a = fmaf(xv[u][j], w[u][e][0].f[j], a);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              a = fmaf(xv[u][4 + j], w[u][e][1].f[j], a);
+            acc[e] = a;
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < RF_MAXE; ++e) {
+    if (e < E) {
+      float v = acc[e];
+      v += dpp_f<DPP_QUAD_1032>(0.f, v);
+      v += dpp_f<DPP_QUAD_2301>(0.f, v);
+      v += dpp_f<DPP_ROW_HALF_MIRROR>(0.f, v);
+      v += dpp_f<DPP_ROW_MIRROR>(0.f, v);
+      if ((lane & 15) == 0) red[e][wave * 4 + (lane >> 4)] = v;
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float l[1] = {-INFINITY};
+  if (lane < E) {
+    float v = red[lane][0];
+#pragma unroll
+    for (int r = 1; r < RF_THREADS / 16; ++r) v += red[lane][r];
+    if (router_bias) v += router_bias[lane];
+    l[0] = v;
+    if (logits_out) logits_out[(size_t)t * E + lane] = v;
+  }
+  float psum[1] = {0.f};
+  select_token<1>(l, t, lane, select_bias, idx_out, gate_out, psum, E, k,
+                  scoring, raw);
+  if (lane < E) partials[(size_t)t * E + lane] = psum[0];
 }
 
 // Column means of the per-block probability partials [nblk, E], in a fixed
@@ -612,6 +750,29 @@ hipError_t launch_route_select_from(const float* part, int ksplit,
     else MOE_SELECT(4, ROUTER_MAX_KSPLIT, false);
   }
 #undef MOE_SELECT
+  return hipGetLastError();
+}
+
+bool route_fused(int T, int E) { return T <= RF_MAXT && E <= RF_MAXE; }
+
+int route_partial_rows(int T, int E) {
+  return route_fused(T, E) ? T : route_blocks(T);
+}
+
+hipError_t launch_route_fused(int dtype, const void* x, const float* wr,
+                              const float* router_bias,
+                              const float* select_bias, float* logits,
+                              int32_t* idx, float* gate, float* partials,
+                              int T, int d, int E, int k, int scoring,
+                              int raw, hipStream_t s) {
+  if (dtype == 1)
+    route_fused_kernel<bf16><<<T, RF_THREADS, 0, s>>>(
+        (const bf16*)x, wr, router_bias, select_bias, logits, idx, gate,
+        partials, d, E, k, scoring, raw);
+  else
+    route_fused_kernel<float><<<T, RF_THREADS, 0, s>>>(
+        (const float*)x, wr, router_bias, select_bias, logits, idx, gate,
+        partials, d, E, k, scoring, raw);
   return hipGetLastError();
 }
 
