@@ -1181,7 +1181,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
     const int n = nbase + ch * 8;
     if (i < gr.rows && n < N) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(&ot(row, ch * 8));
-      stg16(outp + (size_t)(gr.out0 + i) * N + n, v);
+      // non-temporal: the tile is not read again by this launch, and its
+      // lines would otherwise push the shared A and B slices out of L2
+      __builtin_nontemporal_store(
+          v, reinterpret_cast<u32x4*>(outp + (size_t)(gr.out0 + i) * N + n));
     }
   }
 }
