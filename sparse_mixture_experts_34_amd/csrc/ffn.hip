@@ -750,6 +750,15 @@ __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff,
       : "memory", "m0", "scc");
 }
 
+// A wave-uniform pointer in scalar registers (the value is the same in every
+// lane; this only tells the compiler so).
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // dma16s for loads I... of a wave: load i from sbase(i) at offset voff[i]
 // into LDS lds + i * STRIDE.
 template <int STRIDE, typename SB, int... I>
@@ -875,75 +884,84 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
   const int l31 = lane & 31, q = lane >> 5;
 
   // Loads: wave w fills A rows [w*IA*RPI, (w+1)*IA*RPI) and B rows likewise,
-  // RPI rows per instruction; lane l covers row RPI*i + l/CPR, LDS position
-  // l%CPR, i.e. global chunk (l%CPR) ^ key(row).  Each load instruction has
-  // a wave-uniform base (scalar registers) and a 32-bit per-lane byte
-  // offset: A of the up GEMMs is based at x (token rows gathered through
-  // perm, T*d*2 < 2^32 bytes), A of the down GEMM at the tile's first row of
-  // H, B at the tile's first weight row (or first tile row block).
-  const int lr = lane / Geo::CPR;
-  const int lp = lane % Geo::CPR;
+  // RPI = 8 rows per instruction; lane l covers row RPI*i + l/8, LDS position
+  // l%8, i.e. global chunk (l%8) ^ key(row).  An instruction's first row is a
+  // multiple of 8, so key(row) = (l/8)/2 ^ (4 if the instruction index is
+  // odd): one per-lane chunk offset for even and one for odd instructions.
+  // Each load instruction has a wave-uniform base (scalar registers) and a
+  // 32-bit per-lane byte offset.  A: the byte offset of the lane's row from
+  // x (up GEMMs, token rows gathered through perm, T*d*2 < 2^32 bytes) or
+  // from the group's first H row (down GEMM), rows past the group's end
+  // repeating its last row: one register per load, kept across the K loop
+  // (reading them back from an LDS table instead made each issue wait for
+  // the operand reads in flight; up GEMM 3420 -> 3570 us).  B: the uniform
+  // part is the instruction's first weight row (its 8 rows lie in one
+  // matrix and, N being a multiple of 64, all inside it or all past it, so
+  // a past group is clamped whole to the last 8 rows), the per-lane part
+  // row l/8 of the 8 and the chunk: two registers for all B loads.
+  static_assert(BK == 64 && Geo::RPI == 8 && IA % 2 == 0 && IB % 2 == 0,
+                "load layout");
+  const int lr = lane >> 3;
+  const int lp = lane & 7;
+  const uint32_t ch_even = (uint32_t)((lp ^ (lr >> 1)) << 4);
+  const uint32_t ch_odd = (uint32_t)((lp ^ ((lr >> 1) | 4)) << 4);
   const char* abase = MODE == DOWN
-      ? (const char*)a.h + (size_t)(gr.out0 + r0) * K * 2
+      ? (const char*)a.h + (size_t)gr.out0 * K * 2
       : (const char*)a.x;
-  uint32_t ao[IA];
+  uint32_t ao[IA];   // per-lane A offsets, live across the K loop
 #pragma unroll
   for (int i = 0; i < IA; ++i) {
-    const int row = (wave * IA + i) * Geo::RPI + lr;
-    const int ai = min(r0 + row, gr.rows - 1);
-    const int arow = MODE == DOWN ? ai - r0
+    const int ai = min(r0 + (wave * IA + i) * Geo::RPI + lr, gr.rows - 1);
+    const int arow = MODE == DOWN ? ai
                                   : (gr.shared ? ai : a.perm[gr.out0 + ai] / a.k);
-    ao[i] = (uint32_t)arow * ((uint32_t)K * 2u) + ((lp ^ Geo::key(row)) << 4);
+    ao[i] = (uint32_t)arow * ((uint32_t)K * 2u) + ((i & 1) ? ch_odd : ch_even);
   }
   // B rows: SwiGLU block b = r >> 6 holds gate cols [32b, 32b+32) in rows
   // [64b, 64b+32) and the matching up cols in [64b+32, 64b+64), so wave
-  // column wn's two N-tiles are a gate tile and its up tile.  An instruction's
-  // 8 (or, tiled, 16) rows lie in one of them: its matrix is uniform, and
-  // the two matrices' bases (at the tile's first weight row, or first tile
-  // row block) are the only B bases.
+  // column wn's two N-tiles are a gate tile and its up tile.
   const size_t bskip = TW ? (size_t)(nbase >> 4) * (K / 32) * 512
                           : (size_t)nbase * K;
   const char* bm0 = (const char*)((const bf16*)w0v + bskip);
   const char* bm1 = MODE == UP_SWIGLU
       ? (const char*)((const bf16*)w1v + bskip) : bm0;
-  uint32_t bo[IB];
-  bool bup[IB];   // load i reads the up matrix (SwiGLU), uniform
-#pragma unroll
-  for (int i = 0; i < IB; ++i) {
-    const int row0 = (wave * IB + i) * Geo::RPI;   // first row, uniform
-    const int row = row0 + lr;
-    int wrow;
-    if (MODE == UP_SWIGLU) {
-      bup[i] = ((row0 >> 5) & 1) != 0;
-      wrow = nbase + 32 * (row >> 6) + (row & 31);
-    } else {
-      bup[i] = false;
-      wrow = nbase + row;
-    }
-    wrow = min(wrow, N - 1);
-    bo[i] = (uint32_t)(wrow - nbase) * ((uint32_t)K * 2u) +
-            ((lp ^ Geo::key(row)) << 4);
+  const uint32_t b_lane = TW ? (uint32_t)(lane * 16)
+                             : (uint32_t)lr * ((uint32_t)K * 2u);
+  // uniform part of B load i: its matrix and byte offset from that matrix's
+  // tile base
+  auto b_part = [&](int i, bool& up) -> uint32_t {
     if constexpr (TW) {
       // instruction ii = wave * IB + i loads tile (row block ii / 2 of the
-      // slice's B rows, column block ii % 2): weight row block of LDS rows
-      // 16 * (ii / 2) .. +15 (SwiGLU: gate or up rows, as above)
+      // slice's B rows, column block ii % 2)
       const int ii = wave * IB + i;
       const int t0 = 16 * (ii >> 1);
       int wr0;
       if (MODE == UP_SWIGLU) {
-        bup[i] = ((t0 >> 5) & 1) != 0;
+        up = ((t0 >> 5) & 1) != 0;
         wr0 = nbase + 32 * (t0 >> 6) + (t0 & 31);
       } else {
+        up = false;
         wr0 = nbase + t0;
       }
       const int rbg = min(wr0 >> 4, N / 16 - 1);
-      bo[i] = ((uint32_t)(rbg - (nbase >> 4)) * (uint32_t)(K / 32) +
-               (uint32_t)(ii & 1)) * 1024u + (uint32_t)(lane * 16);
+      return ((uint32_t)(rbg - (nbase >> 4)) * (uint32_t)(K / 32) +
+              (uint32_t)(ii & 1)) * 1024u;
+    } else {
+      const int row0 = (wave * IB + i) * Geo::RPI;
+      int wrow0;
+      if (MODE == UP_SWIGLU) {
+        up = ((row0 >> 5) & 1) != 0;
+        wrow0 = nbase + 32 * (row0 >> 6) + (row0 & 31);
+      } else {
+        up = false;
+        wrow0 = nbase + row0;
+      }
+      wrow0 = min(wrow0, N - 8);
+      return (uint32_t)(wrow0 - nbase) * ((uint32_t)K * 2u);
     }
-  }
+  };
   // LDS byte addresses of the stages (link-time constants) and of this
   // wave's first load in a stage
-  auto lds_of = [](const bf16* p) -> uint32_t {
+  auto lds_of = [](const void* p) -> uint32_t {
     return (uint32_t)(uintptr_t)(lds_void_t*)p;
   };
   const uint32_t a_lds[6] = {lds_of(A0), lds_of(A1), lds_of(A2),
@@ -958,12 +976,19 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
     const size_t ka = (size_t)(kb + kt) * BK * 2;            // bytes along K
     const size_t kw = TW ? (size_t)(kb + kt) * 2048 : ka;    // weight bytes
     const char* ak = abase + ka;
-    const char* b0k = bm0 + kw;
-    const char* b1k = bm1 + kw;
     dma16s_seq<ASTR>([&](int) { return ak; }, ao, a_lds[st] + a_w,
                      std::make_integer_sequence<int, IA>());
-    dma16s_seq<BSTR>([&](int i) { return bup[i] ? b1k : b0k; }, bo,
-                     b_lds[st] + b_w, std::make_integer_sequence<int, IB>());
+    uint32_t bo[IB];
+    const char* bs[IB];
+#pragma unroll
+    for (int i = 0; i < IB; ++i) {
+      bool up;
+      const uint32_t u = b_part(i, up);
+      bs[i] = uniform_ptr((up ? bm1 : bm0) + kw + u);
+      bo[i] = TW ? b_lane : b_lane + ((i & 1) ? ch_odd : ch_even);
+    }
+    dma16s_seq<BSTR>([&](int i) { return bs[i]; }, bo, b_lds[st] + b_w,
+                     std::make_integer_sequence<int, IB>());
   };
 
   f32x16 acc[MT][NT];
@@ -1144,32 +1169,44 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
     const int rb = idx - NS * SA;
     return Bs(rb / SB)[rb % SB];
   };
-  // 32x32 accumulator layout: lane holds column lane&31; item v is row
-  // (v&3) + 4*(lane>>5) + 8*(v>>2).
+  // this lane's bias of each of its N-tiles' columns (GELU up and down)
+  float bias_j[NT];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
+  for (int j = 0; j < NT; ++j) {
+    const int n = min(nbase + wn * WN + 32 * j + l31, N - 1);
+    bias_j[j] = (MODE != UP_SWIGLU && biasv) ? (float)((const bf16*)biasv)[n] : 0.f;
+  }
+  // 32x32 accumulator layout: lane holds column lane&31; item v is row
+  // (v&3) + 4*(lane>>5) + 8*(v>>2).  One accumulator tile (SwiGLU: a gate
+  // tile and its up tile) at a time, each copied out whole, so that every
+  // index into the accumulator array is a constant.
+  auto out_tile = [&](int i, int c, const f32x16& t0, const f32x16& t1,
+                      float bias) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int row = wm * WM + 32 * i + (v & 3) + 4 * q + 8 * (v >> 2);
+      float h;
       if (MODE == UP_SWIGLU) {
-        // N-tiles (2p, 2p+1) are a gate tile and its up tile
-#pragma unroll
-        for (int p = 0; p < NT / 2; ++p) {
-          const int c = 32 * (wn * (NT / 2) + p) + l31;
-          const float h = silu(acc[i][2 * p][v]) * acc[i][2 * p + 1][v];
-          ot(row, c) = (bf16)h;
-        }
+        h = silu(t0[v]) * t1[v];
       } else {
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          const int c = wn * WN + 32 * j + l31;
-          const int n = min(nbase + c, N - 1);
-          const float bias = biasv ? (float)((const bf16*)biasv)[n] : 0.f;
-          float v2 = acc[i][j][v] + bias;
-          if (MODE == UP_GELU) v2 = gelu_erf(v2);
-          ot(row, c) = (bf16)v2;
-        }
+        h = t0[v] + bias;
+        if (MODE == UP_GELU) h = gelu_erf(h);
       }
+      ot(row, c) = (bf16)h;
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    if (MODE == UP_SWIGLU) {
+      // N-tiles (2p, 2p+1) are a gate tile and its up tile
+#pragma unroll
+      for (int p = 0; p < NT / 2; ++p)
+        out_tile(i, 32 * (wn * (NT / 2) + p) + l31, acc[i][2 * p],
+                 acc[i][2 * p + 1], 0.f);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        out_tile(i, wn * WN + 32 * j + l31, acc[i][j], acc[i][j], bias_j[j]);
     }
   }
   __syncthreads();
