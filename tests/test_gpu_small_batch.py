@@ -1,8 +1,10 @@
 """The layer on decode-sized batches against the CPU oracle.
 
-Batches of a few dozen tokens take the small-batch paths: the router GEMM
-split along K into up to 16 slices, one token per select wave, and the
-whole dispatch in one workgroup.  Each case checks the layer's expert
+Batches of a few dozen tokens take the small-batch paths: with at most 8
+experts the fused route kernel (one workgroup per token), otherwise the
+router GEMM split along K into up to 16 slices and one token per select
+wave; with at most 64 assignments and 64 experts the one-wave dispatch,
+otherwise the whole dispatch in one workgroup.  Each case checks the layer's expert
 indices, counts, drop count and output against the oracle (indices and
 counts bit for bit, aux within 1e-4 relative, output within the dtype
 tolerance), and, where nothing is reassigned, the indices against
@@ -46,6 +48,22 @@ CASES = [
       overflow="reassign", overflow_seed=21),
     W("sb_t33", T=33, d_model=128, n_experts=8, top_k=2, d_ff=128,
       act="swiglu", dtype="bf16", capacity=0, seed_index=67),
+    # fused route with a router bias and a selection bias, capacity drops in
+    # the one-wave dispatch
+    W("sb_t30_e8_biases_drops", T=30, d_model=256, n_experts=8, top_k=2,
+      d_ff=128, act="swiglu", dtype="bf16", capacity=6, zipf_s=0.8,
+      select_bias_std=0.1, seed_index=68),
+    # fused route with sigmoid scores, a selection bias and raw gates
+    W("sb_t29_e6_sigmoid_bias_raw", T=29, d_model=192, n_experts=6, top_k=3,
+      d_ff=64, act="gelu", dtype="bf16", capacity=0, scoring="sigmoid",
+      select_bias_std=0.1, raw_gates=True, seed_index=69),
+    # the largest batch of the fused route (128 tokens, 256 assignments:
+    # the one-workgroup dispatch)
+    W("sb_t128_e8", T=128, d_model=128, n_experts=8, top_k=2, d_ff=64,
+      act="swiglu", dtype="bf16", capacity=0, seed_index=70),
+    # just past the fused route (129 tokens: router GEMM + select)
+    W("sb_t129_e8", T=129, d_model=128, n_experts=8, top_k=2, d_ff=64,
+      act="swiglu", dtype="bf16", capacity=0, seed_index=71),
 ]
 
 
@@ -63,6 +81,8 @@ def test_small_batch_layer(wl):
     err = rel_inf(host(g["out"]), o["out"])
     log(f"  {wl.name}: out rel err {err:.2e}, dropped {o['n_dropped']}, "
         f"reassigned {o.get('n_reassigned', 0)}")
+    if "drops" in wl.name:
+        assert o["n_dropped"] > 0, "workload must exercise the capacity cut"
     assert err <= TOL[wl.dtype]
     if wl.overflow == "reassign":
         assert o["n_reassigned"] > 0, "workload must exercise reassignment"
