@@ -28,6 +28,13 @@ FLAGS = [
     "-Wno-unused-result",
 ]
 
+# Per-file additions.  The 4-bit GEMM reads each MFMA result back with VALU
+# right away, so its accumulators stay in ordinary VGPRs (the other GEMMs
+# keep theirs in accumulation registers).
+FILE_FLAGS = {
+    "ffn_q4.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc",
@@ -39,7 +46,8 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c",
+           src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n"

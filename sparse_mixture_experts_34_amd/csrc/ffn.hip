@@ -34,7 +34,7 @@
 //           MFMAs, the activation fused into the epilogue, the output tile
 //           staged through LDS for 16-byte row stores, and each XCD's last
 //           round of tiles split along K over its CUs.
-// 4-bit weights use the stream schedule at every batch size; float32
+// 4-bit weights use the stream schedule at every batch size (ffn_q4.hip); float32
 // problems use a plain float32 kernel (same grouping).  bf16 weights may
 // also come in tiled order (wquant 2, moe_tile_bf16: 1 KiB tiles of 16 rows
 // x 32 columns in 16x16x32 operand order); every bf16 schedule has a
@@ -42,43 +42,12 @@
 #include <utility>
 
 #include "common.hpp"
+#include "ffn_common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 
 namespace {
-
-enum { UP_SWIGLU = 0, UP_GELU = 1, DOWN = 2 };
-
-struct Group {
-  int rows;     // rows of this group
-  int out0;     // first output row
-  bool shared;
-};
-
-__device__ __forceinline__ Group group_of(int g, const int32_t* offsets, int E,
-                                          int T, int k) {
-  Group r;
-  if (g < E) {
-    r.out0 = offsets[g];
-    r.rows = offsets[g + 1] - r.out0;
-    r.shared = false;
-  } else {
-    r.out0 = T * k;
-    r.rows = T;
-    r.shared = true;
-  }
-  return r;
-}
-
-// Row of the A operand for output row index i (0-based inside the group).
-template <int MODE, typename ET>
-__device__ __forceinline__ const ET* a_row(const FfnArgs& a, const Group& gr,
-                                           int i, int K) {
-  if (MODE == DOWN) return (const ET*)a.h + (size_t)(gr.out0 + i) * K;
-  const int tok = gr.shared ? i : a.perm[gr.out0 + i] / a.k;
-  return (const ET*)a.x + (size_t)tok * K;
-}
 
 template <int MODE>
 __device__ __forceinline__ void group_weights(const FfnArgs& a, int g,
@@ -119,7 +88,6 @@ __device__ __forceinline__ void group_weights(const FfnArgs& a, int g,
 // (the MFMA operand order, 16 rows x 4 interleaved 16-byte pieces per
 // instruction, reads the same bytes about 10% slower).  Each step's weight
 // registers then pass through a per-wave LDS slot into MFMA B order.
-constexpr int ST_WAVES = 4;
 constexpr int ST_KSTEP = 64;         // K per step (two 16x16x32 MFMAs)
 constexpr int ST_PF = 3;             // prefetch ring depth (steps)
 
@@ -276,245 +244,6 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
           const StreamBuf<NMAT, RT, CG> cur = buf[p];
           if (s + ST_PF < my_steps) load(buf[p], s + ST_PF);
           compute(cur);
-        }
-      }
-    }
-
-    // K-split reduction: waves 1..3 park their sums, wave 0 adds in order
-    if (wave > 0) {
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int c = 0; c < CG; ++c)
-#pragma unroll
-          for (int t = 0; t < RT; ++t)
-            red[wave - 1][(m * CG + c) * RT + t][lane] = acc[m][c][t];
-    }
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-      for (int w = 0; w < ST_WAVES - 1; ++w)
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-          for (int c = 0; c < CG; ++c)
-#pragma unroll
-            for (int t = 0; t < RT; ++t)
-              acc[m][c][t] += red[w][(m * CG + c) * RT + t][lane];
-      // epilogue: lane holds column n0+16c+col, rows rg + 16t + 4*kq + r
-      bf16* outp = (bf16*)(MODE == DOWN ? a.y : a.h);
-#pragma unroll
-      for (int c = 0; c < CG; ++c) {
-        const int n = n0 + 16 * c + col;
-        if (n >= N) continue;
-        float bias = 0.f;
-        if (MODE != UP_SWIGLU && biasv) bias = (float)((const bf16*)biasv)[n];
-#pragma unroll
-        for (int t = 0; t < RT; ++t) {
-          if (t < ntile) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int i = rg + t * 16 + kq * 4 + r;
-              if (i < gr.rows) {
-                float v;
-                if (MODE == UP_SWIGLU)
-                  v = silu(acc[0][c][t][r]) * acc[NMAT - 1][c][t][r];
-                else if (MODE == UP_GELU) v = gelu_erf(acc[0][c][t][r] + bias);
-                else v = acc[0][c][t][r] + bias;
-                outp[(size_t)(gr.out0 + i) * N + n] = (bf16)v;
-              }
-            }
-          }
-        }
-      }
-    }
-    __syncthreads();   // red is reused by the next row group
-  }
-}
-
-// ===========================================================================
-// stream schedule, 4-bit weights
-// ===========================================================================
-// The stream schedule's work split (16*CG columns per workgroup, 4 waves
-// splitting K) with one K step per quantisation group of 128 weights.  Lane
-// (col, kq) takes weights kq*32 .. kq*32+31 of the group in its row: 16
-// code bytes, i.e. four words, each word one 16x16x32 MFMA B operand.  The
-// codes are stored tiled in exactly this lane order (1024 bytes per 16 rows
-// x group), so a wave reads a tile with one fully coalesced load, and the
-// 16 rows' (scale, offset) pairs with one 128-byte line.  A
-// word becomes eight bf16 with one shift and one and-or per pair: the bits
-// 0x4300 | q are exactly the bf16 number 128 + q, so the MFMAs sum
-// x * (128 + q) over the group, and one more MFMA per 32 weights against
-// bf16 ones gives the group's sum of x.  Then
-//   sum x * (lo + q*s) = s * sum x*(128 + q) + (lo - 128*s) * sum x
-// folds the group's scale and offset in after its MFMAs.  The A operand
-// takes the same weights in natural order (lane kq: kq*32 + 8h + 0..7 for
-// MFMA h), matching the code word layout (even weights in the low
-// half-words, odd weights in the high half-words).
-template <int MODE>
-__device__ __forceinline__ void group_weights_q4(
-    const FfnArgs& a, int g, bool shared, int N, int K, const uint8_t*& c0,
-    const uint8_t*& c1, const float*& q0, const float*& q1,
-    const void*& bias) {
-  const size_t cmat = (size_t)N * (K / 2);              // code bytes
-  const size_t qmat = (size_t)N * (K / Q4_GROUP) * 2;   // floats
-  c1 = nullptr;
-  q1 = nullptr;
-  if (MODE == DOWN) {
-    c0 = shared ? (const uint8_t*)a.sw2 : (const uint8_t*)a.w2 + (size_t)g * cmat;
-    q0 = shared ? a.sw2q : a.w2q + (size_t)g * qmat;
-    bias = shared ? a.sb2
-                  : (a.b2 ? (const char*)a.b2 + (size_t)g * N * 2 : nullptr);
-  } else {
-    c0 = shared ? (const uint8_t*)a.sw1 : (const uint8_t*)a.w1 + (size_t)g * cmat;
-    q0 = shared ? a.sw1q : a.w1q + (size_t)g * qmat;
-    if (MODE == UP_SWIGLU) {
-      c1 = shared ? (const uint8_t*)a.sw_up
-                  : (const uint8_t*)a.w_up + (size_t)g * cmat;
-      q1 = shared ? a.sw_upq : a.w_upq + (size_t)g * qmat;
-      bias = nullptr;
-    } else {
-      bias = shared ? a.sb1 : (const char*)a.b1 + (size_t)g * N * 2;
-    }
-  }
-}
-
-template <int NMAT, int RT, int CG>
-struct Q4Buf {
-  u32x4 code[NMAT][CG];   // 32 codes of one weight row, four words
-  float2 qp[NMAT][CG];    // that row's (scale, offset) for the group
-  u32x4 a[RT][4];         // 32 bf16 of one token row per row tile
-};
-
-__device__ __forceinline__ bf16x8 q4_operand(uint32_t word) {
-  V16 r;
-  r.u[0] = 0x43004300u | (word & 0x000F000Fu);
-  r.u[1] = 0x43004300u | ((word >> 4) & 0x000F000Fu);
-  r.u[2] = 0x43004300u | ((word >> 8) & 0x000F000Fu);
-  r.u[3] = 0x43004300u | ((word >> 12) & 0x000F000Fu);
-  return r.h;
-}
-
-template <int MODE, int RT, int CG, int PF>
-__global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_q4_kernel(FfnArgs a) {
-  constexpr int NMAT = MODE == UP_SWIGLU ? 2 : 1;
-  __shared__ f32x4 red[ST_WAVES - 1][NMAT * CG * RT][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = blockIdx.y;
-  const Group gr = group_of(g, a.offsets, a.E, a.T, a.k);
-  if (gr.rows <= 0) return;                 // uniform over the workgroup
-  const int N = MODE == DOWN ? a.d : a.d_ff;
-  const int K = MODE == DOWN ? a.d_ff : a.d;
-  const int n0 = blockIdx.x * 16 * CG;
-  if (n0 >= N) return;                      // uniform over the workgroup
-  const uint8_t* cm[2];
-  const float* qm[2];
-  const void* biasv;
-  group_weights_q4<MODE>(a, g, gr.shared, N, K, cm[0], cm[1], qm[0], qm[1],
-                         biasv);
-
-  const int col = lane & 15;   // B: weight row n0+16c+col; A: token row
-  const int kq = lane >> 4;    // 32-weight quarter of the group
-  const int ngroups = K / Q4_GROUP;
-  const int s_beg = wave * ngroups / ST_WAVES;
-  const int my_steps = (wave + 1) * ngroups / ST_WAVES - s_beg;
-  const uint8_t* crow[NMAT][CG];
-  const float2* qrow[NMAT][CG];
-#pragma unroll
-  for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-    for (int c = 0; c < CG; ++c) {
-      // 16-row block of column group c (a partial last group re-reads the
-      // last block and stores nothing for it)
-      const int nb = min((n0 + 16 * c) >> 4, N / 16 - 1);
-      const size_t tile = (size_t)nb * ngroups + s_beg;
-      crow[m][c] = cm[m] + tile * 1024 + lane * 16;
-      qrow[m][c] = (const float2*)qm[m] + tile * 16 + col;
-    }
-  V16 ones;
-  ones.u = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-
-  for (int rg = 0; rg < gr.rows; rg += RT * 16) {
-    const int ntile = min(RT, (gr.rows - rg + 15) >> 4);
-    const bf16* arow[RT];
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const int i = min(rg + t * 16 + col, gr.rows - 1);
-      arow[t] = a_row<MODE, bf16>(a, gr, i, K) + s_beg * Q4_GROUP + kq * 32;
-    }
-    f32x4 acc[NMAT][CG][RT];
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-      for (int c = 0; c < CG; ++c)
-#pragma unroll
-        for (int t = 0; t < RT; ++t) acc[m][c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    Q4Buf<NMAT, RT, CG> buf[PF];
-    auto load = [&](Q4Buf<NMAT, RT, CG>& b, int s) {
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int c = 0; c < CG; ++c) {
-          // codes stream once: non-temporal (the scale/offset pairs,
-          // 1/16 of the bytes, measured better as ordinary loads)
-          b.code[m][c] = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4*>(crow[m][c] + (size_t)s * 1024));
-          b.qp[m][c] = qrow[m][c][s * 16];
-        }
-#pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        if (t < ntile) {
-#pragma unroll
-          for (int h = 0; h < 4; ++h) b.a[t][h] = ldg16(arow[t] + s * Q4_GROUP + h * 8);
-        }
-      }
-    };
-    auto compute = [&](const Q4Buf<NMAT, RT, CG>& b) {
-#pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        if (t < ntile) {
-          f32x4 xs = f32x4{0.f, 0.f, 0.f, 0.f};
-          f32x4 pg[NMAT][CG];
-#pragma unroll
-          for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-            for (int c = 0; c < CG; ++c) pg[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            V16 av;
-            av.u = b.a[t][h];
-            xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av.h, ones.h, xs, 0, 0, 0);
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-              for (int c = 0; c < CG; ++c)
-                pg[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    av.h, q4_operand(b.code[m][c][h]), pg[m][c], 0, 0, 0);
-          }
-#pragma unroll
-          for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-            for (int c = 0; c < CG; ++c) {
-              const float sc = b.qp[m][c].x;
-              const float cl = b.qp[m][c].y - 128.0f * sc;
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                acc[m][c][t][r] += sc * pg[m][c][r] + cl * xs[r];
-            }
-        }
-      }
-    };
-#pragma unroll
-    for (int p = 0; p < PF; ++p)
-      if (p < my_steps) load(buf[p], p);
-    for (int s0 = 0; s0 < my_steps; s0 += PF) {
-#pragma unroll
-      for (int p = 0; p < PF; ++p) {
-        const int st = s0 + p;
-        if (st < my_steps) {
-          compute(buf[p]);
-          if (st + PF < my_steps) load(buf[p], st + PF);
         }
       }
     }
@@ -748,15 +477,6 @@ __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff,
       :
       : "v"(voff), "s"(sbase), "s"(lds), "n"(IMM)
       : "memory", "m0", "scc");
-}
-
-// A wave-uniform pointer in scalar registers (the value is the same in every
-// lane; this only tells the compiler so).
-__device__ __forceinline__ const char* uniform_ptr(const char* p) {
-  const uint64_t v = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
 // dma16s for loads I... of a wave: load i from sbase(i) at offset voff[i]
@@ -1700,32 +1420,9 @@ Plan plan_of(const FfnArgs& a) {
 }
 }  // namespace
 
-// 4-bit weights: the weight-streaming schedule at every batch size (a
-// decode-path format; larger batches stay correct, re-streaming the
-// weights once per 32 rows of an expert).
-template <int MODE>
-hipError_t launch_q4(const FfnArgs& a, hipStream_t s) {
-  const int N = MODE == DOWN ? a.d : a.d_ff;
-  const int G = a.E + a.n_shared;
-  const int cg = (long long)((N + 31) / 32) * G >= 512 ? 2 : 1;
-  dim3 grid((N + 16 * cg - 1) / (16 * cg), G);
-  const bool rt1 = a.T <= 16;   // a token picks an expert at most once
-  if (cg == 2) {
-    if (rt1) ffn_stream_q4_kernel<MODE, 1, 2, 2><<<grid, ST_WAVES * 64, 0, s>>>(a);
-    else ffn_stream_q4_kernel<MODE, 2, 2, 2><<<grid, ST_WAVES * 64, 0, s>>>(a);
-  } else {
-    if (rt1) ffn_stream_q4_kernel<MODE, 1, 1, 3><<<grid, ST_WAVES * 64, 0, s>>>(a);
-    else ffn_stream_q4_kernel<MODE, 2, 1, 2><<<grid, ST_WAVES * 64, 0, s>>>(a);
-  }
-  return hipGetLastError();
-}
-
 hipError_t launch_expert_up(const FfnArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  if (a.wquant == 1) {   // 4-bit codes
-    if (a.act == 1) return launch_q4<UP_SWIGLU>(a, s);
-    return launch_q4<UP_GELU>(a, s);
-  }
+  if (a.wquant == 1) return launch_q4_up(a, s);   // 4-bit codes
   const Plan p = plan_of(a);
   if (a.wquant == 2) {   // bf16 weights in tiled order
     if (a.act == 1) return launch_mode<UP_SWIGLU, true>(a, s, p.sched, p.rt, p.max_tiles);
@@ -1737,7 +1434,7 @@ hipError_t launch_expert_up(const FfnArgs& a, hipStream_t s) {
 
 hipError_t launch_expert_down(const FfnArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  if (a.wquant == 1) return launch_q4<DOWN>(a, s);   // 4-bit codes
+  if (a.wquant == 1) return launch_q4_down(a, s);   // 4-bit codes
   const Plan p = plan_of(a);
   if (a.wquant == 2) return launch_mode<DOWN, true>(a, s, p.sched, p.rt, p.max_tiles);
   return launch_mode<DOWN, false>(a, s, p.sched, p.rt, p.max_tiles);

@@ -136,6 +136,9 @@ constexpr int SPLIT_TILE_FLOATS = 256 * 256;
 int device_cus();
 hipError_t launch_expert_up(const FfnArgs& a, hipStream_t s);
 hipError_t launch_expert_down(const FfnArgs& a, hipStream_t s);
+// the same with 4-bit weights (wquant 1; called by the two above)
+hipError_t launch_q4_up(const FfnArgs& a, hipStream_t s);
+hipError_t launch_q4_down(const FfnArgs& a, hipStream_t s);
 
 // ---- 4-bit weights ---------------------------------------------------------
 constexpr int Q4_GROUP = 128;   // weights per (scale, offset) pair

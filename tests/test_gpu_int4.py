@@ -153,6 +153,11 @@ SMALL_Q4 = [
     W("q4_swiglu_shared_k8", T=40, d_model=256, n_experts=16, top_k=8,
       d_ff=128, act="swiglu", dtype="bf16", capacity=0, n_shared=1,
       select_bias_std=0.1, seed_index=35, wquant="int4"),
+    # 64 experts at 16 tokens: 64-column down workgroups, 32-column up
+    # workgroups, most experts empty
+    W("q4_t16_e64_down64", T=16, d_model=512, n_experts=64, top_k=2,
+      d_ff=256, act="swiglu", dtype="bf16", capacity=0, seed_index=74,
+      wquant="int4"),
 ]
 
 
