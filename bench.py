@@ -67,7 +67,8 @@ def parse():
 
 
 # the sources the expert GEMM kernels are compiled from
-GEMM_SOURCES = ("common.hpp", "kernels.hpp", "ffn.hip")
+GEMM_SOURCES = ("common.hpp", "kernels.hpp", "ffn_common.hpp", "ffn.hip",
+                "ffn_q4.hip")
 
 
 def kernel_sources_digest() -> str:
