@@ -84,7 +84,21 @@ __device__ __forceinline__ bf16x8 q4_operand(uint32_t word, uint32_t mask,
 
 using gchar = const __attribute__((address_space(1))) char;
 
-template <int MODE, int RT, int CG, int PF>
+// QL: each wave copies the (scale, offset) tiles of its whole K range into
+// LDS once (whole 16-byte chunks, coalesced) and reads each step's pair
+// from there; otherwise every step loads its pairs (8 bytes per lane, 16
+// distinct per instruction) beside the codes.  Those per-step loads cost
+// about an eighth of the up GEMM's time: as many load instructions as the
+// codes for a sixteenth of the bytes.
+extern __shared__ __attribute__((aligned(16))) char q4_lds[];
+
+// LDS bytes the QL variant needs (dynamic; its waves' pair tiles)
+constexpr int q4_ql_bytes(int ngroups, int nmat, int cg) {
+  return ST_WAVES * nmat * cg * ((ngroups + ST_WAVES - 1) / ST_WAVES) * 128;
+}
+constexpr int Q4_QL_MAX = 64 * 1024;
+
+template <int MODE, int RT, int CG, int PF, bool QL>
 __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_q4_kernel(FfnArgs a) {
   constexpr int NMAT = MODE == UP_SWIGLU ? 2 : 1;
   __shared__ f32x4 red[ST_WAVES - 1][NMAT * CG * RT][64];
@@ -124,6 +138,36 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_q4_kernel(FfnArgs a)
       qrow[m][c] = (gchar*)uniform_ptr((const char*)qm[m] + tile * 128);
     }
   const uint32_t c_lane = lane * 16, q_lane = col * 8;
+  // QL: this wave's pair tiles, [m][c][step] x 128 bytes
+  const int spw = (ngroups + ST_WAVES - 1) / ST_WAVES;
+  char* qw = q4_lds + (size_t)wave * (NMAT * CG * spw * 128);
+  if constexpr (QL) {
+    // all of a lane's chunks in flight at once, then into LDS (QJ: chunks
+    // per lane per tile at the largest QL size)
+    constexpr int QJ = Q4_QL_MAX / (ST_WAVES * NMAT * CG * 1024);
+    u32x4 qt[NMAT][CG][QJ];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int c = 0; c < CG; ++c)
+#pragma unroll
+        for (int j = 0; j < QJ; ++j) {
+          const int i = lane + 64 * j;
+          if (i < my_steps * 8)
+            qt[m][c][j] = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(
+                qrow[m][c] + (uint32_t)i * 16u);
+        }
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int c = 0; c < CG; ++c)
+#pragma unroll
+        for (int j = 0; j < QJ; ++j) {
+          const int i = lane + 64 * j;
+          if (i < my_steps * 8)
+            *reinterpret_cast<u32x4*>(qw + (m * CG + c) * spw * 128 + i * 16) = qt[m][c][j];
+        }
+  }
   V16 ones;
   ones.u = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   uint32_t mask, magic;   // nibble pair mask, bf16 128.0 in both halves
@@ -157,8 +201,9 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_q4_kernel(FfnArgs a)
           b.code[m][c] = __builtin_nontemporal_load(
               reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(
                   crow[m][c] + (c_lane + (uint32_t)s * 1024)));
-          b.qp[m][c] = *reinterpret_cast<const __attribute__((address_space(1))) f32x2*>(
-              qrow[m][c] + (q_lane + (uint32_t)s * 128));
+          if constexpr (!QL)
+            b.qp[m][c] = *reinterpret_cast<const __attribute__((address_space(1))) f32x2*>(
+                qrow[m][c] + (q_lane + (uint32_t)s * 128));
         }
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
@@ -168,7 +213,15 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_q4_kernel(FfnArgs a)
         }
       }
     };
-    auto compute = [&](const Q4Buf<NMAT, RT, CG>& b) {
+    auto compute = [&](const Q4Buf<NMAT, RT, CG>& b, int st) {
+      f32x2 qp[NMAT][CG];
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int c = 0; c < CG; ++c)
+          qp[m][c] = QL ? *reinterpret_cast<const f32x2*>(
+                              qw + ((m * CG + c) * spw + st) * 128 + col * 8)
+                        : b.qp[m][c];
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         if (t < ntile) {
@@ -194,8 +247,8 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_q4_kernel(FfnArgs a)
           for (int m = 0; m < NMAT; ++m)
 #pragma unroll
             for (int c = 0; c < CG; ++c) {
-              const float sc = b.qp[m][c].x;
-              const float cl = b.qp[m][c].y - 128.0f * sc;
+              const float sc = qp[m][c].x;
+              const float cl = qp[m][c].y - 128.0f * sc;
 #pragma unroll
               for (int r = 0; r < 4; ++r)
                 acc[m][c][t][r] =
@@ -212,7 +265,7 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_q4_kernel(FfnArgs a)
       for (int p = 0; p < PF; ++p) {
         const int st = s0 + p;
         if (st < my_steps) {
-          compute(buf[p]);
+          compute(buf[p], st);
           if (st + PF < my_steps) load(buf[p], st + PF);
         }
       }
@@ -274,6 +327,17 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_q4_kernel(FfnArgs a)
 // covers the chip.  cg 4 only for the down kernel with one row tile: the
 // up kernel (two matrices) or two row tiles at cg 4 would need more
 // registers than two waves per SIMD leave.
+template <int MODE, int RT, int CG, int PF>
+void launch_q4_shape(const FfnArgs& a, dim3 grid, hipStream_t s) {
+  constexpr int NMAT = MODE == UP_SWIGLU ? 2 : 1;
+  const int K = MODE == DOWN ? a.d_ff : a.d;
+  const int qb = q4_ql_bytes(K / Q4_GROUP, NMAT, CG);
+  if (qb <= Q4_QL_MAX)
+    ffn_stream_q4_kernel<MODE, RT, CG, PF, true><<<grid, ST_WAVES * 64, qb, s>>>(a);
+  else
+    ffn_stream_q4_kernel<MODE, RT, CG, PF, false><<<grid, ST_WAVES * 64, 0, s>>>(a);
+}
+
 template <int MODE>
 hipError_t launch_q4(const FfnArgs& a, hipStream_t s) {
   const int N = MODE == DOWN ? a.d : a.d_ff;
@@ -283,13 +347,13 @@ hipError_t launch_q4(const FfnArgs& a, hipStream_t s) {
   const int cg = MODE == DOWN && rt1 && blocks(64) >= 512 ? 4 : (blocks(32) >= 512 ? 2 : 1);
   dim3 grid((N + 16 * cg - 1) / (16 * cg), G);
   if (cg == 4) {
-    if constexpr (MODE == DOWN) ffn_stream_q4_kernel<MODE, 1, 4, 2><<<grid, ST_WAVES * 64, 0, s>>>(a);
+    if constexpr (MODE == DOWN) launch_q4_shape<MODE, 1, 4, 2>(a, grid, s);
   } else if (cg == 2) {
-    if (rt1) ffn_stream_q4_kernel<MODE, 1, 2, 2><<<grid, ST_WAVES * 64, 0, s>>>(a);
-    else ffn_stream_q4_kernel<MODE, 2, 2, 2><<<grid, ST_WAVES * 64, 0, s>>>(a);
+    if (rt1) launch_q4_shape<MODE, 1, 2, 2>(a, grid, s);
+    else launch_q4_shape<MODE, 2, 2, 2>(a, grid, s);
   } else {
-    if (rt1) ffn_stream_q4_kernel<MODE, 1, 1, 3><<<grid, ST_WAVES * 64, 0, s>>>(a);
-    else ffn_stream_q4_kernel<MODE, 2, 1, 2><<<grid, ST_WAVES * 64, 0, s>>>(a);
+    if (rt1) launch_q4_shape<MODE, 1, 1, 3>(a, grid, s);
+    else launch_q4_shape<MODE, 2, 1, 2>(a, grid, s);
   }
   return hipGetLastError();
 }
