@@ -347,7 +347,10 @@ hipError_t launch_q4(const FfnArgs& a, hipStream_t s) {
   const int cg = MODE == DOWN && rt1 && blocks(64) >= 512 ? 4 : (blocks(32) >= 512 ? 2 : 1);
   dim3 grid((N + 16 * cg - 1) / (16 * cg), G);
   if (cg == 4) {
-    if constexpr (MODE == DOWN) launch_q4_shape<MODE, 1, 4, 2>(a, grid, s);
+    // no in-wave prefetch: 132 VGPRs, and the waves of the other
+    // workgroup on the CU cover the load latency (down GEMM 50.3 -> 48.1 us
+    // against a two-step ring)
+    if constexpr (MODE == DOWN) launch_q4_shape<MODE, 1, 4, 1>(a, grid, s);
   } else if (cg == 2) {
     if (rt1) launch_q4_shape<MODE, 1, 2, 2>(a, grid, s);
     else launch_q4_shape<MODE, 2, 2, 2>(a, grid, s);
