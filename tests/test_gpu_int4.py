@@ -158,6 +158,12 @@ SMALL_Q4 = [
     W("q4_t16_e64_down64", T=16, d_model=512, n_experts=64, top_k=2,
       d_ff=256, act="swiglu", dtype="bf16", capacity=0, seed_index=74,
       wquant="int4"),
+    # 258 groups along K in the up projection: the (scale, offset) pairs of a
+    # workgroup exceed what the kernel stages in LDS, so they are loaded
+    # step by step
+    W("q4_long_k_pairs_per_step", T=4, d_model=33024, n_experts=2, top_k=1,
+      d_ff=128, act="swiglu", dtype="bf16", capacity=0, seed_index=75,
+      wquant="int4"),
 ]
 
 
