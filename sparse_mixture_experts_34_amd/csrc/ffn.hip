@@ -958,13 +958,15 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
 // streams its own weight rows from HBM into a register ring, in whole
 // 128-byte lines that a per-wave LDS slot reshuffles into 16x16x32 B
 // operand order (or, with tiled weights, as 1 KiB tiles already in that
-// order); the panel's token rows (A) are read once per workgroup with
-// ordinary loads, written to a double-buffered, XOR-swizzled LDS slice and
-// read by all eight waves.
+// order); the panel's token rows (A) go once per workgroup from global
+// memory straight into a ring of three XOR-swizzled LDS slices (direct-to-
+// LDS loads, two steps ahead) and are read by all eight waves.  (Through
+// registers and LDS stores, as first built, the A path cost about an eighth
+// of the DeepSeek-V3 up GEMM: 3371 -> 3177 us, Switch down 325 -> 304 us.)
 // Row tiles past the panel's rows issue no MFMAs and no loads, so a ragged
-// expert costs its own rows, not a full tile.  Every load is an ordinary
-// compiler-visible load, so the compiler's waits are exact: a wait for one
-// slice never waits for later weight loads.
+// expert costs its own rows, not a full tile.  The weight loads are
+// ordinary compiler-visible loads; the A loads are not, and each step ends
+// with a wait counted for the loads issued after the next step's A.
 constexpr int PN_KSTEP = 64;     // K per step (two 16x16x32 MFMAs)
 // Panel configuration (measured on the DeepSeek-V3 and Switch workloads;
 // 192- and 128-row panels, two steps of lookahead, 4 waves x 64 weight rows
@@ -1022,6 +1024,7 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
   static_assert(CG * NMAT == NBG && AI * W * 64 * 8 == SL, "shape");
   __shared__ __attribute__((aligned(16))) bf16 S0[SL];
   __shared__ __attribute__((aligned(16))) bf16 S1[SL];
+  __shared__ __attribute__((aligned(16))) bf16 S2[SL];
   __shared__ u32x4 xs[TW ? 1 : W][NMAT * CG * 2][64];   // reshuffle per wave
   __shared__ int s_info[3];
 
@@ -1042,24 +1045,31 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
   const int col = lane & 15, kq = lane >> 4;
   const int nbase = nb * COLS;
 
-  // A loads: thread covers rows (i*512 + tid) / 8, chunk tid % 8 of each
-  // step (8 threads read one row's 128 bytes); 32-bit element offsets.
-  // Rows past the panel re-read its last row (one cached line per
-  // instruction): every load is unconditional, which keeps the compiler's
-  // wait counts exact across the loop.
-  const bf16* abase = (const bf16*)(MODE == DOWN ? a.h : a.x);
+  // A slices go from global memory straight into LDS (direct-to-LDS
+  // loads, 16 bytes per lane, one instruction = 8 rows x 128 bytes): load i
+  // of wave w covers rows 64i + 8w + lane/8 of the panel, LDS position
+  // lane % 8 of its row, i.e. global chunk (lane % 8) ^ key(row); the key of
+  // those rows depends only on w and lane/8.  Each lane keeps one 32-bit
+  // byte offset per load from a wave-uniform base: the token row from x (up
+  // GEMMs, through perm; T*d*2 < 2^32 bytes) or the row from the group's
+  // first H row (down GEMM).  Rows past the panel re-read its last row.
+  const char* abase = MODE == DOWN ? (const char*)a.h + (size_t)gr.out0 * K * 2
+                                   : (const char*)a.x;
   uint32_t ao[AI];
-  int lo[AI];
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
-    const int row = (i * W * 64 + tid) >> 3;
-    const int p = tid & 7;
+    const int row = i * 64 + wave * 8 + (lane >> 3);
     const int ri = r0 + min(row, nvalid - 1);
-    const int arow_g = MODE == DOWN ? gr.out0 + ri
-                                    : (gr.shared ? ri : a.perm[gr.out0 + ri] / a.k);
-    ao[i] = (uint32_t)arow_g * (uint32_t)K + (uint32_t)(p << 3);
-    lo[i] = row * PN_KSTEP + ((p ^ pn_key(row)) << 3);
+    const int arow = MODE == DOWN ? ri
+                                  : (gr.shared ? ri : a.perm[gr.out0 + ri] / a.k);
+    ao[i] = (uint32_t)arow * ((uint32_t)K * 2u) +
+            (uint32_t)(((lane & 7) ^ pn_key(row)) << 4);
   }
+  // LDS byte address of this wave's first A load in each slice (uniform)
+  const uint32_t a_w = (uint32_t)__builtin_amdgcn_readfirstlane(wave * 8 * PN_KSTEP * 2);
+  const uint32_t a_lds[3] = {(uint32_t)(uintptr_t)(lds_void_t*)S0 + a_w,
+                             (uint32_t)(uintptr_t)(lds_void_t*)S1 + a_w,
+                             (uint32_t)(uintptr_t)(lds_void_t*)S2 + a_w};
   // B: wave column group c holds weight rows nbase + 16*(wave*CG + c) + col.
   // MFMA h of a 64-wide step contracts k-chunk kq + 4h (8 elements) of lane
   // group kq, for A and B alike: with this order the A operand reads of
@@ -1093,19 +1103,13 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
   const int aoff1 = col * PN_KSTEP + (((kq + 4) ^ pn_key(col)) << 3);
 
   const int nk = K / PN_KSTEP;
-  u32x4 ar[L][AI];
-  // Loads past the last step re-read the last step (cached, never used).
-  // the first NA of this thread's A loads (rows below NA * W * 64 / 8)
-  auto loadA = [&](auto nac, u32x4 (&r)[AI], int s) {
+  // A step s into slice st: the first NA of this lane's loads (rows below
+  // NA * 64); loads past the last step re-read the last step (never used)
+  auto dmaA = [&](auto nac, int st, int s) {
     constexpr int NA = decltype(nac)::value;
-    const int k0 = min(s, nk - 1) * PN_KSTEP;
-#pragma unroll
-    for (int i = 0; i < NA; ++i) r[i] = ldg16(abase + ao[i] + k0);
-  };
-  auto storeA = [&](auto nac, const u32x4 (&r)[AI], bf16* S) {
-    constexpr int NA = decltype(nac)::value;
-#pragma unroll
-    for (int i = 0; i < NA; ++i) *reinterpret_cast<u32x4*>(S + lo[i]) = r[i];
+    const char* ak = uniform_ptr(abase + (size_t)min(s, nk - 1) * PN_KSTEP * 2);
+    dma16s_seq<64 * PN_KSTEP * 2>([&](int) { return ak; }, ao, a_lds[st],
+                                  std::make_integer_sequence<int, NA>());
   };
   PanelB<NMAT, CG> ring[NSLOT];
   auto loadB = [&](PanelB<NMAT, CG>& b, int s) {
@@ -1190,44 +1194,46 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
       }
       __builtin_amdgcn_sched_group_barrier(0x008, RA * NM - BR * NM, 0);
     };
-    // Step s (u = s mod U): reads slice s % 2 and weight slot s % (L+1);
-    // first writes A step s+1 (register set (s+1) % L) into the other
-    // slice, whose readers finished at the last barrier, and its weight
-    // slot into the wave's reshuffle slot; reloads the A set and refills
-    // the weight slot with step s+1+L, then runs the MFMAs (which read the
-    // weights back from the reshuffle slot in MFMA order).
+    // Step s (u = s mod U): reads A slice s % 3 and weight slot s % 2.
+    // It issues A step s+2 into slice (s+2) % 3, whose readers finished at
+    // the last barrier, then refills the weight slot with step s+2 (after
+    // the slot went to the wave's reshuffle slot; with tiled weights, after
+    // the MFMAs that read the slot itself), and runs the MFMAs (row-major
+    // weights read back from the reshuffle slot in MFMA order).  Every step
+    // issues NA A loads, then BL weight loads, so at its end the loads
+    // issued after A step s+1 number BL + NA + BL: waiting for at most that
+    // many leaves the later steps in flight.  (The compiler's own wait for
+    // a weight slot counts only the weight loads; it also waits for the A
+    // step issued before the slot's successor, which that step needs one
+    // step later anyway.)
+    static_assert(L == 1, "A ring of three slices, weights two steps ahead");
+    constexpr int BL = NMAT * CG * 2;   // weight loads per step
+    constexpr int WAITN = 2 * BL + NA;
+    auto S = [&](int i) -> bf16* { return i == 0 ? S0 : (i == 1 ? S1 : S2); };
     auto step = [&](int s, int u) {
-      bf16* cur = (u & 1) ? S1 : S0;
-      bf16* nxt = (u & 1) ? S0 : S1;
-      storeA(na, ar[(u + 1) % L], nxt);
+      bf16* cur = S(u % 3);
       if constexpr (TW) {
-        // the MFMAs read the weight slot itself, then it is refilled
-        loadA(na, ar[(u + 1) % L], s + 1 + L);
+        dmaA(na, (u + 2) % 3, s + 2);
         compute(cur, ring[u % NSLOT]);
-        loadB(ring[u % NSLOT], s + 1 + L);
+        loadB(ring[u % NSLOT], s + 2);
       } else {
         stageB(ring[u % NSLOT]);
-        loadA(na, ar[(u + 1) % L], s + 1 + L);
-        loadB(ring[u % NSLOT], s + 1 + L);
+        dmaA(na, (u + 2) % 3, s + 2);
+        loadB(ring[u % NSLOT], s + 2);
         compute(cur, ring[u % NSLOT]);
       }
-      lds_barrier();
+      slice_barrier<WAITN>();
     };
-    // prologue in the loop's issue order: A step 0 into S0, then A step j
-    // (register set j % L) and weight step j for j = 1..L; weight step 0
-    // right after A step 0
-    loadA(na, ar[0], 0);
+    // prologue in the loop's issue order: A step 0, weight step 0, A step
+    // 1, weight step 1; then wait for A step 0
+    dmaA(na, 0, 0);
     loadB(ring[0], 0);
-    storeA(na, ar[0], S0);
-#pragma unroll
-    for (int j = 1; j <= L; ++j) {
-      loadA(na, ar[j % L], j);
-      loadB(ring[j], j);
-    }
-    lds_barrier();
-    // whole trips of U steps (constant slice, set and slot indices), then
-    // the remaining steps
-    constexpr int U = pn_lcm(2, pn_lcm(L, NSLOT));
+    dmaA(na, 1, 1);
+    loadB(ring[1], 1);
+    slice_barrier<WAITN>();
+    // whole trips of U steps (constant slice and slot indices), then the
+    // remaining steps
+    constexpr int U = pn_lcm(3, NSLOT);
     const int ntrip = nk / U;
     for (int tr = 0; tr < ntrip; ++tr) {
 #pragma unroll
