@@ -1248,6 +1248,9 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
   static_assert(MT % 2 == 0, "half panel");
   if (ntile > MT / 2) kloop(IntC<MT>{});
   else kloop(IntC<MT / 2>{});
+  // the redundant tail A loads land in LDS before the workgroup can end
+  // (the next workgroup on this CU may take the same LDS)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // epilogue: lane holds column n of group c and rows 16t + 4kq + r
   bf16* outp = (bf16*)(MODE == DOWN ? a.y : a.h);
