@@ -1001,12 +1001,8 @@ struct PanelB {
 constexpr int pn_gcd(int x, int y) { return y == 0 ? x : pn_gcd(y, x % y); }
 constexpr int pn_lcm(int x, int y) { return x / pn_gcd(x, y) * y; }
 
-// BM rows per panel; L steps of lookahead for both operands: step s stores
-// A step s+1 into LDS and issues A step s+1+L and weight step s+1+L, so L
-// register sets of A and L+1 weight slots are live.  A and weight loads of
-// one step are issued together, A first: vector loads complete in order, so
-// a wait for A step s+1 also waits for weight step s, which step s needs
-// anyway, and for nothing later.
+// BM rows per panel; L = 1: step s issues A step s+2 (direct-to-LDS, a
+// ring of three slices) and weight step s+2 (L+1 register slots), A first.
 // W waves per workgroup, NBG groups of 16 weight rows per wave (SwiGLU:
 // NBG/2 gate groups and the matching up groups).
 // TW: weights in tiled order (each weight load reads one 1 KiB tile in MFMA
