@@ -313,10 +313,12 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
 // row r sits at position c ^ key(r) so that the MFMA operand reads (32 rows,
 // one chunk) spread over all banks.  The key depends only on the low row
 // bits, which makes the swizzled offset of a lane the same for every 32-row
-// tile: one register per K-substep, tile offsets are immediates.  Two stages
-// live in four distinct arrays so the compiler sees that the stage being
-// loaded never aliases the stage being read: the next slice loads during the
-// MFMAs.
+// tile: one register per K-substep, tile offsets are immediates.  A and B
+// have rings of their own (NSA and NSB stages, each stage a distinct array
+// so the compiler sees that the stage being loaded never aliases the stage
+// being read): 160 KiB of LDS holds five 32 KiB slices, so the operand
+// that streams from HBM gets three stages (two slices in flight) and the
+// other two.
 //
 // Tile order: logical tiles run expert by expert, and inside an expert
 // n-block by n-block with the m-tiles innermost, so neighbouring tiles share
@@ -325,22 +327,29 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
 // contiguous run of logical tiles and its L2 serves the shared slices.
 constexpr int TL_BN = 256;   // B rows per tile (SwiGLU: 128 gate + 128 up)
 constexpr int N_XCD = 8;
-// One configuration is launched: 256-row tiles, two 64-wide K stages (one
-// slice in flight).  The template also takes narrower slices and deeper
-// rings (NS stages, NS - 1 slices in flight); 128-row tiles with six 32-wide
-// stages and 256-row tiles with four 32-wide stages both measured slower at
-// every batch size past the panel range.
+// One tile shape is launched: 256-row tiles over 64-wide K slices.  The
+// template also takes narrower slices and deeper rings; 128-row tiles with
+// six 32-wide stages and 256-row tiles with four 32-wide stages both
+// measured slower at every batch size past the panel range.
 constexpr int TL_WAVES = 8;
+// Stages per ring: the up GEMMs' weights stream from HBM (the token rows
+// are re-read from L2 and the memory-side cache), so B gets the third
+// stage; the down GEMM's A (the hidden rows, written by the up GEMM) is the
+// larger stream, so A gets it.  Mixtral-shaped prefill, same box: one
+// slice in flight for both, up 3.42 ms and down 1.79 ms; two B slices for
+// up 3.29 ms; two A slices for down 1.65 ms.
+constexpr int tl_nsa(int mode) { return mode == DOWN ? 3 : 2; }
+constexpr int tl_nsb(int mode) { return mode == DOWN ? 2 : 3; }
 
 // Logical tiles run group by group, n-block by n-block, row tiles (m)
 // innermost; group g has ceil(rows/BM) * NB of them.  Whole workgroup of
 // NTHR (>= number of groups) threads: thread g < G gets its group's first
 // logical tile (excl) and end (incl) from a prefix scan (wave shuffles, then
-// wave totals through LDS); every thread gets the total.
+// wave totals through s_wsum, NTHR / 64 ints of LDS); every thread gets the
+// total.
 template <int NTHR>
-__device__ void tile_scan(const FfnArgs& a, int G, int BM, int NB, int& excl,
-                          int& incl, int& total) {
-  __shared__ int s_wsum[NTHR / 64];
+__device__ void tile_scan(const FfnArgs& a, int G, int BM, int NB,
+                          int* s_wsum, int& excl, int& incl, int& total) {
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   int span = 0;
@@ -393,9 +402,10 @@ __device__ __forceinline__ bool publish_tile(int G, int BM, int NB, int L,
 template <int NTHR>
 __device__ bool find_panel_tile(const FfnArgs& a, int G, int BM, int NB,
                                 int* s_info) {
+  __shared__ int s_wsum[NTHR / 64];
   if (threadIdx.x == 0) s_info[1] = -1;
   int excl, incl, total;
-  tile_scan<NTHR>(a, G, BM, NB, excl, incl, total);
+  tile_scan<NTHR>(a, G, BM, NB, s_wsum, excl, incl, total);
   const int slot = blockIdx.x / N_XCD;
   const int L = ((slot / NB) * N_XCD + blockIdx.x % N_XCD) * NB + slot % NB;
   return publish_tile(G, BM, NB, L, excl, incl, s_info);
@@ -407,15 +417,17 @@ __device__ bool find_panel_tile(const FfnArgs& a, int G, int BM, int NB,
 // R = n / cpx whole rounds of the XCD's cpx CUs; the lo = n - R*cpx tiles
 // left over would leave most CUs idle in a last round, so (given a split
 // workspace, and when s = min(cpx / lo, nk) >= 2) each is cut into s K
-// ranges spread over the CUs.  s_info: group, first row, n-block, first and
-// end K slice, split item (-1: whole tile), counter index, pieces s.  False
-// for a workgroup with no work.
+// ranges spread over the CUs.  s_info (TL_INFO ints of LDS, then the scan's
+// NTHR / 64): group, first row, n-block, first and end K slice, split item
+// (-1: whole tile), counter index, pieces s.  False for a workgroup with no
+// work.
+constexpr int TL_INFO = 16;
 template <int NTHR>
 __device__ bool find_tile_split(const FfnArgs& a, int G, int BM, int NB,
                                 int nk, int* s_info) {
   if (threadIdx.x == 0) s_info[1] = -1;
   int excl, incl, total;
-  tile_scan<NTHR>(a, G, BM, NB, excl, incl, total);
+  tile_scan<NTHR>(a, G, BM, NB, s_info + TL_INFO, excl, incl, total);
   const int x = blockIdx.x % N_XCD, slot = blockIdx.x / N_XCD;
   const int per = (total + N_XCD - 1) / N_XCD;
   const int first = x * per;
@@ -499,6 +511,9 @@ __device__ __forceinline__ void slice_barrier() {
                : "memory");
 }
 
+constexpr int pn_gcd(int x, int y) { return y == 0 ? x : pn_gcd(y, x % y); }
+constexpr int pn_lcm(int x, int y) { return x / pn_gcd(x, y) * y; }
+
 // LDS geometry of one K slice of BK bf16 per row: rows of BK*2 bytes, CPR
 // 16-byte chunks per row; chunk c of row r sits at position c ^ key(r).  The
 // key spreads a 32-row MFMA operand read (one chunk of 32 consecutive rows)
@@ -517,7 +532,7 @@ struct SliceGeom {
 // TW: weights in tiled order: a B slice is 16 row blocks x 2 column
 // blocks of 1 KiB tiles, each loaded by one direct-to-LDS instruction and
 // kept in tile order in LDS (BK = 64).
-template <int MODE, int BM, int BK, int NS, int WAVES, bool TW>
+template <int MODE, int BM, int BK, int NSA, int NSB, int WAVES, bool TW>
 __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
                                                                   int NB) {
   using Geo = SliceGeom<BK>;
@@ -530,52 +545,59 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
   constexpr int IA = BM / Geo::RPI / WAVES;      // A loads per wave, slice
   constexpr int IB = TL_BN / Geo::RPI / WAVES;   // B loads per wave, slice
   constexpr int PER = IA + IB;                      // loads per wave, slice
-  constexpr int D = NS - 1;                         // slices in flight
+  // NSA stages of A slices and NSB of B slices: DA and DB slices in flight
+  constexpr int DA = NSA - 1, DB = NSB - 1;
+  constexpr int DMAX = DA > DB ? DA : DB;
+  // Each slice issues the A slice DA ahead and the B slice DB ahead, the one
+  // with less lookahead first; a slice's end waits until only the loads
+  // issued after the last one the next slice needs are in flight.
+  constexpr int WAITN = DA == DB ? (DA - 1) * PER
+                      : DA > DB ? IA + (DB - 1) * PER : IB + (DA - 1) * PER;
   constexpr int SA = BM * BK, SB = TL_BN * BK;      // elements per slice
   static_assert(IA >= 1 && IB >= 1, "every wave loads A and B rows");
   static_assert(!TW || (BK == 64 && IB * WAVES * Geo::RPI == TL_BN &&
                         TL_BN / 16 * 2 == IB * WAVES),
                 "tiled weights: one 1 KiB tile per B load instruction");
-  // NS stages of A and B slices; every stage index below is a compile-time
-  // constant, so the compiler can see that the stage being loaded never
-  // aliases the stage being read and does not make LDS reads wait for the
-  // loads in flight.
-  static_assert(NS >= 2 && NS <= 6, "2 to 6 stages");
+  // Every stage index below is a compile-time constant, so the compiler can
+  // see that the stage being loaded never aliases the stage being read and
+  // does not make LDS reads wait for the loads in flight.
+  static_assert(NSA >= 2 && NSA <= 6 && NSB >= 2 && NSB <= 6 &&
+                DA - DB <= 1 && DB - DA <= 1, "2 to 6 stages, lookaheads within one");
   __shared__ __attribute__((aligned(16))) bf16 A0[SA];
   __shared__ __attribute__((aligned(16))) bf16 A1[SA];
-  __shared__ __attribute__((aligned(16))) bf16 A2[NS > 2 ? SA : 8];
-  __shared__ __attribute__((aligned(16))) bf16 A3[NS > 3 ? SA : 8];
-  __shared__ __attribute__((aligned(16))) bf16 A4[NS > 4 ? SA : 8];
-  __shared__ __attribute__((aligned(16))) bf16 A5[NS > 5 ? SA : 8];
+  __shared__ __attribute__((aligned(16))) bf16 A2[NSA > 2 ? SA : 8];
+  __shared__ __attribute__((aligned(16))) bf16 A3[NSA > 3 ? SA : 8];
+  __shared__ __attribute__((aligned(16))) bf16 A4[NSA > 4 ? SA : 8];
+  __shared__ __attribute__((aligned(16))) bf16 A5[NSA > 5 ? SA : 8];
   __shared__ __attribute__((aligned(16))) bf16 B0[SB];
   __shared__ __attribute__((aligned(16))) bf16 B1[SB];
-  __shared__ __attribute__((aligned(16))) bf16 B2[NS > 2 ? SB : 8];
-  __shared__ __attribute__((aligned(16))) bf16 B3[NS > 3 ? SB : 8];
-  __shared__ __attribute__((aligned(16))) bf16 B4[NS > 4 ? SB : 8];
-  __shared__ __attribute__((aligned(16))) bf16 B5[NS > 5 ? SB : 8];
-  __shared__ int s_info[9];
+  __shared__ __attribute__((aligned(16))) bf16 B2[NSB > 2 ? SB : 8];
+  __shared__ __attribute__((aligned(16))) bf16 B3[NSB > 3 ? SB : 8];
+  __shared__ __attribute__((aligned(16))) bf16 B4[NSB > 4 ? SB : 8];
+  __shared__ __attribute__((aligned(16))) bf16 B5[NSB > 5 ? SB : 8];
   // stage s's arrays (s is a constant after unrolling, so each access names
-  // one distinct object)
+  // one distinct object; stages past NSA or NSB are never named, so their
+  // placeholder arrays take no LDS)
   auto As = [&](int st) -> bf16* {
-    switch (st) {
-      case 0: return A0;
-      case 1: return A1;
-      case 2: return A2;
-      case 3: return A3;
-      case 4: return A4;
-      default: return A5;
-    }
+    if constexpr (NSA > 5) if (st == 5) return A5;
+    if constexpr (NSA > 4) if (st == 4) return A4;
+    if constexpr (NSA > 3) if (st == 3) return A3;
+    if constexpr (NSA > 2) if (st == 2) return A2;
+    return st == 1 ? A1 : A0;
   };
   auto Bs = [&](int st) -> bf16* {
-    switch (st) {
-      case 0: return B0;
-      case 1: return B1;
-      case 2: return B2;
-      case 3: return B3;
-      case 4: return B4;
-      default: return B5;
-    }
+    if constexpr (NSB > 5) if (st == 5) return B5;
+    if constexpr (NSB > 4) if (st == 4) return B4;
+    if constexpr (NSB > 3) if (st == 3) return B3;
+    if constexpr (NSB > 2) if (st == 2) return B2;
+    return st == 1 ? B1 : B0;
   };
+  // The tile's parameters and the tile scan's scratch live in the last A
+  // stage: its first load is issued by slice 0, after the prologue's
+  // barrier, and every wave has read them into scalar registers before it
+  // (the split path's counter slot is used after the loads have landed).
+  static_assert(SA * 2 >= (TL_INFO + TL_THREADS / 64) * 4, "tile info fits");
+  int* const s_info = reinterpret_cast<int*>(As(NSA - 1));
 
   const int G = a.E + a.n_shared;
   const int Kd = MODE == DOWN ? a.d_ff : a.d;
@@ -587,6 +609,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
   const int kb = __builtin_amdgcn_readfirstlane(s_info[3]);
   const int ke = __builtin_amdgcn_readfirstlane(s_info[4]);
   const int item = __builtin_amdgcn_readfirstlane(s_info[5]);
+  const int sp_ctr = __builtin_amdgcn_readfirstlane(s_info[6]);
+  const int sp_n = __builtin_amdgcn_readfirstlane(s_info[7]);
   Group gr = group_of(g, a.offsets, a.E, a.T, a.k);
   gr.out0 = __builtin_amdgcn_readfirstlane(gr.out0);
   gr.rows = __builtin_amdgcn_readfirstlane(gr.rows);
@@ -692,12 +716,13 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
   constexpr int BSTR = TW ? 1024 : Geo::RPI * BK * 2;
   const uint32_t a_w = (uint32_t)(wave * IA * ASTR);
   const uint32_t b_w = (uint32_t)(wave * IB * BSTR);
-  auto issue = [&](int kt, int st) {
-    const size_t ka = (size_t)(kb + kt) * BK * 2;            // bytes along K
-    const size_t kw = TW ? (size_t)(kb + kt) * 2048 : ka;    // weight bytes
-    const char* ak = abase + ka;
+  auto issue_a = [&](int kt, int st) {
+    const char* ak = abase + (size_t)(kb + kt) * BK * 2;
     dma16s_seq<ASTR>([&](int) { return ak; }, ao, a_lds[st] + a_w,
                      std::make_integer_sequence<int, IA>());
+  };
+  auto issue_b = [&](int kt, int st) {
+    const size_t kw = TW ? (size_t)(kb + kt) * 2048 : (size_t)(kb + kt) * BK * 2;
     uint32_t bo[IB];
     const char* bs[IB];
 #pragma unroll
@@ -710,6 +735,21 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
     dma16s_seq<BSTR>([&](int i) { return bs[i]; }, bo, b_lds[st] + b_w,
                      std::make_integer_sequence<int, IB>());
   };
+  // The loads slice k issues: A slice k + DA and B slice k + DB, clamped to
+  // the piece's last slice, into stages (u + DA) % NSA and (u + DB) % NSB,
+  // u = k mod lcm(NSA, NSB) a constant after unrolling.  The prologue runs
+  // this for k = u = -DMAX .. -1, issuing only slices >= 0.
+  const int nk = ke - kb;   // K slices of this piece
+  auto issue = [&](int u, int k) {
+    const int sa = u + DA, sb = u + DB;
+    if (DA > DB) {
+      if (sb >= 0) issue_b(min(k + DB, nk - 1), sb % NSB);
+      if (sa >= 0) issue_a(min(k + DA, nk - 1), sa % NSA);
+    } else {
+      if (sa >= 0) issue_a(min(k + DA, nk - 1), sa % NSA);
+      if (sb >= 0) issue_b(min(k + DB, nk - 1), sb % NSB);
+    }
+  };
 
   f32x16 acc[MT][NT];
 #pragma unroll
@@ -719,7 +759,6 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int nk = ke - kb;   // K slices of this piece
   // MFMA operand rows: A rows wm*WM + 32i + l31, B rows wn*64 + 32j + l31;
   // their swizzle key is key(l31) for every tile
   const int akey = Geo::key(l31);
@@ -787,28 +826,30 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
 #pragma unroll
   for (int j = 0; j < NT; ++j) bv[LS][j].u = u32x4{0u, 0u, 0u, 0u};
 
-  // Prologue: slices 0..D-1 in flight (clamped to the last slice when the
-  // piece is shorter), then wait for slice 0.
+  // Prologue: A slices 0..DA-1 and B slices 0..DB-1 in flight (clamped to
+  // the last slice when the piece is shorter), in the order the main loop
+  // keeps, then wait for slice 0.
 #pragma unroll
-  for (int s = 0; s < D; ++s) issue(min(s, nk - 1), s);
-  slice_barrier<(D - 1) * PER>();
-  // Main loop, NS slices per trip with constant stage indices.  Slice k
-  // reads stage k % NS; before it, slice k + D is issued into stage
-  // (k + D) % NS, last read by slice k - 1 (one barrier ago).  After slice k
-  // the wave waits until slice k + 1 has landed: all later slices may stay
-  // in flight.  The slice body has no branch: near the end the last slice
-  // is issued again into the stage just freed (D redundant slices per tile,
-  // never read), so every slice issues PER loads and the wait count is
-  // constant; the loads, the first LDS reads and the MFMAs of a slice
-  // schedule as one block.
-  for (int kt = 0; kt < nk; kt += NS) {
+  for (int j = -DMAX; j < 0; ++j) issue(j, j);
+  slice_barrier<WAITN>();
+  // Main loop, lcm(NSA, NSB) slices per trip with constant stage indices.
+  // Slice k reads A stage k % NSA and B stage k % NSB; before it, A slice
+  // k + DA and B slice k + DB are issued into the stages slice k - 1 read
+  // (one barrier ago).  After slice k the wave waits until slice k + 1 has
+  // landed: all later loads may stay in flight.  The slice body has no
+  // branch: near the end the last slice is issued again into the stage just
+  // freed (redundant loads, never read), so every slice issues PER loads and
+  // the wait count is constant; the loads, the first LDS reads and the MFMAs
+  // of a slice schedule as one block.
+  constexpr int U = pn_lcm(NSA, NSB);
+  for (int kt = 0; kt < nk; kt += U) {
 #pragma unroll
-    for (int u = 0; u < NS; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int k = kt + u;
       if (k < nk) {
-        issue(min(k + D, nk - 1), (u + D) % NS);
-        compute_deferred(As(u), Bs(u));
-        slice_barrier<(D - 1) * PER>();
+        issue(u, k);
+        compute_deferred(As(u % NSA), Bs(u % NSB));
+        slice_barrier<WAITN>();
       }
     }
   }
@@ -820,7 +861,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
   // to arrive adds them all in piece order and stores the tile ----
   if (item >= 0) {
     static_assert(MT * NT * 16 * TL_THREADS <= SPLIT_TILE_FLOATS, "split tile");
-    const int ctr = s_info[6], sp = s_info[7];
+    const int ctr = sp_ctr, sp = sp_n;
     // 16-byte partials: float4 (i, j, v4) of thread tid at
     // ((i*NT + j)*4 + v4)*TL_THREADS + tid
     f32x4* pp = reinterpret_cast<f32x4*>(a.split_part + (size_t)item * SPLIT_TILE_FLOATS);
@@ -880,13 +921,13 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
   // ---- epilogue: activation, stage the bf16 tile in LDS, store rows ----
   // The output tile (BM x ncols bf16, row-major) is staged in the A stages
   // and, past their end, in the B stages.
-  static_assert(BM * TL_BN <= NS * (SA + SB), "output tile fits the LDS");
+  static_assert(BM * TL_BN <= NSA * SA + NSB * SB, "output tile fits the LDS");
   __syncthreads();
   auto ot = [&](int row, int col) -> bf16& {
     const int idx = row * ncols + col;
     const int st = idx / SA;
-    if (st < NS) return As(st)[idx - st * SA];
-    const int rb = idx - NS * SA;
+    if (st < NSA) return As(st)[idx - st * SA];
+    const int rb = idx - NSA * SA;
     return Bs(rb / SB)[rb % SB];
   };
   // this lane's bias of each of its N-tiles' columns (GELU up and down)
@@ -998,8 +1039,6 @@ struct PanelB {
   u32x4 b[NMAT][CG][2];
 };
 
-constexpr int pn_gcd(int x, int y) { return y == 0 ? x : pn_gcd(y, x % y); }
-constexpr int pn_lcm(int x, int y) { return x / pn_gcd(x, y) * y; }
 
 // BM rows per panel; L = 1: step s issues A step s+2 (direct-to-LDS, a
 // ring of three slices) and weight step s+2 (L+1 register slots), A first.
@@ -1368,7 +1407,7 @@ hipError_t launch_mode(const FfnArgs& a, hipStream_t s, int sched, int rt,
       const hipError_t e = launch_fill_zero32(a.split_cnt, (long long)N_XCD * a.split_cpx, s);
       if (e != hipSuccess) return e;
     }
-    ffn_tiled_kernel<MODE, 256, 64, 2, TL_WAVES, TW>
+    ffn_tiled_kernel<MODE, 256, 64, tl_nsa(MODE), tl_nsb(MODE), TL_WAVES, TW>
         <<<(unsigned)tiles, TL_WAVES * 64, 0, s>>>(a, NB);
   } else if (sched == 4) {
     // max_tiles counts panels of PN_BM rows
