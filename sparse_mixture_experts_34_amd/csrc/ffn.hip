@@ -422,6 +422,12 @@ __device__ bool find_panel_tile(const FfnArgs& a, int G, int BM, int NB,
 // (-1: whole tile), counter index, pieces s.  False for a workgroup with no
 // work.
 constexpr int TL_INFO = 16;
+// A split costs about as much as 50 K slices of a tile (the partial tiles'
+// stores, the device-scope fence that makes them visible to the other
+// pieces, and the sum): a last round is split only when that takes at
+// least TL_SPLIT_MIN_SAVED slices off it, into at most TL_SPLIT_MAX pieces.
+constexpr int TL_SPLIT_MIN_SAVED = 48;
+constexpr int TL_SPLIT_MAX = 8;
 template <int NTHR>
 __device__ bool find_tile_split(const FfnArgs& a, int G, int BM, int NB,
                                 int nk, int* s_info) {
@@ -435,7 +441,8 @@ __device__ bool find_tile_split(const FfnArgs& a, int G, int BM, int NB,
   const int cpx = a.split_part ? a.split_cpx : 0;
   const int R = cpx > 0 ? n / cpx : 0;
   const int lo = n - R * cpx;
-  const int sp = (cpx > 0 && lo > 0) ? min(cpx / lo, nk) : 1;
+  int sp = (cpx > 0 && lo > 0) ? min(min(cpx / lo, nk), TL_SPLIT_MAX) : 1;
+  if (nk - nk / sp < TL_SPLIT_MIN_SAVED) sp = 1;
   int L = total, kb = 0, ke = nk, item = -1, ctr = 0;
   if (sp < 2) {
     if (slot < n) L = first + slot;
@@ -882,8 +889,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
     __threadfence();
     // pieces of a tile are consecutive items (tile tl of the XCD: items
     // x*cpx + tl*sp + 0 .. sp-1); this one is piece pc.  Sum in piece
-    // order, one 32x32 accumulator tile at a time (its four loads per
-    // piece issued together).
+    // order, this piece's own partial read back like the others, one 32x32
+    // accumulator tile at a time with the loads of four pieces issued
+    // together (indices past the last piece re-read it and are not added).
+    static_assert(TL_SPLIT_MAX % 4 == 0, "pieces in batches of four");
     const int pc = (item % a.split_cpx) % sp;
     const f32x4* p0 = reinterpret_cast<const f32x4*>(
         a.split_part + (size_t)(item - pc) * SPLIT_TILE_FLOATS);
@@ -894,21 +903,22 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
         f32x4 sum[4];
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4) sum[v4] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int q = 0; q < sp; ++q) {
-          f32x4 pv[4];
-          if (q == pc) {
 #pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4)
-              pv[v4] = f32x4{acc[i][j][4 * v4], acc[i][j][4 * v4 + 1],
-                             acc[i][j][4 * v4 + 2], acc[i][j][4 * v4 + 3]};
-          } else {
+        for (int q0 = 0; q0 < TL_SPLIT_MAX; q0 += 4) {
+          if (q0 < sp) {
+            f32x4 pv[4][4];
 #pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4)
-              pv[v4] = p0[(size_t)q * (SPLIT_TILE_FLOATS / 4) +
-                          ((i * NT + j) * 4 + v4) * TL_THREADS + tid];
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+              for (int v4 = 0; v4 < 4; ++v4)
+                pv[u][v4] = p0[(size_t)min(q0 + u, sp - 1) * (SPLIT_TILE_FLOATS / 4) +
+                               ((i * NT + j) * 4 + v4) * TL_THREADS + tid];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (q0 + u < sp)
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4) sum[v4] += pv[u][v4];
           }
-#pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4) sum[v4] += pv[v4];
         }
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4)
@@ -919,17 +929,31 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
   }
 
   // ---- epilogue: activation, stage the bf16 tile in LDS, store rows ----
-  // The output tile (BM x ncols bf16, row-major) is staged in the A stages
-  // and, past their end, in the B stages.
-  static_assert(BM * TL_BN <= NSA * SA + NSB * SB, "output tile fits the LDS");
-  __syncthreads();
-  auto ot = [&](int row, int col) -> bf16& {
-    const int idx = row * ncols + col;
-    const int st = idx / SA;
-    if (st < NSA) return As(st)[idx - st * SA];
-    const int rb = idx - NSA * SA;
-    return Bs(rb / SB)[rb % SB];
+  // The output tile (BM x NCOLS bf16, row-major) is staged in the A stages
+  // and, past their end, in the B stages, RPS rows per stage.  A wave's
+  // 32-row MFMA tile lies in one stage, and so does each pass of the store
+  // loop; the stage is picked with scalar code (a wave-uniform index), so
+  // every LDS access is one base register plus a constant offset.
+  constexpr int NCOLS = MODE == UP_SWIGLU ? TL_BN / 2 : TL_BN;
+  constexpr int RPS = SA / NCOLS;           // staged rows per stage
+  constexpr int CPR = NCOLS / 8;            // 16-byte chunks per row
+  constexpr int PASSES = BM * CPR / TL_THREADS;
+  constexpr int PPS = SA / 8 / TL_THREADS;  // store passes per stage
+  static_assert(SA == SB && RPS % 32 == 0 && (SA / 8) % TL_THREADS == 0 &&
+                BM * NCOLS <= NSA * SA + NSB * SB, "output tile staging");
+  typedef __attribute__((address_space(3))) bf16 lds_bf16;
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  auto stage_lds = [&](int st) -> uint32_t {   // st: wave-uniform
+    uint32_t r = a_lds[0];
+#pragma unroll
+    for (int s2 = 1; s2 < NSA; ++s2)
+      if (st == s2) r = a_lds[s2];
+#pragma unroll
+    for (int s2 = 0; s2 < NSB; ++s2)
+      if (st == NSA + s2) r = b_lds[s2];
+    return r;
   };
+  __syncthreads();
   // this lane's bias of each of its N-tiles' columns (GELU up and down)
   float bias_j[NT];
 #pragma unroll
@@ -943,9 +967,12 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
   // index into the accumulator array is a constant.
   auto out_tile = [&](int i, int c, const f32x16& t0, const f32x16& t1,
                       float bias) {
+    const int row0 = wm * WM + 32 * i;   // wave-uniform
+    const int st = row0 / RPS;
+    lds_bf16* p = (lds_bf16*)(uintptr_t)(
+        stage_lds(st) + 2u * (uint32_t)((row0 - st * RPS + 4 * q) * NCOLS + c));
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int row = wm * WM + 32 * i + (v & 3) + 4 * q + 8 * (v >> 2);
       float h;
       if (MODE == UP_SWIGLU) {
         h = silu(t0[v]) * t1[v];
@@ -953,7 +980,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
         h = t0[v] + bias;
         if (MODE == UP_GELU) h = gelu_erf(h);
       }
-      ot(row, c) = (bf16)h;
+      p[((v & 3) + 8 * (v >> 2)) * NCOLS] = (bf16)h;
     }
   };
 #pragma unroll
@@ -972,13 +999,15 @@ __global__ __launch_bounds__(WAVES * 64, 1) void ffn_tiled_kernel(FfnArgs a,
   }
   __syncthreads();
   bf16* outp = (bf16*)(MODE == DOWN ? a.y : a.h);
-  const int cpr = ncols / 8;   // 16-byte chunks per output row
-  for (int idx = tid; idx < BM * cpr; idx += TL_THREADS) {
-    const int row = idx / cpr, ch = idx - row * cpr;
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int idx = ps * TL_THREADS + tid;   // 16-byte chunk of the tile
+    const int row = idx / CPR, ch = idx - row * CPR;
     const int i = r0 + row;
     const int n = nbase + ch * 8;
     if (i < gr.rows && n < N) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(&ot(row, ch * 8));
+      const u32x4 v = *(const lds_u32x4*)(uintptr_t)(
+          stage_lds(ps / PPS) + 16u * (uint32_t)(idx - (ps / PPS) * (SA / 8)));
       // non-temporal: the tile is not read again by this launch, and its
       // lines would otherwise push the shared A and B slices out of L2
       __builtin_nontemporal_store(

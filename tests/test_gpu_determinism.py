@@ -26,11 +26,12 @@ CASES = [
     # panel, shared expert
     W("det_panel", T=500, d_model=192, n_experts=4, top_k=2, d_ff=320,
       act="swiglu", dtype="bf16", capacity=0, n_shared=1, seed_index=51),
-    # tiled, split last round, drops
-    W("det_tiled_drops", T=1500, d_model=128, n_experts=4, top_k=2, d_ff=256,
-      act="gelu", dtype="bf16", capacity=700, seed_index=52),
-    # tiled, split last round
-    W("det_tiled", T=4200, d_model=256, n_experts=2, top_k=1, d_ff=512,
+    # tiled, drops, the up GEMM's last round split along K (K = 4096: 64
+    # slices, 3 tiles left per XCD, 8 pieces)
+    W("det_tiled_drops", T=1500, d_model=4096, n_experts=4, top_k=2,
+      d_ff=256, act="gelu", dtype="bf16", capacity=700, seed_index=52),
+    # tiled, the down GEMM's last round split along K (K = 4096)
+    W("det_tiled", T=4200, d_model=256, n_experts=2, top_k=1, d_ff=4096,
       act="swiglu", dtype="bf16", capacity=0, seed_index=53),
 ]
 # the same schedules with tiled bf16 weights

@@ -55,6 +55,12 @@ CASES = [
     (W("ffnb_tiled", T=2100, d_model=128, n_experts=2, top_k=1,
        d_ff=384, act="gelu", dtype="bf16", capacity=0, seed_index=45),
      [255, 1025]),
+    # tiled with K = 4096 in both GEMMs: 64 tiles each, 8 left per XCD
+    # after no whole round, so with a workspace both last rounds are split
+    # into 4 K pieces
+    (W("ffnb_tiled_ksplit", T=700, d_model=4096, n_experts=2, top_k=1,
+       d_ff=4096, act="gelu", dtype="bf16", capacity=0, seed_index=48),
+     [300, 385]),
 ]
 
 

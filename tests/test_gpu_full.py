@@ -13,8 +13,8 @@ benchmark times.
 * The expert FFN (moe_expert_ffn) on the oracle's grouping: every row of
   the largest expert's group against the oracle.  On the Mixtral-shaped
   prefill layer also the last expert, whose tiles end the last XCD's run
-  of tiles in both GEMMs (its last round is split along K, and its last
-  row tile is partial); on the DeepSeek-V3-shaped layer also the always-on
+  of tiles in both GEMMs (the down GEMM's last round is split along K, and
+  its last row tile is partial); on the DeepSeek-V3-shaped layer also the always-on
   shared expert (all 4096 rows).
 """
 
@@ -163,9 +163,11 @@ def _tiles_of_groups(rows, bm, nb):
     return [(int(e - s), int(e)) for s, e in zip(spans, ends)]
 
 
-def _split_tiles(total, cpx):
+def _split_tiles(total, cpx, nk):
     """Logical tiles whose last round the tiled schedule splits along K:
-    each XCD's contiguous run leaves lo tiles after its whole rounds."""
+    each XCD's contiguous run leaves lo tiles after its whole rounds; they
+    are cut into s = min(cpx // lo, nk, 8) pieces when s >= 2 and the split
+    takes at least 48 of the nk K slices off the last round."""
     per = (total + 7) // 8
     out = []
     for xcd in range(8):
@@ -173,8 +175,10 @@ def _split_tiles(total, cpx):
         n = max(0, min(per, total - first))
         whole = n // cpx
         lo = n - whole * cpx
-        if lo > 0 and cpx // lo >= 2:
-            out += list(range(first + whole * cpx, first + n))
+        if lo > 0:
+            s = min(cpx // lo, nk, 8)
+            if s >= 2 and nk - nk // s >= 48:
+                out += list(range(first + whole * cpx, first + n))
     return out
 
 
@@ -209,8 +213,9 @@ def _expert_rows_check(inp, wl, o_disp, e, label):
 def test_full_size_expert_rows(full):
     """The largest routed expert's whole row group on every workload; on the
     Mixtral-shaped prefill layer also the last expert (its tiles take the
-    K-split last round of the last XCD in both GEMMs, and its last row tile
-    is partial); on the DeepSeek-V3-shaped layer also the shared expert."""
+    K-split last round of the last XCD in the down GEMM, and its last row
+    tile is partial); on the DeepSeek-V3-shaped layer also the shared
+    expert."""
     wl, inp = full
     d = _oracle_grouping(inp, wl)
     rows = np.diff(d["offsets"]).tolist()
@@ -219,14 +224,15 @@ def test_full_size_expert_rows(full):
     if wl.name == "mixtral_prefill":
         e = wl.n_experts - 1
         cpx = torch.cuda.get_device_properties(0).multi_processor_count // 8
-        for gemm, nb in (("up", (wl.d_ff + 127) // 128),
-                         ("down", (wl.d_model + 255) // 256)):
+        for gemm, nb, nk in (("up", (wl.d_ff + 127) // 128, wl.d_model // 64),
+                             ("down", (wl.d_model + 255) // 256, wl.d_ff // 64)):
             spans = _tiles_of_groups(rows, 256, nb)
-            split = set(_split_tiles(spans[-1][1], cpx))
+            split = set(_split_tiles(spans[-1][1], cpx, nk))
             mine = set(range(*spans[e]))
             log(f"  {gemm} GEMM: {spans[-1][1]} tiles, {len(split)} split "
                 f"along K, {len(split & mine)} of them in expert {e}")
-            assert split & mine, "expert must own tiles of the K-split round"
+            if gemm == "down":
+                assert split & mine, "expert must own tiles of the K-split round"
         assert rows[e] % 256 != 0, "expert must end in a partial row tile"
         _expert_rows_check(inp, wl, d, e, f"expert {e} ({rows[e]} rows)")
     if wl.n_shared:

@@ -57,8 +57,9 @@ CASES = [
     W("tw_panel_gelu_drops", T=3000, d_model=256, n_experts=16, top_k=1,
       d_ff=448, act="gelu", dtype="bf16", capacity=200, zipf_s=0.3,
       seed_index=63, wquant="bf16_tiled"),
-    # tiled: T*k > 256*E, ragged M, partial N blocks, K split of the tail
-    W("tw_tiled_swiglu", T=2200, d_model=128, n_experts=2, top_k=1,
+    # tiled: T*k > 256*E, ragged M, partial N blocks; the up GEMM's last
+    # round split along K (K = 4096: 4 tiles left per XCD, 8 pieces)
+    W("tw_tiled_swiglu", T=2200, d_model=4096, n_experts=2, top_k=1,
       d_ff=384, act="swiglu", dtype="bf16", capacity=0, seed_index=64,
       wquant="bf16_tiled"),
     W("tw_tiled_gelu_shared_drops", T=2100, d_model=320, n_experts=2,

@@ -32,9 +32,15 @@ CASES = [
     (W("na_gelu_shared_drops", T=700, d_model=256, n_experts=8, top_k=2,
        d_ff=512, act="gelu", dtype="bf16", capacity=150, n_shared=1,
        zipf_s=0.5, seed_index=90), 37, True),
-    # 256-row tiled schedule (T*k > 256*E), then the panel schedule
+    # 256-row tiled schedule (T*k > 256*E), then the panel schedule; K of
+    # 256 and 384 is too short for moe_layer_forward to split a last round
     (W("na_tiled", T=1500, d_model=256, n_experts=4, top_k=2, d_ff=384,
-       act="swiglu", dtype="bf16", capacity=0, seed_index=91), 300, False),
+       act="swiglu", dtype="bf16", capacity=0, seed_index=91), 300, True),
+    # the same schedule with K = 4096 in the down GEMM, whose last round
+    # moe_layer_forward splits along K
+    (W("na_tiled_ksplit", T=1500, d_model=256, n_experts=4, top_k=2,
+       d_ff=4096, act="swiglu", dtype="bf16", capacity=0, seed_index=92),
+     300, False),
     # float32 problem
     (synth.WORKLOADS["tiny_gelu_f32"], 9, True),
 ]
