@@ -1144,8 +1144,13 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
   // 8h + lane/8, bytes 16 * (lane % 8) of the step; half lines per
   // instruction were slower: DeepSeek-V3 layer 5.75 against 5.51 ms) and
   // pass through a per-wave LDS slot into MFMA order: row col, chunk
-  // kq + 4h is register col / 8, lane 8 * (col % 8) + kq + 4h.  Plain loads:
-  // the non-temporal hint was mixed here (Switch faster, DeepSeek slower).
+  // kq + 4h is register col / 8, row col % 8, chunk kq + 4h.  In the slot,
+  // chunk ch of row r of register b sits at position 8r + (ch ^ (r/2) ^ 4b),
+  // so that the 16 lanes of an MFMA-order read (16 rows, one chunk) and of a
+  // store (two rows, eight chunks) fall on distinct banks of a 256-byte
+  // window (unswizzled, the reads met 8-way conflicts: 1.9e8 conflict
+  // cycles per DeepSeek-V3 up GEMM).  Plain loads: the non-temporal hint
+  // was mixed here (Switch faster, DeepSeek slower).
   uint32_t boff[CG][2];   // element offsets (same rows in every matrix)
 #pragma unroll
   for (int c = 0; c < CG; ++c)
@@ -1153,7 +1158,13 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
     for (int h = 0; h < 2; ++h)
       boff[c][h] = (uint32_t)min(nbase + 16 * (wave * CG + c) + 8 * h + (lane >> 3), N - 1) *
                        (uint32_t)K + (uint32_t)((lane & 7) * 8);
-  const int xsrc = col >> 3, xlane = 8 * (col & 7) + kq;
+  const int xsrc = col >> 3;
+  // slot positions: this lane's store of register b, and its MFMA-order
+  // read of half h
+  const int xst[2] = {(lane & 56) | ((lane & 7) ^ (lane >> 4)),
+                      (lane & 56) | ((lane & 7) ^ (lane >> 4) ^ 4)};
+  const int xrd[2] = {8 * (col & 7) + (kq ^ ((col & 7) >> 1) ^ (xsrc << 2)),
+                      8 * (col & 7) + ((kq + 4) ^ ((col & 7) >> 1) ^ (xsrc << 2))};
   // tiled weights: element offset of group c's tile at column block 0
   // (rows clamped to the last row block), this lane's 16 bytes
   uint32_t toff[CG];
@@ -1198,7 +1209,7 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
 #pragma unroll
       for (int c = 0; c < CG; ++c)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) xs[wave][(m * CG + c) * 2 + h][lane] = b.b[m][c][h];
+        for (int h = 0; h < 2; ++h) xs[wave][(m * CG + c) * 2 + h][xst[h]] = b.b[m][c][h];
   };
 
   f32x4 acc[NMAT][CG][MT];
@@ -1231,7 +1242,7 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
 #pragma unroll
           for (int c = 0; c < CG; ++c)
             bw[m][c].u = TW ? b.b[m][c][h]
-                            : xs[TW ? 0 : wave][(m * CG + c) * 2 + xsrc][xlane + 4 * h];
+                            : xs[TW ? 0 : wave][(m * CG + c) * 2 + xsrc][xrd[h]];
         const bf16* sa = S + (h ? aoff1 : aoff0);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
