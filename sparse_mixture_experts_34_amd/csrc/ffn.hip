@@ -397,18 +397,78 @@ __device__ __forceinline__ bool publish_tile(int G, int BM, int NB, int L,
 // Panel schedule: workgroups reach the 8 XCDs round-robin by id (slot =
 // id / 8 on XCD id % 8); runs of NB logical tiles (one panel's n-blocks,
 // which share its token rows) are dealt to the XCDs in turn, so XCD x's
-// slot j takes tile ((j / NB) * 8 + x) * NB + j % NB.  False for a
-// workgroup with no tile (the grid is an upper bound).
+// slot j takes tile ((j / NB) * 8 + x) * NB + j % NB.  Logical tiles run
+// group by group and panel by panel with the n-blocks innermost; with
+// by_cost, workgroups (which start roughly in id order) take the expensive
+// panels first: every panel with more than BM/2 rows (the full-size K loop,
+// about twice the matrix work of a half panel) of every group, then each
+// group's half panel (its last panel when that holds at most BM/2 rows).
+// The up GEMMs use it: in group order DeepSeek-V3's up GEMM left the CUs
+// idle 8% of the time at its end (the last CU finishing 270 us after the
+// average), and the order took it from 3100 to 3063 us.  The down GEMMs'
+// panels are short (38-83 us against 130-286 us there) and ran 1.5-2%
+// slower in that order, so they keep group order.  False for a workgroup
+// with no tile (the grid is an upper bound).
 template <int NTHR>
 __device__ bool find_panel_tile(const FfnArgs& a, int G, int BM, int NB,
-                                int* s_info) {
-  __shared__ int s_wsum[NTHR / 64];
-  if (threadIdx.x == 0) s_info[1] = -1;
-  int excl, incl, total;
-  tile_scan<NTHR>(a, G, BM, NB, s_wsum, excl, incl, total);
+                                bool by_cost, int* s_info) {
+  __shared__ int s_wsum[2][NTHR / 64];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  if (t == 0) s_info[1] = -1;
+  // this thread's group: full-loop panels nf and half panels nh (0 or 1;
+  // without by_cost every panel counts in the first class)
+  int nf = 0, nh = 0, np = 0;
+  if (t < G) {
+    const int rows = t < a.E ? a.offsets[t + 1] - a.offsets[t] : a.T;
+    np = (rows + BM - 1) / BM;
+    nh = (by_cost && np > 0 && rows - (np - 1) * BM <= BM / 2) ? 1 : 0;
+    nf = np - nh;
+  }
+  // inclusive prefix sums of the two classes' tile counts (wave shuffles,
+  // then wave totals through LDS)
+  int inf = nf * NB, inh = nh * NB;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int vf = __shfl_up(inf, o, 64), vh = __shfl_up(inh, o, 64);
+    if (lane >= o) {
+      inf += vf;
+      inh += vh;
+    }
+  }
+  if (lane == 63) {
+    s_wsum[0][wave] = inf;
+    s_wsum[1][wave] = inh;
+  }
+  __syncthreads();
+  int bf = 0, bh = 0, tf = 0;
+#pragma unroll
+  for (int w = 0; w < NTHR / 64; ++w) {
+    const int wf = s_wsum[0][w], wh = s_wsum[1][w];
+    if (w < wave) {
+      bf += wf;
+      bh += wh;
+    }
+    tf += wf;
+  }
+  inf += bf;
+  inh += bh;
   const int slot = blockIdx.x / N_XCD;
   const int L = ((slot / NB) * N_XCD + blockIdx.x % N_XCD) * NB + slot % NB;
-  return publish_tile(G, BM, NB, L, excl, incl, s_info);
+  if (t < G) {
+    const int ef = inf - nf * NB, eh = tf + inh - nh * NB;
+    if (L >= ef && L < inf) {          // full-loop panel (L - ef) / NB
+      s_info[0] = t;
+      s_info[1] = ((L - ef) / NB) * BM;
+      s_info[2] = (L - ef) % NB;
+    } else if (L >= eh && L < eh + nh * NB) {   // the half panel
+      s_info[0] = t;
+      s_info[1] = (np - 1) * BM;
+      s_info[2] = L - eh;
+    }
+  }
+  __syncthreads();
+  return s_info[1] >= 0;
 }
 
 // Tiled schedule: XCD x takes the contiguous run of ceil(total / 8)
@@ -1093,7 +1153,7 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
   __shared__ int s_info[3];
 
   const int G = a.E + a.n_shared;
-  if (!find_panel_tile<W * 64>(a, G, BM, NB, s_info)) return;
+  if (!find_panel_tile<W * 64>(a, G, BM, NB, MODE != DOWN, s_info)) return;
   const int g = s_info[0], r0 = s_info[1], nb = s_info[2];
   const Group gr = group_of(g, a.offsets, a.E, a.T, a.k);
   const int N = MODE == DOWN ? a.d : a.d_ff;
