@@ -1378,10 +1378,11 @@ __global__ __launch_bounds__(W * 64, 1) void ffn_panel_kernel(FfnArgs a,
     for (int u = 0; u < U - 1; ++u)
       if (ntrip * U + u < nk) step(ntrip * U + u, u);
   };
-  // two instances: panels filling at most half the tiles run the half-size
-  // loop (more instances overflow the register file)
-  static_assert(MT % 2 == 0, "half panel");
-  if (ntile > MT / 2) kloop(IntC<MT>{});
+  // three instances: panels filling at most half or three quarters of the
+  // tiles run a shorter loop
+  static_assert(MT % 4 == 0, "half and three-quarter panels");
+  if (ntile > MT * 3 / 4) kloop(IntC<MT>{});
+  else if (ntile > MT / 2) kloop(IntC<MT * 3 / 4>{});
   else kloop(IntC<MT / 2>{});
   // the redundant tail A loads land in LDS before the workgroup can end
   // (the next workgroup on this CU may take the same LDS)
