@@ -103,6 +103,11 @@ struct StreamBuf {
 template <int MODE, int RT, int CG, bool TW>
 __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
   constexpr int NMAT = MODE == UP_SWIGLU ? 2 : 1;
+  // prefetch ring depth: the one-row-tile down GEMM takes two steps, which
+  // leaves it under 128 VGPRs, four workgroups per CU: the decode down
+  // GEMM's 1024 workgroups are then all resident at once instead of
+  // running 1.33 rounds of three per CU
+  constexpr int PF = (MODE == DOWN && RT == 1) ? 2 : ST_PF;
   __shared__ f32x4 red[ST_WAVES - 1][NMAT * CG * RT][64];
   __shared__ u32x4 xs[TW ? 1 : ST_WAVES][NMAT * CG * 2][64];   // reshuffle
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -171,7 +176,7 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
 #pragma unroll
         for (int t = 0; t < RT; ++t) acc[m][c][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    StreamBuf<NMAT, RT, CG> buf[ST_PF];
+    StreamBuf<NMAT, RT, CG> buf[PF];
     auto load = [&](StreamBuf<NMAT, RT, CG>& b, int s) {
       const int k0 = s * ST_KSTEP;
 #pragma unroll
@@ -233,16 +238,16 @@ __global__ __launch_bounds__(ST_WAVES * 64) void ffn_stream_kernel(FfnArgs a) {
       }
     };
 #pragma unroll
-    for (int p = 0; p < ST_PF; ++p)
+    for (int p = 0; p < PF; ++p)
       if (p < my_steps) load(buf[p], p);
-    for (int s0 = 0; s0 < my_steps; s0 += ST_PF) {
+    for (int s0 = 0; s0 < my_steps; s0 += PF) {
 #pragma unroll
-      for (int p = 0; p < ST_PF; ++p) {
+      for (int p = 0; p < PF; ++p) {
         const int s = s0 + p;
         if (s < my_steps) {
           stage(buf[p]);
           const StreamBuf<NMAT, RT, CG> cur = buf[p];
-          if (s + ST_PF < my_steps) load(buf[p], s + ST_PF);
+          if (s + PF < my_steps) load(buf[p], s + PF);
           compute(cur);
         }
       }
