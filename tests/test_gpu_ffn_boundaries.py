@@ -61,6 +61,16 @@ CASES = [
     (W("ffnb_tiled_ksplit", T=700, d_model=4096, n_experts=2, top_k=1,
        d_ff=4096, act="gelu", dtype="bf16", capacity=0, seed_index=48),
      [300, 385]),
+    # panel with few panels and a long K (the Switch-shaped down GEMM's
+    # situation): 128 K steps in the GELU down GEMM (biases, a two-panel
+    # expert), then in a SwiGLU up GEMM with the shared expert's two panels
+    (W("ffnb_panel_longk_down", T=600, d_model=512, n_experts=4, top_k=1,
+       d_ff=8192, act="gelu", dtype="bf16", capacity=0, seed_index=49),
+     [130, 0, 257, 200]),
+    (W("ffnb_panel_longk_up", T=300, d_model=8192, n_experts=4, top_k=2,
+       d_ff=256, act="swiglu", dtype="bf16", capacity=0, n_shared=1,
+       seed_index=50),
+     [100, 129, 0, 256]),
 ]
 
 
@@ -140,3 +150,4 @@ def test_expert_ffn_boundaries(wl, counts, tiled):
         f"up+down {err2:.2e} ({worst2:.2e}); with workspace {err3:.2e} "
         f"({worst3:.2e})")
     assert max(err, worst, err2, worst2, err3, worst3) <= TOL["bf16"]
+
