@@ -57,6 +57,29 @@ CASES = [
     W("sb_t29_e6_sigmoid_bias_raw", T=29, d_model=192, n_experts=6, top_k=3,
       d_ff=64, act="gelu", dtype="bf16", capacity=0, scoring="sigmoid",
       select_bias_std=0.1, raw_gates=True, seed_index=69),
+    # decode size at the one-wave dispatch's limit (64 assignments), router
+    # and selection biases, capacity drops
+    W("sb_t16_e8_k4_biases_drops", T=16, d_model=256, n_experts=8, top_k=4,
+      d_ff=128, act="swiglu", dtype="bf16", capacity=6, zipf_s=0.8,
+      select_bias_std=0.1, seed_index=72),
+    # 80 assignments at decode size: the one-workgroup dispatch
+    W("sb_t16_e8_k5", T=16, d_model=128, n_experts=8, top_k=5, d_ff=64,
+      act="swiglu", dtype="bf16", capacity=0, seed_index=73),
+    # three experts, top-1 sigmoid scores with a selection bias, raw gates
+    W("sb_t7_e3_k1_sigmoid_raw", T=7, d_model=192, n_experts=3, top_k=1,
+      d_ff=64, act="gelu", dtype="bf16", capacity=0, scoring="sigmoid",
+      select_bias_std=0.1, raw_gates=True, seed_index=74),
+    # d = 320 (a partial trip of the fused route's K loop), shared expert
+    W("sb_t12_e6_gelu_shared", T=12, d_model=320, n_experts=6, top_k=2,
+      d_ff=128, act="gelu", dtype="bf16", capacity=0, n_shared=1,
+      seed_index=75),
+    # the fused route writing logits for overflow reassignment at decode size
+    W("sb_t16_reassign", T=16, d_model=128, n_experts=8, top_k=1, d_ff=64,
+      act="gelu", dtype="bf16", capacity=1, zipf_s=1.1, seed_index=76,
+      overflow="reassign", overflow_seed=5),
+    # float32 at decode size
+    W("sb_t16_f32", T=16, d_model=64, n_experts=8, top_k=2, d_ff=64,
+      act="swiglu", dtype="f32", capacity=0, seed_index=77),
     # the largest batch of the fused route (128 tokens, 256 assignments:
     # the one-workgroup dispatch)
     W("sb_t128_e8", T=128, d_model=128, n_experts=8, top_k=2, d_ff=64,
