@@ -256,27 +256,8 @@ def measure(wl, steps, warmup, dev):
     same = bool(torch.equal(out, out2))
 
     # dominant kernel: the longest single-kernel step (up or down GEMM)
-    esz = 2 if wl.dtype == "bf16" else 4
+    krn = gemm_work(wl, cnt, kept_total)
     touched = sum(1 for c in cnt if c > 0) + wl.n_shared
-    nmat_up = 2 if wl.act == "swiglu" else 1
-    if q4:
-        # codes (half a byte per weight) + float32 (scale, offset) per 128
-        qb = lambda n: n // 2 + (n // 128) * 8
-        up_w = touched * (nmat_up * qb(f * d) +
-                          (f * esz if wl.act == "gelu" else 0))
-        dn_w = touched * (qb(d * f) + (d * esz if wl.act == "gelu" else 0))
-    else:
-        up_w = touched * (nmat_up * f * d +
-                          (f if wl.act == "gelu" else 0)) * esz
-        dn_w = touched * (d * f + (d if wl.act == "gelu" else 0)) * esz
-    krn = {
-        "expert_up": {
-            "bytes": up_w + kept_total_rows(kept_total, wl) * (d + f) * esz,
-            "flops": 2 * kept_total_rows(kept_total, wl) * d * f * nmat_up},
-        "expert_down": {
-            "bytes": dn_w + kept_total_rows(kept_total, wl) * (f + d) * esz,
-            "flops": 2 * kept_total_rows(kept_total, wl) * d * f},
-    }
     dom = max(krn, key=lambda n: per[n])
     kb, kf, kt = krn[dom]["bytes"], krn[dom]["flops"], per[dom]
     if wl.dtype == "bf16":
@@ -363,6 +344,34 @@ def copy_calibration(mib):
 
 def kept_total_rows(kept_total, wl):
     return kept_total + wl.n_shared * wl.T
+
+
+def gemm_work(wl, counts, kept_total):
+    """Algorithmic bytes and FLOPs of each expert GEMM launch: the touched
+    experts' weights (and GELU biases) once, plus the rows it reads and
+    writes (A rows of K elements, output rows of N); 2 FLOPs per
+    multiply-add over the kept and shared rows."""
+    d, f = wl.d_model, wl.d_ff
+    esz = 2 if wl.dtype == "bf16" else 4
+    touched = sum(1 for c in counts if c > 0) + wl.n_shared
+    nmat_up = 2 if wl.act == "swiglu" else 1
+    if wl.wquant == "int4":
+        # codes (half a byte per weight) + float32 (scale, offset) per 128
+        qb = lambda n: n // 2 + (n // 128) * 8
+        up_w = touched * (nmat_up * qb(f * d) +
+                          (f * esz if wl.act == "gelu" else 0))
+        dn_w = touched * (qb(d * f) + (d * esz if wl.act == "gelu" else 0))
+    else:
+        up_w = touched * (nmat_up * f * d +
+                          (f if wl.act == "gelu" else 0)) * esz
+        dn_w = touched * (d * f + (d if wl.act == "gelu" else 0)) * esz
+    rows = kept_total_rows(kept_total, wl)
+    return {
+        "expert_up": {"bytes": up_w + rows * (d + f) * esz,
+                      "flops": 2 * rows * d * f * nmat_up},
+        "expert_down": {"bytes": dn_w + rows * (f + d) * esz,
+                        "flops": 2 * rows * d * f},
+    }
 
 
 def cpu_baseline(wl, inp, n_tokens=None, gpu_idx=None, gpu_out=None):

@@ -81,3 +81,43 @@ def test_int4_decode_bytes():
     # half a byte per weight plus a float32 (scale, offset) per 128 weights
     assert B == 8 * (per_expert // 2 + per_expert // 128 * 8) + 393_216
     assert t_roof(F, B) * 1e6 == pytest.approx(99.14, abs=0.01)
+
+
+# ---- the dominant kernel's algorithmic work (bench roofline.achieved) -----
+
+def test_gemm_work_decode():
+    w = bench.gemm_work(WL["mixtral_decode"], [4] * 8, 32)
+    # gate + up weights of 8 experts once, 32 rows in (d) and out (d_ff)
+    assert w["expert_up"]["bytes"] == 8 * 2 * 14336 * 4096 * 2 + \
+        32 * (4096 + 14336) * 2 == 1_880_227_840
+    assert w["expert_up"]["flops"] == 2 * 32 * 4096 * 14336 * 2
+    assert w["expert_down"]["bytes"] == 8 * 4096 * 14336 * 2 + \
+        32 * (14336 + 4096) * 2
+
+
+def test_gemm_work_prefill():
+    w = bench.gemm_work(WL["mixtral_prefill"], [2048] * 8, 16384)
+    assert w["expert_up"]["flops"] == 2 * 16384 * 4096 * 14336 * 2 \
+        == 3_848_290_697_216
+    assert w["expert_down"]["flops"] * 2 == w["expert_up"]["flops"]
+    # 3.85 TFLOP over 2.48 GB: far past the 312.5 FLOP/B ridge
+    assert w["expert_up"]["bytes"] == 2_483_027_968
+
+
+def test_gemm_work_int4_and_gelu_bias():
+    w = bench.gemm_work(WL["mixtral_decode_int4"], [4] * 8, 32)
+    codes = 2 * 14336 * 4096 // 2 + 2 * 14336 * 4096 // 128 * 8
+    assert w["expert_up"]["bytes"] == 8 * codes + 32 * (4096 + 14336) * 2
+    # GELU experts: one up matrix and its bias; 43 touched Switch experts
+    s = bench.gemm_work(WL["switch_top1_cf1"], [1] * 43 + [0] * 21, 2664)
+    assert s["expert_up"]["bytes"] == 43 * (8192 * 2048 + 8192) * 2 + \
+        2664 * (2048 + 8192) * 2 == 1_498_103_808
+    assert s["expert_up"]["flops"] == 2 * 2664 * 2048 * 8192
+
+
+def test_gemm_work_shared_expert_rows():
+    w = bench.gemm_work(WL["deepseek_v3"], [128] * 256, 32768)
+    rows = 32768 + 4096            # routed assignments + the shared expert
+    assert w["expert_up"]["flops"] == 2 * rows * 7168 * 2048 * 2
+    assert w["expert_up"]["bytes"] == 257 * 2 * 2048 * 7168 * 2 + \
+        rows * (7168 + 2048) * 2 == 15_770_583_040
