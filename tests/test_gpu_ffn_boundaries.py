@@ -1,7 +1,8 @@
 """GPU parity of the expert FFN (moe_expert_ffn) against the CPU oracle on
 hand-made groupings whose per-expert row counts sit on every boundary of the
 bf16 schedules: empty experts, one row, 15/16/17 rows (16-row MFMA tiles),
-127/128/129 rows (half and full 256-row panels), 255/256/257 rows (one or
+127/128/129 rows (half and full 256-row panels), 144/160/161/193 rows (the
+three-quarter panel loop and just past it), 255/256/257 rows (one or
 two panels or 256-row tiles), with and without a shared expert,
 odd numbers of 64-wide K steps and partial weight blocks.  The schedule is
 chosen from T, k and E only (stream up to 64 assignments per expert on
@@ -43,6 +44,11 @@ CASES = [
     (W("ffnb_panel_swiglu_b", T=500, d_model=192, n_experts=4, top_k=2,
        d_ff=320, act="swiglu", dtype="bf16", capacity=0, seed_index=42),
      [1, 127, 255, 256]),
+    # the three-quarter panel loop (129-192 rows: 12 row tiles) from 144 to
+    # 161 rows, and just past it
+    (W("ffnb_panel_swiglu_c", T=500, d_model=192, n_experts=4, top_k=2,
+       d_ff=320, act="swiglu", dtype="bf16", capacity=0, seed_index=51),
+     [144, 160, 161, 193]),
     (W("ffnb_panel_gelu", T=500, d_model=256, n_experts=4, top_k=2,
        d_ff=448, act="gelu", dtype="bf16", capacity=0, n_shared=1,
        seed_index=43),
