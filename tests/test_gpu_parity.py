@@ -71,6 +71,21 @@ SMALL = [
     # 256-row tiles and a ragged one) with SwiGLU
     W("swiglu_tiled_mid", T=1500, d_model=128, n_experts=4, top_k=2,
       d_ff=256, act="swiglu", dtype="bf16", capacity=0, seed_index=28),
+    # both sides of each schedule threshold, chosen from T*k/E alone:
+    # 64 assignments per expert (stream), 64.25 (panel), 256 (panel),
+    # 256.25 (tiled)
+    W("sched_stream_edge", T=256, d_model=128, n_experts=8, top_k=2,
+      d_ff=192, act="swiglu", dtype="bf16", capacity=0, router_std=0.02,
+      seed_index=80),
+    W("sched_panel_low_edge", T=257, d_model=128, n_experts=8, top_k=2,
+      d_ff=192, act="swiglu", dtype="bf16", capacity=0, router_std=0.02,
+      seed_index=81),
+    W("sched_panel_high_edge", T=1024, d_model=128, n_experts=8, top_k=2,
+      d_ff=192, act="gelu", dtype="bf16", capacity=0, router_std=0.02,
+      seed_index=82),
+    W("sched_tiled_edge", T=1025, d_model=128, n_experts=8, top_k=2,
+      d_ff=192, act="gelu", dtype="bf16", capacity=0, router_std=0.02,
+      seed_index=83),
     # tiled, many rows per expert: ragged M and partial N blocks
     W("swiglu_bm256", T=2200, d_model=128, n_experts=2, top_k=1, d_ff=384,
       act="swiglu", dtype="bf16", capacity=0, seed_index=23),
