@@ -190,7 +190,7 @@ def test_int4_layer(wl):
     log(f"  {wl.name}: out rel err {err:.2e} (moe delta {derr:.2e})")
     assert np.isfinite(out).all()
     assert err <= TOL["bf16"]
-    assert derr <= 5 * TOL["bf16"]
+    assert derr <= TOL["bf16"]
     g2 = gpu_layer(qin, wl)
     assert torch.equal(g["out"], g2["out"])
 
@@ -201,7 +201,7 @@ def test_int4_full_size_decode_sampled():
     inp = make(wl)
     qin = moe.quantize_weights(inp)
     g = gpu_layer(qin, wl)
-    tokens = np.array([0, 9])
+    tokens = np.array([0, 5, 9, 15])
     o = oracle_q4_layer(inp, wl, tokens=tokens)
     assert host(g["idx"]).tolist() == o["idx"].tolist()
     assert host(g["counts"]).tolist() == o["counts"].tolist()
@@ -212,5 +212,6 @@ def test_int4_full_size_decode_sampled():
     log(f"  {wl.name}: sampled out rel err {err:.2e} (moe delta {derr:.2e})")
     assert np.isfinite(out).all()
     assert err <= TOL["bf16"]
+    assert derr <= TOL["bf16"]
     del inp, qin
     torch.cuda.empty_cache()
