@@ -169,6 +169,7 @@ def test_layer_forward(wl):
     log(f"  {wl.name}: layer out rel err {err:.2e} (moe delta {derr:.2e}), "
         f"dropped {o['n_dropped']}")
     assert err <= TOL[wl.dtype]
+    assert derr <= TOL[wl.dtype]
     # bit-identical on a second run
     g2 = gpu_layer(inp, wl)
     assert torch.equal(g["out"], g2["out"])
