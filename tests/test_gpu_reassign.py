@@ -85,9 +85,12 @@ def test_reassign_layer(wl):
     aux = float(host(g["aux"])[0])
     assert abs(aux - o["aux"]) <= AUX_RTOL * abs(o["aux"])
     err = rel_inf(host(g["out"]), o["out"])
+    x = host(inp["x"])
+    derr = rel_inf(host(g["out"]) - x, o["out"] - x)
     log(f"  {wl.name}: reassigned {o['n_reassigned']}, still dropped "
-        f"{o['n_dropped']}, out rel err {err:.2e}")
+        f"{o['n_dropped']}, out rel err {err:.2e} (moe delta {derr:.2e})")
     assert err <= TOL[wl.dtype]
+    assert derr <= TOL[wl.dtype]
     g2 = gpu_layer(inp, wl)
     assert torch.equal(g["out"], g2["out"])
 
@@ -143,6 +146,10 @@ def test_reassign_full_size_switch():
     assert int(host(g["n_dropped"])[0]) == o["n_dropped"]
     out = host(g["out"][torch.as_tensor(tokens, device="cuda")])
     err = rel_inf(out, o["out"])
+    x = host(inp["x"])[tokens]
+    derr = rel_inf(out - x, o["out"] - x)
     log(f"  {wl.name}: reassigned {o['n_reassigned']}, still dropped "
-        f"{o['n_dropped']}, sampled out rel err {err:.2e}")
+        f"{o['n_dropped']}, sampled out rel err {err:.2e} (moe delta "
+        f"{derr:.2e})")
     assert err <= TOL["bf16"]
+    assert derr <= TOL["bf16"]

@@ -82,8 +82,12 @@ def test_layer_variant(wl):
     aux = float(host(g["aux"])[0])
     assert abs(aux - o["aux"]) <= AUX_RTOL * abs(o["aux"])
     err = rel_inf(host(g["out"]), o["out"])
-    log(f"  {wl.name}: out rel err {err:.2e}, aux {aux:.6f}")
+    x = host(inp["x"])
+    derr = rel_inf(host(g["out"]) - x, o["out"] - x)
+    log(f"  {wl.name}: out rel err {err:.2e} (moe delta {derr:.2e}), "
+        f"aux {aux:.6f}")
     assert err <= TOL[wl.dtype]
+    assert derr <= TOL[wl.dtype]
 
 
 @pytest.mark.parametrize("E", [4, 64, 256])

@@ -102,11 +102,14 @@ def test_small_batch_layer(wl):
     aux = float(host(g["aux"])[0])
     assert abs(aux - o["aux"]) <= AUX_RTOL * abs(o["aux"])
     err = rel_inf(host(g["out"]), o["out"])
-    log(f"  {wl.name}: out rel err {err:.2e}, dropped {o['n_dropped']}, "
-        f"reassigned {o.get('n_reassigned', 0)}")
+    x = host(inp["x"])
+    derr = rel_inf(host(g["out"]) - x, o["out"] - x)
+    log(f"  {wl.name}: out rel err {err:.2e} (moe delta {derr:.2e}), "
+        f"dropped {o['n_dropped']}, reassigned {o.get('n_reassigned', 0)}")
     if "drops" in wl.name:
         assert o["n_dropped"] > 0, "workload must exercise the capacity cut"
     assert err <= TOL[wl.dtype]
+    assert derr <= TOL[wl.dtype]
     if wl.overflow == "reassign":
         assert o["n_reassigned"] > 0, "workload must exercise reassignment"
         return
