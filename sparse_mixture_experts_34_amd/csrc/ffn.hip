@@ -22,13 +22,16 @@
 // assignments per expert T*k/E):
 //   stream  up to 64 (decode): a workgroup owns 32 output columns, its
 //           waves split K, and each streams its weight rows once from HBM
-//           straight into MFMA B registers (16x16x32) with a 3-deep register
-//           prefetch ring; the handful of token rows ride along as the A
-//           operand; partial sums meet in LDS.
+//           in whole 128-byte lines into a register prefetch ring (three
+//           steps; two for the one-row-tile down GEMM), reordered into
+//           16x16x32 MFMA B order through a per-wave LDS slot; the handful
+//           of token rows ride along as the A operand; partial sums meet in
+//           LDS.
 //   panel   up to 256 (many experts, moderate batch): a workgroup owns up to
 //           256 rows of one expert and 256 weight rows over all of K; the
-//           weights stream once from HBM into MFMA B registers, the token
-//           rows are shared through LDS.
+//           weights stream once from HBM the same way (lines, per-wave LDS
+//           reorder), the token rows go straight into LDS and are shared by
+//           the workgroup's waves.
 //   tiled   more (prefill): 256-row by 256-column workgroup tiles,
 //           A and B loaded straight into XOR-swizzled LDS stages, 32x32x16
 //           MFMAs, the activation fused into the epilogue, the output tile
