@@ -24,6 +24,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -75,12 +76,21 @@ GEMM_SOURCES = ("common.hpp", "kernels.hpp", "ffn_common.hpp", "ffn.hip",
                 "ffn_q4.hip")
 
 
+def code_only(text: str) -> str:
+    """A C++ source without its comments and with its white space collapsed:
+    what the compiler sees of it (these sources hold no string literal with
+    a comment marker), so a comment-only edit leaves the digest alone."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return " ".join(text.split())
+
+
 def kernel_sources_digest() -> str:
     d = os.path.join(ROOT, "sparse_mixture_experts_34_amd", "csrc")
     h = hashlib.sha256()
     for f in GEMM_SOURCES:
         h.update(f.encode())
-        h.update(open(os.path.join(d, f), "rb").read())
+        h.update(code_only(open(os.path.join(d, f)).read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -121,3 +121,13 @@ def test_gemm_work_shared_expert_rows():
     assert w["expert_up"]["flops"] == 2 * rows * 7168 * 2048 * 2
     assert w["expert_up"]["bytes"] == 257 * 2 * 2048 * 7168 * 2 + \
         rows * (7168 + 2048) * 2 == 15_770_583_040
+
+
+def test_traffic_digest_ignores_comments_only():
+    # the HBM-traffic records are keyed to the GEMM sources' code: comments
+    # and white space do not count, any code change does
+    src = "int f(int a) {  // sum\n  return a + 1; /* one\nmore */ }\n"
+    same = "int f(int a) { return a + 1;   }  // edited comment\n"
+    other = "int f(int a) { return a + 2; }\n"
+    assert bench.code_only(src) == bench.code_only(same)
+    assert bench.code_only(src) != bench.code_only(other)
