@@ -81,9 +81,10 @@ __device__ __forceinline__ void group_weights(const FfnArgs& a, int g,
 // ===========================================================================
 // A workgroup owns 32 output columns (two groups of 16) of one group; its 4
 // waves split the K steps into contiguous quarters, stream their weight rows
-// into registers (3-deep prefetch ring) and add their partial sums through
-// LDS in the fixed order 0,1,2,3.  Two column groups per workgroup halve the
-// token-row (A) reads per weight byte.
+// into registers (a prefetch ring of ST_PF steps; two for the one-row-tile
+// down GEMM, below) and add their partial sums through LDS in the fixed
+// order 0,1,2,3.  Two column groups per workgroup halve the token-row (A)
+// reads per weight byte.
 //
 // Weight loads are non-temporal and cover whole 128-byte lines: a load
 // instruction reads 8 rows x 128 bytes (lane l: row l / 8, bytes 16 * (l %
